@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Throughput of the fused-epilogue batched GEMM on one MI355X.
+
+One step = one call of the whole hot path (persistent GEMM + fused epilogue,
+a single kernel launch) on inputs already resident in HBM.  Default workload:
+M = N = K = 8192, L = 1, fp16 A/B (K-major), fp16 C, X, D, Y (N-major),
+alpha 2, beta 1, x_factor 3 -- the shape and scalars of the CuTe DSL
+example's "Example usage".
+
+Prints ONE JSON line with the metric, a roofline object for the kernel
+(MFMA-bound: achieved TFLOP/s from HIP events around every launch, on the
+stream the kernel runs on, against the datasheet dense peak) and the CPU
+oracle timed on a bounded sample of the same workload as a baseline.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s and % of MFMA dense peak, 8192³ fp16 GEMM w/ fused epilogue"
+# MI355X datasheet dense MFMA peaks, TFLOP/s (TOP/s for int8)
+PEAK = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "i8": 5000.0}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in ("beta_epilogue_amd/csrc/gemm_epi_kernel.hpp",
+                "beta_epilogue_amd/csrc/gemm_epi.hip"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed counter runs, only while the
+    kernel sources are the ones the counters were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = rec.get(workload)
+    if not e or e.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(p, ins, target_s: float):
+    """The oracle, as it stands, on whole rows of D; scaled to TFLOP/s."""
+    import numpy as np
+    import oracle
+    threads = oracle.host_threads()
+
+    def rows_points(nrows):
+        ms = np.linspace(0, p.M * p.L - 1, nrows).astype(np.int64)
+        pts = np.empty((nrows * p.N, 3), np.int64)
+        pts[:, 0] = np.repeat(ms // p.M, p.N)
+        pts[:, 1] = np.repeat(ms % p.M, p.N)
+        pts[:, 2] = np.tile(np.arange(p.N), nrows)
+        return pts
+
+    def timed(nrows):
+        pts = rows_points(nrows)
+        t0 = time.perf_counter()
+        oracle.gemm_epi_points(p.M, p.N, p.K, p.L, ins["A"], ins["B"], ins["C"],
+                               ins["X"], points=pts, ab=p.ab, c=p.c, x=p.x,
+                               a_major=p.a_major, b_major=p.b_major,
+                               cd_major=p.cd_major, alpha=p.alpha, beta=p.beta,
+                               x_factor=p.x_factor, nthreads=threads)
+        return time.perf_counter() - t0
+
+    r0 = max(1, threads)
+    dt0 = timed(r0)
+    rows = int(min(p.M * p.L, max(r0, r0 * target_s / max(dt0, 1e-3))))
+    dt = timed(rows)
+    flops = 2.0 * p.K * rows * p.N
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d whole rows of D (%d outputs, K=%d fp64 dot products "
+                      "plus the epilogue each), %.1f s" % (rows, rows * p.N, p.K, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload index 0..4 (2 = 8192^3 fp16 with C, X, D, Y)")
+    ap.add_argument("--variant", type=int, default=-1)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py: this build runs on one GPU only (the GEMM is sharded "
+                  "by output tiles with no exchange; see the design notes); "
+                  "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import beta_epilogue_amd as ge
+
+    p = synth.CONFIGS[args.config]
+    print("bench: workload %s M=%d N=%d K=%d L=%d" % (p.name, p.M, p.N, p.K, p.L),
+          file=sys.stderr, flush=True)
+    ins = synth.make_inputs(p)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in ins.items()}
+    shape = p.storage_shape("D")
+    D = torch.empty(shape, dtype=synth.TORCH_DTYPE[p.d], device="cuda")
+    Y = torch.empty(shape, dtype=synth.TORCH_DTYPE[p.y], device="cuda") if p.y else None
+    g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, a_major=p.a_major,
+                     b_major=p.b_major, cd_major=p.cd_major, c=p.c, x=p.x,
+                     d=p.d, y=p.y, variant=args.variant)
+    plan = g.plan
+    stream = torch.cuda.current_stream()
+
+    def step():
+        g(dev["A"], dev["B"], dev["C"], dev["X"], D=D, Y=Y, alpha=p.alpha,
+          beta=p.beta, x_factor=p.x_factor, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    region_ms = starts[0].elapsed_time(ends[-1])
+    ms_per_step = region_ms / K
+    avg_launch_ms = sum(launch_ms) / K
+    flops = p.flops
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK[p.ab]
+    print("bench: %d steps, %.4f ms/step (events), %.4f ms/launch avg, min %.4f "
+          "max %.4f, wall %.3f s, %s" % (K, ms_per_step, avg_launch_ms,
+                                         min(launch_ms), max(launch_ms), wall,
+                                         plan["name"]), file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(p, ins, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.ab,
+        "data": "synthetic (seeded; distributions of the workload definition)",
+        "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "L": p.L,
+                   "ab": p.ab, "a_major": p.a_major, "b_major": p.b_major,
+                   "cd_major": p.cd_major, "c": p.c, "x": p.x, "d": p.d,
+                   "y": p.y, "alpha": p.alpha, "beta": p.beta,
+                   "x_factor": p.x_factor, "accumulate": "i32" if p.ab == "i8" else "f32"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(p.name),
+                     "algorithmic_bytes": p.algorithmic_bytes(),
+                     "kernel": plan["name"], "avg_launch_ms": round(avg_launch_ms, 5)},
+        "cpu_baseline": cpu,
+        "plan": plan,
+    }
+    print(json.dumps(out), flush=True)
+    g.close()
+
+
+if __name__ == "__main__":
+    main()

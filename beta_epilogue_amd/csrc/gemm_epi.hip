@@ -1,0 +1,336 @@
+// gemm_epi.hip -- C ABI of the fused-epilogue batched GEMM (see
+// include/gemm_epi.h): validation, variant choice, persistent launch.
+//
+// Conventions follow the Blackwell pipeline API card ("Host side": a plan is
+// built once and checked before launch, errors come back as codes with a
+// string function; "Device side": one handle serves the whole persistent
+// grid) and the "Constraints" of the CuTe DSL example
+// custom_epilogue_dense_gemm.py (A/B share a type, C/D/X/Y share a
+// majorness, contiguous extents are 16-byte multiples).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "gemm_epi.h"
+#include "gemm_epi_kernel.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+using gemm_epi::Params;
+typedef void (*launch_fn)(const Params&, int grid, hipStream_t s);
+
+struct Variant {
+  const char* name;
+  int ab;          // A/B element type
+  int a_major;     // GEMM_EPI_MAJOR_*
+  int b_major;
+  int cd_major;
+  int bm, bn, bk, threads, lds;
+  launch_fn launch;
+};
+
+template <class CF>
+void launch(const Params& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_epi::gemm_epi_kernel<CF>, dim3(grid), dim3(CF::THREADS), 0, s, p);
+}
+
+template <int AB, bool AK, bool BK, bool CDN>
+constexpr Variant make_variant(const char* name) {
+  using CF = gemm_epi::Cfg<AB, AK, BK, CDN>;
+  return Variant{name,
+                 AB,
+                 AK ? GEMM_EPI_MAJOR_K : GEMM_EPI_MAJOR_M,
+                 BK ? GEMM_EPI_MAJOR_K : GEMM_EPI_MAJOR_N,
+                 CDN ? GEMM_EPI_MAJOR_N : GEMM_EPI_MAJOR_M,
+                 CF::BM,
+                 CF::BN,
+                 CF::BK,
+                 CF::THREADS,
+                 CF::LDS_BYTES,
+                 &launch<CF>};
+}
+
+using namespace gemm_epi;
+const Variant kVariants[] = {
+    make_variant<T_F16, true, true, true>("f16_kk_n_256x256x64"),
+    make_variant<T_F16, true, true, false>("f16_kk_m_256x256x64"),
+    make_variant<T_BF16, true, true, true>("bf16_kk_n_256x256x64"),
+    make_variant<T_BF16, true, true, false>("bf16_kk_m_256x256x64"),
+    make_variant<T_E4M3, true, true, true>("e4m3_kk_n_256x256x128"),
+    make_variant<T_E4M3, true, true, false>("e4m3_kk_m_256x256x128"),
+    make_variant<T_I8, true, true, true>("i8_kk_n_256x256x128"),
+    make_variant<T_I8, true, true, false>("i8_kk_m_256x256x128"),
+    make_variant<T_I8, false, true, true>("i8_mk_n_256x256x128"),
+    make_variant<T_I8, false, true, false>("i8_mk_m_256x256x128"),
+};
+constexpr int kNumVariants = (int)(sizeof kVariants / sizeof kVariants[0]);
+
+int elem_bytes(int t) {
+  switch (t) {
+    case GEMM_EPI_F16:
+    case GEMM_EPI_BF16: return 2;
+    case GEMM_EPI_E4M3:
+    case GEMM_EPI_I8: return 1;
+    case GEMM_EPI_F32:
+    case GEMM_EPI_I32: return 4;
+    default: return 0;
+  }
+}
+
+bool is_float_out(int t) { return t == GEMM_EPI_F16 || t == GEMM_EPI_BF16 || t == GEMM_EPI_F32; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+}  // namespace
+
+struct gemm_epi_handle {
+  gemm_epi_desc desc;
+  int variant;
+  int grid;
+  int cus;
+  int device;
+  int64_t tiles_m, tiles_n, tiles;
+  int group_m;
+};
+
+// Static validation: everything that needs no device.
+static int validate_desc(const gemm_epi_desc* d) {
+  if (!d) return fail(GEMM_EPI_ERR_INVALID_ARG, "desc is NULL");
+  if (d->M < 1 || d->N < 1 || d->K < 1 || d->L < 1)
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "M, N, K, L must be >= 1 (got %lld %lld %lld %lld)",
+                (long long)d->M, (long long)d->N, (long long)d->K, (long long)d->L);
+  int64_t mk, nk, mn, t;
+  if (!mul_ok(d->M, d->K, &mk) || !mul_ok(mk, d->L, &t) || !mul_ok(d->N, d->K, &nk) ||
+      !mul_ok(nk, d->L, &t) || !mul_ok(d->M, d->N, &mn) || !mul_ok(mn, d->L, &t) ||
+      !mul_ok(t, 4, &t))
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "tensor byte sizes overflow int64");
+  if (d->a_major != GEMM_EPI_MAJOR_K && d->a_major != GEMM_EPI_MAJOR_M)
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "a_major must be K or M");
+  if (d->b_major != GEMM_EPI_MAJOR_K && d->b_major != GEMM_EPI_MAJOR_N)
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "b_major must be K or N");
+  if (d->cd_major != GEMM_EPI_MAJOR_N && d->cd_major != GEMM_EPI_MAJOR_M)
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "cd_major must be N or M");
+  const int ab = d->ab_dtype;
+  if (ab != GEMM_EPI_F16 && ab != GEMM_EPI_BF16 && ab != GEMM_EPI_E4M3 && ab != GEMM_EPI_I8)
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "ab_dtype must be F16, BF16, E4M3 or I8");
+  const bool int_path = ab == GEMM_EPI_I8;
+  auto out_ok = [&](int t, bool allow_none) {
+    if (t == GEMM_EPI_NONE) return allow_none;
+    return int_path ? t == GEMM_EPI_I32 : is_float_out(t);
+  };
+  for (int t : {d->c_dtype, d->x_dtype, d->d_dtype, d->y_dtype})
+    if (t < GEMM_EPI_NONE || t > GEMM_EPI_I32)
+      return fail(GEMM_EPI_ERR_INVALID_ARG, "unknown dtype code %d", t);
+  if (!out_ok(d->c_dtype, true) || !out_ok(d->x_dtype, true) || !out_ok(d->d_dtype, false) ||
+      !out_ok(d->y_dtype, true))
+    return fail(GEMM_EPI_ERR_UNSUPPORTED,
+                int_path ? "int8 A/B need int32 C/X/D/Y (D required)"
+                         : "float A/B need F16/BF16/F32 C/X/D/Y (D required)");
+  // 16-byte rule on the contiguous extent of every tensor.
+  const int es = elem_bytes(ab);
+  const int64_t a_contig = d->a_major == GEMM_EPI_MAJOR_K ? d->K : d->M;
+  const int64_t b_contig = d->b_major == GEMM_EPI_MAJOR_K ? d->K : d->N;
+  if ((a_contig * es) % 16 || (b_contig * es) % 16)
+    return fail(GEMM_EPI_ERR_ALIGNMENT,
+                "contiguous extent of A (%lld) and B (%lld) must be a multiple of 16 bytes",
+                (long long)a_contig, (long long)b_contig);
+  const int64_t cd_contig = d->cd_major == GEMM_EPI_MAJOR_N ? d->N : d->M;
+  for (int t : {d->c_dtype, d->x_dtype, d->d_dtype, d->y_dtype})
+    if (t != GEMM_EPI_NONE && (cd_contig * elem_bytes(t)) % 16)
+      return fail(GEMM_EPI_ERR_ALIGNMENT,
+                  "contiguous extent %lld of C/X/D/Y is not a multiple of 16 bytes",
+                  (long long)cd_contig);
+  return GEMM_EPI_OK;
+}
+
+static bool variant_fits(const Variant& v, const gemm_epi_desc* d) {
+  return v.ab == d->ab_dtype && v.a_major == d->a_major && v.b_major == d->b_major &&
+         v.cd_major == d->cd_major;
+}
+
+extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
+                                       gemm_epi_handle** out) {
+  g_last_error[0] = 0;
+  if (!out) return fail(GEMM_EPI_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = validate_desc(desc);
+  if (rc) return rc;
+  if (variant < -1 || variant >= kNumVariants)
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "variant %d out of range", variant);
+  if (variant == -1) {
+    for (int i = 0; i < kNumVariants; ++i)
+      if (variant_fits(kVariants[i], desc)) {
+        variant = i;
+        break;
+      }
+    if (variant == -1)
+      return fail(GEMM_EPI_ERR_UNSUPPORTED,
+                  "no kernel for this dtype/majorness combination (ab=%d a=%d b=%d cd=%d)",
+                  desc->ab_dtype, desc->a_major, desc->b_major, desc->cd_major);
+  } else if (!variant_fits(kVariants[variant], desc)) {
+    return fail(GEMM_EPI_ERR_UNSUPPORTED, "variant %s cannot run this problem",
+                kVariants[variant].name);
+  }
+  const Variant& v = kVariants[variant];
+  // Buffer offsets within one tile's rows are 32-bit.
+  const int es = elem_bytes(desc->ab_dtype);
+  if ((int64_t)v.bm * desc->K * es >= (int64_t(1) << 31) ||
+      (int64_t)v.bn * desc->K * es >= (int64_t(1) << 31))
+    return fail(GEMM_EPI_ERR_UNSUPPORTED, "K too large for 32-bit tile offsets");
+
+  // Device query (the only part that needs a GPU).
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(GEMM_EPI_ERR_DEVICE, "hipGetDevice failed");
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return fail(GEMM_EPI_ERR_DEVICE, "hipGetDeviceProperties failed");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(GEMM_EPI_ERR_DEVICE, "device %d is %s, this library is built for gfx950", dev,
+                prop.gcnArchName);
+
+  gemm_epi_handle* h = new (std::nothrow) gemm_epi_handle;
+  if (!h) return fail(GEMM_EPI_ERR_INVALID_ARG, "out of host memory");
+  h->desc = *desc;
+  h->variant = variant;
+  h->device = dev;
+  h->cus = prop.multiProcessorCount;
+  h->tiles_m = (desc->M + v.bm - 1) / v.bm;
+  h->tiles_n = (desc->N + v.bn - 1) / v.bn;
+  h->tiles = h->tiles_m * h->tiles_n * desc->L;
+  h->group_m = 4;
+  const int64_t occupancy = 1;  // one 256x256 workgroup per compute unit
+  h->grid = (int)std::min<int64_t>(h->tiles, (int64_t)h->cus * occupancy);
+  *out = h;
+  return GEMM_EPI_OK;
+}
+
+extern "C" int gemm_epi_create(const gemm_epi_desc* desc, gemm_epi_handle** out) {
+  return gemm_epi_create_variant(desc, -1, out);
+}
+
+static bool integral_24(float v) {
+  return std::isfinite(v) && std::nearbyint(v) == v && std::fabs(v) <= 16777216.0f;
+}
+
+extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void* B, const void* C,
+                            const void* X, void* D, void* Y, float alpha, float beta,
+                            float x_factor, void* stream) {
+  g_last_error[0] = 0;
+  if (!h) return fail(GEMM_EPI_ERR_INVALID_ARG, "handle is NULL");
+  const gemm_epi_desc& d = h->desc;
+  if (!A || !B || !D) return fail(GEMM_EPI_ERR_INVALID_ARG, "A, B and D are required");
+  const bool use_c = d.c_dtype != GEMM_EPI_NONE && beta != 0.0f;
+  const bool use_x = d.x_dtype != GEMM_EPI_NONE && x_factor != 0.0f;
+  if (use_c && !C) return fail(GEMM_EPI_ERR_INVALID_ARG, "C is NULL but beta != 0");
+  if (use_x && !X) return fail(GEMM_EPI_ERR_INVALID_ARG, "X is NULL but x_factor != 0");
+  if ((d.y_dtype != GEMM_EPI_NONE) != (Y != nullptr))
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "Y must be given exactly when y_dtype is set");
+  for (const void* ptr : {A, B, (const void*)D, use_c ? C : nullptr, use_x ? X : nullptr,
+                          (const void*)Y})
+    if (((uintptr_t)ptr) & 15u) return fail(GEMM_EPI_ERR_ALIGNMENT, "pointer %p is not 16-byte aligned", ptr);
+  const bool int_path = d.ab_dtype == GEMM_EPI_I8;
+  if (int_path && !(integral_24(alpha) && integral_24(beta) && integral_24(x_factor)))
+    return fail(GEMM_EPI_ERR_UNSUPPORTED,
+                "int32 outputs need integral alpha, beta, x_factor with |value| <= 2^24");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
+    return fail(GEMM_EPI_ERR_DEVICE, "current device %d is not the handle's device %d", dev,
+                h->device);
+
+  Params p;
+  p.A = A;
+  p.B = B;
+  p.C = use_c ? C : nullptr;
+  p.X = use_x ? X : nullptr;
+  p.D = D;
+  p.Y = Y;
+  p.M = d.M;
+  p.N = d.N;
+  p.K = d.K;
+  p.tiles_total = h->tiles;
+  p.L = (int32_t)d.L;
+  p.tiles_m = (int32_t)h->tiles_m;
+  p.tiles_n = (int32_t)h->tiles_n;
+  p.group_m = h->group_m;
+  p.c_dtype = use_c ? d.c_dtype : GEMM_EPI_NONE;
+  p.x_dtype = use_x ? d.x_dtype : GEMM_EPI_NONE;
+  p.d_dtype = d.d_dtype;
+  p.y_dtype = d.y_dtype;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.xf = x_factor;
+  p.ialpha = int_path ? (int32_t)alpha : 0;
+  p.ibeta = int_path ? (int32_t)beta : 0;
+  p.ix = int_path ? (int32_t)x_factor : 0;
+  p.xcd_remap = (h->grid % 8 == 0) ? 1 : 0;
+
+  (void)hipGetLastError();  // clear a stale error so the check below is ours
+  kVariants[h->variant].launch(p, h->grid, (hipStream_t)stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GEMM_EPI_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return GEMM_EPI_OK;
+}
+
+extern "C" int gemm_epi_destroy(gemm_epi_handle* h) {
+  delete h;
+  return GEMM_EPI_OK;
+}
+
+extern "C" int gemm_epi_get_plan(const gemm_epi_handle* h, gemm_epi_plan* out) {
+  if (!h || !out) return fail(GEMM_EPI_ERR_INVALID_ARG, "NULL argument");
+  const Variant& v = kVariants[h->variant];
+  std::memset(out, 0, sizeof *out);
+  out->variant = h->variant;
+  out->tile_m = v.bm;
+  out->tile_n = v.bn;
+  out->tile_k = v.bk;
+  out->threads = v.threads;
+  out->grid = h->grid;
+  out->tiles = h->tiles;
+  out->lds_bytes = v.lds;
+  out->cus = h->cus;
+  std::snprintf(out->name, sizeof out->name, "%s", v.name);
+  return GEMM_EPI_OK;
+}
+
+extern "C" int gemm_epi_variant_count(void) { return kNumVariants; }
+
+extern "C" const char* gemm_epi_variant_name(int variant) {
+  if (variant < 0 || variant >= kNumVariants) return nullptr;
+  return kVariants[variant].name;
+}
+
+extern "C" const char* gemm_epi_status_string(int code) {
+  switch (code) {
+    case GEMM_EPI_OK: return "success";
+    case GEMM_EPI_ERR_INVALID_ARG: return "invalid argument";
+    case GEMM_EPI_ERR_UNSUPPORTED: return "unsupported problem";
+    case GEMM_EPI_ERR_ALIGNMENT: return "alignment requirement not met";
+    case GEMM_EPI_ERR_DEVICE: return "device error";
+    case GEMM_EPI_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char* gemm_epi_last_error(void) { return g_last_error; }

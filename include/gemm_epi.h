@@ -1,0 +1,158 @@
+/*
+ * gemm_epi.h -- C ABI of the MI355X (gfx950) fused-epilogue batched GEMM.
+ *
+ * The operation (CuTe DSL example "custom_epilogue_dense_gemm.py", module
+ * docstring, "Tensor dimensions" and the epilogue formula it states):
+ *
+ *     Y[l] = A[l] . B[l]^T
+ *     D[l] = alpha * (A[l] . B[l]^T) + beta * C[l] + x_factor * X[l]
+ *
+ * A is M x K x L, B is N x K x L, C, X, D and Y are M x N x L.  Inputs are
+ * fp16, bf16, fp8 (OCP e4m3fn) or int8; accumulation is fp32, or int32 for
+ * int8.  The epilogue runs in fp32 (int32 for int8) on the unrounded
+ * accumulator and rounds to nearest-even into the output types.  No ReLU is
+ * applied: the docstring's formula has none.
+ *
+ * Conventions (taken from the Blackwell pipeline API card, "Host side" and
+ * "Device side", and the CuTe DSL example's "Constraints"):
+ *   - every entry point returns a status code; gemm_epi_status_string() maps
+ *     it to text and gemm_epi_last_error() gives the calling thread's detail;
+ *   - everything that can be validated without the device is validated in
+ *     gemm_epi_create(); nothing ever falls back silently to another path;
+ *   - the contiguous extent of every tensor is a multiple of 16 bytes and
+ *     every base pointer is 16-byte aligned;
+ *   - C, X, D and Y share one majorness; A and B share one element type;
+ *   - one immutable handle per problem shape, reusable from any host thread
+ *     and on any stream of the device it was created on.
+ *
+ * Layout: every tensor is packed, batch index outermost.  The majorness
+ * letter names the contiguous mode:
+ *   A  'K': A[l][m][k] at l*M*K + m*K + k     'M': at l*M*K + k*M + m
+ *   B  'K': B[l][n][k] at l*N*K + n*K + k     'N': at l*N*K + k*N + n
+ *   CD 'N': T[l][m][n] at l*M*N + m*N + n     'M': at l*M*N + n*M + m
+ *
+ * Memory ownership: all tensor pointers are device pointers owned by the
+ * caller, which keeps them alive until the work queued on the stream has
+ * finished.  The library allocates no device memory; a handle is a small
+ * host object.
+ */
+#ifndef GEMM_EPI_H
+#define GEMM_EPI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  GEMM_EPI_OK = 0,
+  GEMM_EPI_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, bad enum */
+  GEMM_EPI_ERR_UNSUPPORTED = 2, /* valid request this library does not run */
+  GEMM_EPI_ERR_ALIGNMENT = 3,   /* 16-byte rule broken (extent or pointer) */
+  GEMM_EPI_ERR_DEVICE = 4,      /* no usable gfx950 device / HIP query failed */
+  GEMM_EPI_ERR_LAUNCH = 5       /* the kernel launch itself failed */
+};
+
+/* Element types.  GEMM_EPI_NONE marks an absent C, X or Y. */
+enum {
+  GEMM_EPI_NONE = 0,
+  GEMM_EPI_F16 = 1,  /* IEEE binary16 */
+  GEMM_EPI_BF16 = 2, /* bfloat16 */
+  GEMM_EPI_E4M3 = 3, /* OCP fp8 e4m3fn (A/B only) */
+  GEMM_EPI_I8 = 4,   /* int8 (A/B only) */
+  GEMM_EPI_F32 = 5,  /* binary32 (C/X/D/Y only) */
+  GEMM_EPI_I32 = 6   /* int32 (C/X/D/Y only, with int8 inputs) */
+};
+
+/* Majorness: the contiguous mode of a tensor (see the table above). */
+enum { GEMM_EPI_MAJOR_K = 0, GEMM_EPI_MAJOR_M = 1, GEMM_EPI_MAJOR_N = 2 };
+
+typedef struct gemm_epi_desc {
+  int64_t M, N, K, L;  /* all >= 1 */
+  int32_t a_major;     /* GEMM_EPI_MAJOR_K or _M */
+  int32_t b_major;     /* GEMM_EPI_MAJOR_K or _N */
+  int32_t cd_major;    /* GEMM_EPI_MAJOR_N or _M: C, X, D and Y alike */
+  int32_t ab_dtype;    /* F16, BF16, E4M3 or I8 */
+  int32_t c_dtype;     /* NONE, or F16/BF16/F32 (float A/B), I32 (int8 A/B) */
+  int32_t x_dtype;     /* as c_dtype */
+  int32_t d_dtype;     /* F16/BF16/F32 (float A/B) or I32 (int8 A/B) */
+  int32_t y_dtype;     /* NONE, or as d_dtype */
+} gemm_epi_desc;
+
+typedef struct gemm_epi_handle gemm_epi_handle;
+
+/* What a handle will launch (for reports and tuning). */
+typedef struct gemm_epi_plan {
+  int32_t variant;      /* index into the variant table */
+  int32_t tile_m, tile_n, tile_k; /* workgroup tile; tile_k in elements */
+  int32_t threads;      /* threads per workgroup */
+  int32_t grid;         /* persistent workgroups launched */
+  int64_t tiles;        /* L * ceil(M/tile_m) * ceil(N/tile_n) */
+  int32_t lds_bytes;    /* LDS per workgroup */
+  int32_t cus;          /* compute units of the device */
+  char name[64];        /* kernel variant name */
+} gemm_epi_plan;
+
+/*
+ * Validate a problem and build an immutable plan for it.
+ * desc : problem description (read only, not retained).
+ * out  : receives the new handle, or NULL on any error.
+ * Static checks come first and need no device: sizes >= 1 and the packed
+ * element counts within int64; dtype combinations; contiguous extents a
+ * multiple of 16 bytes; one majorness for C/D/X/Y (by construction).  Then
+ * the current HIP device is queried once (compute units, architecture);
+ * anything but gfx950 is GEMM_EPI_ERR_DEVICE.  Allocates only the host
+ * object.  Returns GEMM_EPI_OK or an error code.
+ */
+int gemm_epi_create(const gemm_epi_desc* desc, gemm_epi_handle** out);
+
+/*
+ * As gemm_epi_create, but forces kernel variant `variant` (0 <=
+ * variant < gemm_epi_variant_count()); -1 picks the default variant.  A
+ * variant that cannot run the problem is GEMM_EPI_ERR_UNSUPPORTED.
+ */
+int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
+                            gemm_epi_handle** out);
+
+/*
+ * Enqueue one fused GEMM on `stream` (a hipStream_t; NULL is the null
+ * stream) and return without waiting.
+ * A, B, D  : required device pointers.
+ * C, X     : read only; may be NULL only if their dtype is NONE or their
+ *            scalar (beta, x_factor) is 0, in which case they are not read.
+ * Y        : NULL exactly when y_dtype is NONE.
+ * alpha, beta, x_factor : fp32 scalars.  With int32 outputs they must be
+ *            integers of magnitude <= 2^24 (the epilogue is then exact int32
+ *            arithmetic), else GEMM_EPI_ERR_UNSUPPORTED.
+ * Every pointer must be 16-byte aligned.  Outputs must not overlap inputs;
+ * C and X are never written.  Checks happen before anything is enqueued;
+ * GEMM_EPI_ERR_LAUNCH reports a failed launch.  Faults inside the kernel
+ * surface at the caller's next synchronisation.  Thread-safe.
+ */
+int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void* B,
+                 const void* C, const void* X, void* D, void* Y, float alpha,
+                 float beta, float x_factor, void* stream);
+
+/* Free a handle (NULL is fine).  No run on it may still be being enqueued. */
+int gemm_epi_destroy(gemm_epi_handle* h);
+
+/* Fill *out with what the handle launches. */
+int gemm_epi_get_plan(const gemm_epi_handle* h, gemm_epi_plan* out);
+
+/* Number of compiled kernel variants and the name of one. */
+int gemm_epi_variant_count(void);
+const char* gemm_epi_variant_name(int variant);
+
+/* Static text for a status code ("unknown status" for anything else). */
+const char* gemm_epi_status_string(int code);
+
+/* Detail of the calling thread's last error ("" if none). */
+const char* gemm_epi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_EPI_H */

@@ -1,0 +1,126 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry
+point, and its static validation returns the documented codes before any
+device query."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import beta_epilogue_amd as ge
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_epi.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_epi_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ge.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), "missing export " + n
+
+
+def test_status_strings():
+    assert ge.status_string(0) == "success"
+    for c in range(1, 6):
+        assert ge.status_string(c) not in ("success", "unknown status")
+    assert ge.status_string(99) == "unknown status"
+
+
+def test_variant_table():
+    n = ge.gemm_epi_variant_count()
+    assert n >= 10
+    names = [ge.gemm_epi_variant_name(i) for i in range(n)]
+    assert len(set(names)) == n
+    assert ge.gemm_epi_variant_name(-1) is None and ge.gemm_epi_variant_name(n) is None
+
+
+def _create(**kw):
+    base = dict(M=256, N=256, K=256, L=1, ab="f16", c="f16", x="f16", d="f16", y="f16")
+    base.update(kw)
+    M, N, K, L = base.pop("M"), base.pop("N"), base.pop("K"), base.pop("L")
+    desc = ge.make_desc(M, N, K, L, **base)
+    h = ctypes.c_void_p(1234)
+    rc = ge.lib().gemm_epi_create(ctypes.byref(desc), ctypes.byref(h))
+    return rc, h.value
+
+
+BAD = [
+    (dict(M=0), ge.GEMM_EPI_ERR_INVALID_ARG),
+    (dict(K=-8), ge.GEMM_EPI_ERR_INVALID_ARG),
+    (dict(L=0), ge.GEMM_EPI_ERR_INVALID_ARG),
+    (dict(M=2**40, N=2**40), ge.GEMM_EPI_ERR_INVALID_ARG),       # int64 overflow
+    (dict(ab="f32"), ge.GEMM_EPI_ERR_INVALID_ARG),                # not an A/B type
+    (dict(ab="i8"), ge.GEMM_EPI_ERR_UNSUPPORTED),                 # int8 needs int32 outs
+    (dict(ab="f16", d="i32"), ge.GEMM_EPI_ERR_UNSUPPORTED),
+    (dict(ab="f16", c="e4m3"), ge.GEMM_EPI_ERR_UNSUPPORTED),
+    (dict(d=None), ge.GEMM_EPI_ERR_UNSUPPORTED),                  # D required
+    (dict(K=100), ge.GEMM_EPI_ERR_ALIGNMENT),                     # 200 B rows
+    (dict(N=100), ge.GEMM_EPI_ERR_ALIGNMENT),                     # f16 C/D rows
+    (dict(ab="e4m3", K=8), ge.GEMM_EPI_ERR_ALIGNMENT),            # 8 B rows
+    (dict(a_major="M", M=100), ge.GEMM_EPI_ERR_ALIGNMENT),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_create_static_validation(kw, code):
+    rc, h = _create(**kw)
+    assert rc == code, (rc, ge.last_error())
+    assert h is None  # *out cleared on error
+    assert ge.last_error()
+
+
+def test_create_bad_enums():
+    desc = ge.make_desc(256, 256, 256, 1, ab="f16", d="f16")
+    desc.a_major = 2  # 'N' is not a majorness of A
+    h = ctypes.c_void_p()
+    assert ge.lib().gemm_epi_create(ctypes.byref(desc), ctypes.byref(h)) == \
+        ge.GEMM_EPI_ERR_INVALID_ARG
+    desc = ge.make_desc(256, 256, 256, 1, ab="f16", d="f16")
+    desc.d_dtype = 17
+    assert ge.lib().gemm_epi_create(ctypes.byref(desc), ctypes.byref(h)) == \
+        ge.GEMM_EPI_ERR_INVALID_ARG
+    assert ge.lib().gemm_epi_create(None, ctypes.byref(h)) == ge.GEMM_EPI_ERR_INVALID_ARG
+    assert ge.lib().gemm_epi_create(ctypes.byref(desc), None) == ge.GEMM_EPI_ERR_INVALID_ARG
+
+
+def test_unsupported_layout_is_an_error_not_a_fallback():
+    rc, _ = _create(b_major="N")  # no N-major B kernel yet
+    assert rc in (ge.GEMM_EPI_ERR_UNSUPPORTED, ge.GEMM_EPI_ERR_DEVICE)
+    if rc == ge.GEMM_EPI_ERR_UNSUPPORTED:
+        assert "no kernel" in ge.last_error()
+
+
+def test_run_and_plan_reject_null_handle():
+    assert ge.lib().gemm_epi_run(None, 16, 16, None, None, 16, None, 1.0, 0.0, 0.0,
+                                 None) == ge.GEMM_EPI_ERR_INVALID_ARG
+    p = ge.gemm_epi_plan()
+    assert ge.lib().gemm_epi_get_plan(None, ctypes.byref(p)) == ge.GEMM_EPI_ERR_INVALID_ARG
+    assert ge.lib().gemm_epi_destroy(None) == ge.GEMM_EPI_OK
+
+
+def test_valid_problem_needs_a_device_here():
+    """With no GPU, a valid problem passes validation and stops at the device
+    query (never a silent CPU path)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc, h = _create()
+    assert rc == ge.GEMM_EPI_ERR_DEVICE and h is None
+
+
+def test_product_does_not_reference_the_oracle():
+    """The product package never imports or links the oracle."""
+    pkg = os.path.join(ROOT, "beta_epilogue_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f

@@ -1,0 +1,149 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every test here needs an MI355X and the built library.  Inputs come from the
+seeded generators in ``synth``; expected values only ever come from the
+oracle.  Each case prints its name and shape before touching the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity import parity_full, parity_sampled, run_gpu, to_f64
+
+pytestmark = pytest.mark.gpu
+
+CFG = synth.CONFIGS
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def small(p, M, N, K, L=None):
+    return p.replace(name=p.name + "_small", M=M, N=N, K=K, L=L or p.L)
+
+
+# Scaled-down versions of the five workloads: same types, layouts, scalars and
+# value distributions; several 256x256 tiles with ragged M, N and K tails.
+SMALL_CASES = [
+    (CFG[0], True),                                  # 128^3, exact by construction
+    (small(CFG[1], 592, 528, 392), False),           # bf16 -> f32
+    (small(CFG[2], 600, 520, 392), False),           # f16, C X D Y
+    (small(CFG[3], 592, 528, 400, L=2), False),      # int8, A M-major, batched
+    (small(CFG[4], 600, 528, 400), False),           # e4m3 -> f16
+]
+
+
+@pytest.mark.parametrize("p,exact", SMALL_CASES, ids=[c[0].name for c in SMALL_CASES])
+def test_parity_small_full_oracle(p, exact):
+    _say("case", p.name, p.M, p.N, p.K, p.L)
+    (ed, ey), plan = parity_full(p, exact=exact)
+    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4], ids=[c.name for c in CFG[1:]])
+def test_parity_full_size_sampled(i):
+    """The benchmark shapes, in the launch configuration the bench times."""
+    p = CFG[i]
+    _say("case", p.name, p.M, p.N, p.K, p.L)
+    (ed, ey), plan, npts = parity_sampled(p)
+    _say("  plan", plan["name"], "grid", plan["grid"], "points", npts,
+         "err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_config0_bit_exact():
+    p = CFG[0]
+    _say("case", p.name)
+    (ed, ey), plan = parity_full(p, exact=True)
+    assert ed == 0.0
+
+
+EDGE = [
+    CFG[2].replace(name="one_row", M=1, N=8, K=8, L=1),
+    CFG[2].replace(name="tiny_batched", M=3, N=16, K=24, L=3),
+    CFG[2].replace(name="k_tail_only", M=256, N=256, K=72, L=1),
+    CFG[2].replace(name="cd_mmajor_f16", M=264, N=136, K=136, L=2, cd_major="M"),
+    CFG[1].replace(name="cd_mmajor_f32", M=520, N=260, K=200, cd_major="M", seed=6100),
+    CFG[1].replace(name="bf16_out", M=300, N=264, K=128, d="bf16", c="bf16", seed=6200),
+    CFG[1].replace(name="y_only_f32", M=130, N=260, K=64, y="f32", beta=0.0, c=None,
+                   seed=6300),
+    CFG[4].replace(name="e4m3_mmajor_cd", M=264, N=296, K=160, cd_major="M", seed=6400),
+    CFG[4].replace(name="e4m3_xy", M=260, N=264, K=256, x="bf16", y="f32", x_factor=-1.5,
+                   seed=6500),
+    CFG[3].replace(name="i8_kmajor_xy", M=260, N=264, K=160, L=1, a_major="K", x="i32",
+                   y="i32", alpha=-3.0, beta=2.0, x_factor=5.0, dist_x="i1000", seed=6600),
+    CFG[3].replace(name="i8_mmajor_cdm", M=272, N=260, K=176, L=2, cd_major="M", seed=6700),
+    CFG[3].replace(name="i8_mmajor_ktail", M=48, N=40, K=48, L=1, seed=6800),
+    CFG[2].replace(name="f16_large_k", M=256, N=512, K=4104, seed=6900),
+]
+
+
+@pytest.mark.parametrize("p", EDGE, ids=[e.name for e in EDGE])
+def test_parity_edge_cases(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
+    (ed, ey), plan = parity_full(p)
+    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_beta_zero_does_not_read_c():
+    """beta = 0 skips C: NaN in C cannot reach D (C is given but unread)."""
+    p = CFG[2].replace(name="beta0_nan_c", M=256, N=264, K=64, beta=0.0, x_factor=0.0)
+    ins = synth.make_inputs(p)
+    ins["C"] = torch.full_like(ins["C"], float("nan"))
+    ins["X"] = torch.full_like(ins["X"], float("nan"))
+    _say("case", p.name)
+    D, Y, _ = run_gpu(p, ins)
+    assert np.all(np.isfinite(to_f64(D)))
+    (ed, ey), _ = parity_full(p, ins=ins)
+
+
+def test_every_variant_runs():
+    """Each compiled kernel variant passes parity on a problem it accepts."""
+    import beta_epilogue_amd as ge
+    names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
+    base = {
+        "f16": CFG[2].replace(M=264, N=272, K=136, L=2),
+        "bf16": CFG[1].replace(M=264, N=272, K=136, L=2),
+        "e4m3": CFG[4].replace(M=264, N=272, K=144, L=2),
+        "i8": CFG[3].replace(M=272, N=264, K=144, L=2),
+    }
+    for i, name in enumerate(names):
+        ab, layout = name.split("_")[0], name.split("_")[1:3]
+        p = base[ab].replace(name="variant_" + name,
+                             a_major="K" if layout[0][0] == "k" else "M",
+                             b_major="K" if layout[0][1] == "k" else "N",
+                             cd_major=layout[1].upper())
+        _say("variant", i, name)
+        (ed, ey), plan = parity_full(p, variant=i)
+        assert plan["name"] == name
+
+
+def test_run_rejects_misaligned_pointer():
+    import beta_epilogue_amd as ge
+    p = CFG[2].replace(M=64, N=64, K=64)
+    g = ge.FusedGemm(p.M, p.N, p.K, ab="f16", c="f16", x="f16", d="f16", y="f16")
+    a = torch.zeros(64 * 64 + 8, dtype=torch.float16, device="cuda")
+    d = torch.zeros(64 * 64, dtype=torch.float16, device="cuda")
+    with pytest.raises(ge.GemmEpiError) as e:
+        ge.gemm_epi_run(g.handle, a.data_ptr() + 2, a.data_ptr(), None, None,
+                        d.data_ptr(), d.data_ptr(), 1.0, 0.0, 0.0, None)
+    assert e.value.code == ge.GEMM_EPI_ERR_ALIGNMENT
+    with pytest.raises(ge.GemmEpiError) as e:  # Y required: y_dtype is set
+        ge.gemm_epi_run(g.handle, a.data_ptr(), a.data_ptr(), None, None,
+                        d.data_ptr(), None, 1.0, 0.0, 0.0, None)
+    assert e.value.code == ge.GEMM_EPI_ERR_INVALID_ARG
+    g.close()
+
+
+def test_int_scalars_must_be_integral():
+    import beta_epilogue_amd as ge
+    g = ge.FusedGemm(64, 64, 64, ab="i8", c="i32", d="i32")
+    a = torch.zeros(64 * 64, dtype=torch.int8, device="cuda")
+    d = torch.zeros(64 * 64, dtype=torch.int32, device="cuda")
+    with pytest.raises(ge.GemmEpiError) as e:
+        g(a, a, d, D=d, alpha=1.5, beta=1.0)
+    assert e.value.code == ge.GEMM_EPI_ERR_UNSUPPORTED
+    g.close()
