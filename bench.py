@@ -100,6 +100,9 @@ def main():
     ap.add_argument("--variant", type=int, default=-1)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes "
+                         "--steps times (scales the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -113,6 +116,17 @@ def main():
     import torch
     import synth
     import beta_epilogue_amd as ge
+
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        src.fill_(7)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_calibration, "steps": args.steps}))
+        return
 
     p = synth.CONFIGS[args.config]
     print("bench: workload %s M=%d N=%d K=%d L=%d" % (p.name, p.M, p.N, p.K, p.L),

@@ -309,6 +309,12 @@ __device__ __forceinline__ void store4_f(void* p, int dt, int64_t i, v4f v) {
   }
 }
 
+// Accumulator element as the 32-bit pattern stored in LDS.  (The element is
+// read into a scalar first: bit-casting a vector-element lvalue directly
+// reads element 0 with this compiler.)
+__device__ __forceinline__ float acc_bits(float v) { return v; }
+__device__ __forceinline__ float acc_bits(int v) { return __int_as_float(v); }
+
 template <class CF, class ACC>
 __device__ __forceinline__ void epilogue(const Params& p, const ACC (&acc)[CF::FM][CF::FN], char* lds,
                                          int wave, int lane, int l, int mw, int nw) {
@@ -331,8 +337,8 @@ __device__ __forceinline__ void epilogue(const Params& p, const ACC (&acc)[CF::F
           for (int v = 0; v < 16; ++v) {
             const int line = ii * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
             const int col = j * 32 + l32;
-            *(float*)(lds + region + (line * EL::PITCH + col) * 4) =
-                __builtin_bit_cast(float, acc[2 * h + ii][j][v]);
+            const auto e = acc[2 * h + ii][j][v];
+            *(float*)(lds + region + (line * EL::PITCH + col) * 4) = acc_bits(e);
           }
     } else {
 #pragma unroll
@@ -344,10 +350,9 @@ __device__ __forceinline__ void epilogue(const Params& p, const ACC (&acc)[CF::F
             const int line = jj * 32 + l32;
             const int row = i * 32 + v4 * 8 + half * 4;
             const ACC& a = acc[i][2 * h + jj];
-            const v4f w = {__builtin_bit_cast(float, a[v4 * 4 + 0]),
-                           __builtin_bit_cast(float, a[v4 * 4 + 1]),
-                           __builtin_bit_cast(float, a[v4 * 4 + 2]),
-                           __builtin_bit_cast(float, a[v4 * 4 + 3])};
+            const auto e0 = a[v4 * 4 + 0], e1 = a[v4 * 4 + 1];
+            const auto e2 = a[v4 * 4 + 2], e3 = a[v4 * 4 + 3];
+            const v4f w = {acc_bits(e0), acc_bits(e1), acc_bits(e2), acc_bits(e3)};
             *(v4f*)(lds + region + (line * EL::PITCH + row) * 4) = w;
           }
     }
