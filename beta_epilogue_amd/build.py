@@ -16,7 +16,7 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # keep packed-fp32 instructions out of generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wno-pass-failed",
+    "-Wno-pass-failed", "-Wno-inline-asm",
 ]
 
 

@@ -50,14 +50,13 @@ void launch(const Params& p, int grid, hipStream_t s) {
   hipLaunchKernelGGL(gemm_epi::gemm_epi_kernel<CF>, dim3(grid), dim3(CF::THREADS), 0, s, p);
 }
 
-template <int AB, bool AK, bool BK, bool CDN>
+template <class CF>
 constexpr Variant make_variant(const char* name) {
-  using CF = gemm_epi::Cfg<AB, AK, BK, CDN>;
   return Variant{name,
-                 AB,
-                 AK ? GEMM_EPI_MAJOR_K : GEMM_EPI_MAJOR_M,
-                 BK ? GEMM_EPI_MAJOR_K : GEMM_EPI_MAJOR_N,
-                 CDN ? GEMM_EPI_MAJOR_N : GEMM_EPI_MAJOR_M,
+                 CF::AB,
+                 CF::A_KMAJOR ? GEMM_EPI_MAJOR_K : GEMM_EPI_MAJOR_M,
+                 CF::B_KMAJOR ? GEMM_EPI_MAJOR_K : GEMM_EPI_MAJOR_N,
+                 CF::CD_NMAJOR ? GEMM_EPI_MAJOR_N : GEMM_EPI_MAJOR_M,
                  CF::BM,
                  CF::BN,
                  CF::BK,
@@ -67,18 +66,39 @@ constexpr Variant make_variant(const char* name) {
 }
 
 using namespace gemm_epi;
+// Cfg<ab, A K-major, B K-major, C/D N-major, BM, BN, ROWB, waves M, waves N, stages>
+// The first variant that fits a problem is its default.
+#define V(AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, NAME) \
+  make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S>>(NAME)
+#define VR(AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, NAME) \
+  make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, 1>>(NAME)
 const Variant kVariants[] = {
-    make_variant<T_F16, true, true, true>("f16_kk_n_256x256x64"),
-    make_variant<T_F16, true, true, false>("f16_kk_m_256x256x64"),
-    make_variant<T_BF16, true, true, true>("bf16_kk_n_256x256x64"),
-    make_variant<T_BF16, true, true, false>("bf16_kk_m_256x256x64"),
-    make_variant<T_E4M3, true, true, true>("e4m3_kk_n_256x256x128"),
-    make_variant<T_E4M3, true, true, false>("e4m3_kk_m_256x256x128"),
-    make_variant<T_I8, true, true, true>("i8_kk_n_256x256x128"),
-    make_variant<T_I8, true, true, false>("i8_kk_m_256x256x128"),
-    make_variant<T_I8, false, true, true>("i8_mk_n_256x256x128"),
-    make_variant<T_I8, false, true, false>("i8_mk_m_256x256x128"),
+    V(T_F16, true, true, true, 256, 256, 64, 2, 2, 4, "f16_kk_n_256x256_r64_w4_s4"),
+    V(T_F16, true, true, true, 256, 256, 128, 2, 2, 2, "f16_kk_n_256x256_r128_w4_s2"),
+    V(T_F16, true, true, true, 256, 256, 64, 2, 2, 3, "f16_kk_n_256x256_r64_w4_s3"),
+    V(T_F16, true, true, true, 256, 256, 128, 2, 4, 2, "f16_kk_n_256x256_r128_w8_s2"),
+    V(T_F16, true, true, true, 256, 256, 64, 2, 4, 4, "f16_kk_n_256x256_r64_w8_s4"),
+    V(T_F16, true, true, true, 256, 128, 128, 2, 2, 3, "f16_kk_n_256x128_r128_w4_s3"),
+    V(T_F16, true, true, true, 256, 256, 64, 2, 2, 5, "f16_kk_n_256x256_r64_w4_s5"),
+    V(T_F16, true, true, true, 256, 256, 64, 2, 4, 5, "f16_kk_n_256x256_r64_w8_s5"),
+    VR(T_F16, true, true, true, 256, 256, 64, 2, 4, 2, "f16_kk_n_256x256_r64_w8_s2_reg"),
+    VR(T_F16, true, true, true, 256, 256, 64, 2, 2, 2, "f16_kk_n_256x256_r64_w4_s2_reg"),
+    VR(T_F16, true, true, true, 256, 256, 128, 2, 4, 2, "f16_kk_n_256x256_r128_w8_s2_reg"),
+    V(T_F16, true, true, false, 256, 256, 64, 2, 2, 4, "f16_kk_m_256x256_r64_w4_s4"),
+    V(T_BF16, true, true, true, 256, 256, 64, 2, 2, 4, "bf16_kk_n_256x256_r64_w4_s4"),
+    V(T_BF16, true, true, true, 256, 128, 128, 2, 2, 3, "bf16_kk_n_256x128_r128_w4_s3"),
+    V(T_BF16, true, true, false, 256, 256, 64, 2, 2, 4, "bf16_kk_m_256x256_r64_w4_s4"),
+    V(T_E4M3, true, true, true, 256, 256, 128, 2, 2, 2, "e4m3_kk_n_256x256_r128_w4_s2"),
+    V(T_E4M3, true, true, true, 256, 128, 128, 2, 2, 3, "e4m3_kk_n_256x128_r128_w4_s3"),
+    V(T_E4M3, true, true, false, 256, 256, 128, 2, 2, 2, "e4m3_kk_m_256x256_r128_w4_s2"),
+    V(T_I8, true, true, true, 256, 256, 64, 2, 2, 4, "i8_kk_n_256x256_r64_w4_s4"),
+    V(T_I8, true, true, false, 256, 256, 64, 2, 2, 4, "i8_kk_m_256x256_r64_w4_s4"),
+    V(T_I8, false, true, true, 256, 256, 64, 2, 2, 2, "i8_mk_n_256x256_r64_w4_s2"),
+    V(T_I8, false, true, true, 256, 256, 128, 2, 2, 2, "i8_mk_n_256x256_r128_w4_s2"),
+    V(T_I8, false, true, false, 256, 256, 64, 2, 2, 2, "i8_mk_m_256x256_r64_w4_s2"),
 };
+#undef V
+#undef VR
 constexpr int kNumVariants = (int)(sizeof kVariants / sizeof kVariants[0]);
 
 int elem_bytes(int t) {

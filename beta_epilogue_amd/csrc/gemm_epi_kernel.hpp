@@ -4,28 +4,31 @@
 // docstring, "Tensor dimensions" and its epilogue formula):
 //   Y = A.B^T,  D = alpha*(A.B^T) + beta*C + x_factor*X,  per batch l.
 //
-// Structure of one workgroup (4 waves, one wave per SIMD):
+// Structure of one workgroup (a compile-time configuration, see Cfg):
 //   * persistent tile loop: workgroup ids are remapped so that each of the 8
 //     XCDs walks a contiguous run of tiles of a grouped raster, which keeps
 //     the A row panels and B column panels of concurrently running tiles in
-//     that XCD's L2 (the pages' persistent scheduler, "Device side" of the
-//     Blackwell pipeline API card, made XCD-aware);
-//   * global -> LDS staging: each LDS row holds 128 bytes of K of one tile
-//     row, split into eight 16-byte chunks stored at chunk ^ swizzle(row) so
-//     that the MFMA fragment reads hit distinct banks.  K-major operands go
-//     straight to LDS with buffer_load_dwordx4 ... lds (the buffer's range
-//     check turns rows past M/N and chunks past K into zeros); M-major int8
-//     A is loaded to registers, transposed 8x8 bytes with v_perm and written
-//     with ds_write_b64.  Two stages: the next K tile streams in while the
-//     current one is multiplied (the pages' multi-stage pipeline, "Depth and
-//     shared memory");
+//     that XCD's L2 (the persistent tile loop of the Blackwell pipeline API
+//     card, "Device side", made XCD-aware);
+//   * global -> LDS staging into a STAGES-deep ring: each LDS row holds ROWB
+//     bytes of K of one tile row as 16-byte chunks stored at chunk ^ swz(row)
+//     so that the MFMA fragment reads of 16 consecutive rows hit 16 distinct
+//     16-byte bank groups of the 64-bank LDS.  K-major operands go straight
+//     to LDS with buffer_load_dwordx4 ... lds (the buffer's range check turns
+//     rows past M/N and chunks past K into zeros); M-major int8 A is loaded
+//     to registers, transposed 8x8 bytes with v_perm and written with
+//     ds_write_b64.  Each K tile waits only for its own stage (counted
+//     vmcnt), so STAGES-1 tiles stay in flight (the multi-stage pipeline of
+//     the API card's "Depth and shared memory");
 //   * MFMA mainloop: v_mfma_f32_32x32x16_{f16,bf16}, v_mfma_f32_32x32x64_f8f6f4
-//     (e4m3 x e4m3) or v_mfma_i32_32x32x32_i8; each wave owns a 128x128
-//     quarter of the 256x256 tile, 16 accumulator blocks of 32x32;
+//     (e4m3 x e4m3) or v_mfma_i32_32x32x32_i8 on 32x32 accumulator blocks in
+//     AGPRs; the fragments of k step s+1 are read while step s multiplies;
 //   * fused epilogue on the fp32 (int32) accumulator: Y = acc, D = alpha*acc
 //     + beta*C + x_factor*X, rounded to nearest-even into the output types;
-//     all loads of an element precede its stores (the example's epilogue
-//     comment), C and X are only read.
+//     each 32-wide block of the accumulator is re-laid out through a small
+//     per-wave LDS region so C/X loads and D/Y stores move 4 contiguous
+//     elements per lane; all loads of an element precede its stores (the
+//     example's epilogue comment) and C and X are only read.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -46,6 +49,7 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
+
 
 // Kernel arguments (passed by value).
 struct Params {
@@ -110,70 +114,197 @@ template <> struct Mma<T_E4M3> {
 };
 
 // Compile-time kernel configuration.
-template <int AB_, bool A_KMAJOR_, bool B_KMAJOR_, bool CD_NMAJOR_>
+//   BM x BN     workgroup tile (multiples of 32 per wave)
+//   ROWB        K bytes per LDS row per stage (64 or 128)
+//   WAVES_M/N   wave grid; each wave owns (BM/WAVES_M) x (BN/WAVES_N)
+//   STAGES      depth of the LDS ring
+//   LOADER      how K-major tiles reach LDS (see below)
+template <int AB_, bool A_KMAJOR_, bool B_KMAJOR_, bool CD_NMAJOR_, int BM_ = 256, int BN_ = 256,
+          int ROWB_ = 128, int WAVES_M_ = 2, int WAVES_N_ = 2, int STAGES_ = 2, int LOADER_ = 0>
 struct Cfg {
+  // LOADER 0: K-major tiles go global -> LDS by buffer_load ... lds (DMA).
+  // LOADER 1: global -> VGPR by buffer_load_dwordx4, then ds_write_b128
+  //           (two register stages in flight; LDS writes use the LDS's own
+  //           port instead of the texture-data path).
+  static constexpr int LOADER = LOADER_;
   static constexpr int AB = AB_;
   static constexpr bool A_KMAJOR = A_KMAJOR_, B_KMAJOR = B_KMAJOR_, CD_NMAJOR = CD_NMAJOR_;
-  static constexpr int BM = 256, BN = 256;           // workgroup tile
-  static constexpr int ROWB = 128;                   // K bytes per LDS row per stage
-  static constexpr int BK = ROWB / Mma<AB>::ESIZE;   // K elements per stage
-  static constexpr int WAVES_M = 2, WAVES_N = 2;
+  static constexpr int BM = BM_, BN = BN_, ROWB = ROWB_;
+  static constexpr int CH = ROWB / 16;                  // 16-byte chunks per LDS row
+  static constexpr int ROWS_PER_DMA = 1024 / ROWB;       // rows one wave DMA writes
+  static constexpr int SWZ_SHIFT = CH == 8 ? 1 : 2;      // 16 rows -> 16 bank groups
+  static constexpr int BK = ROWB / Mma<AB>::ESIZE;       // K elements per stage
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int THREADS = NW * 64;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile
   static constexpr int FM = WM / 32, FN = WN / 32;           // 32x32 blocks
+  static constexpr int STAGES = STAGES_;
   static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
-  static constexpr int STAGES = 2;
   static constexpr int PIPE_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int EPI_BYTES = NW * 64 * 132 * 4;  // per-wave epilogue regions
+  // epilogue: per wave, 32 lines of the block being re-laid out
+  static constexpr int EPI_LINE = CD_NMAJOR ? WN : WM;
+  static constexpr int EPI_PITCH = EPI_LINE + (CD_NMAJOR ? 8 : 4);  // words
+  static constexpr int EPI_WAVE_BYTES = 32 * EPI_PITCH * 4;
+  static constexpr int EPI_BYTES = NW * EPI_WAVE_BYTES;
   static constexpr int LDS_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
   static constexpr int KSTEPS = ROWB / Mma<AB>::KSB;
+  static_assert(KSTEPS >= 1, "a stage must hold at least one MFMA k step");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
 };
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// Calls f(IntC<I>{}) for I = B .. E-1, in order, at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IntC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Chunk swizzle: the 16-byte chunk c of LDS row r lives at c ^ swz(r).
-__device__ __forceinline__ int swz(int row) { return row & 7; }
+template <class CF>
+__device__ __forceinline__ int swz(int row) {
+  return (row >> CF::SWZ_SHIFT) & (CF::CH - 1);
+}
 
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
+// s_waitcnt vmcnt(N) for a compile-time N (gfx9 encoding: vmcnt in bits
+// [3:0] and [15:14], expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS hand-offs.  Waits only for this wave's LDS
+// operations; the DMA stages are covered by the counted vmcnt waits, and
+// global stores of the epilogue stay in flight.  (__syncthreads() would add a
+// release fence that drains every outstanding memory operation first.)
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------
-// Staging of a K-major operand tile (R rows x 128 bytes) straight into LDS.
-// One wave instruction moves 64 chunks = 8 rows = 1 KiB of LDS, written
-// linearly: lane j fills physical chunk j%8 of row j/8, so it fetches the
-// logical chunk (j%8) ^ swz(row) from global memory.
+// Staging of a K-major operand tile (R rows x ROWB bytes) straight into LDS.
+// One wave instruction moves 64 chunks = 1 KiB of LDS, written linearly:
+// lane j fills physical chunk j % CH of row j / CH, so it fetches the logical
+// chunk (j % CH) ^ swz(row) from global memory.
 // ---------------------------------------------------------------------------
-template <int R, int NW>
+//
+// The DMA is issued through inline asm on purpose: the compiler tracks LDS
+// DMA it emits itself and then waits for every outstanding VMEM operation
+// before any later LDS read, which would drain the whole ring each K tile.
+// Completion is instead tracked here with counted vmcnt waits followed by a
+// workgroup barrier.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// Raw buffer descriptor: base, stride 0, num_records bytes, default format.
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = (uint64_t)base;
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)nbytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+template <class CF, int R>
 struct KMajorStager {
-  static constexpr int NQ = R / (8 * NW);
-  static_assert(NQ * 8 * NW == R, "rows must split evenly over the waves");
-  __amdgpu_buffer_rsrc_t rsrc;
+  static constexpr int NQ = R / (CF::ROWS_PER_DMA * CF::NW);
+  static_assert(NQ * CF::ROWS_PER_DMA * CF::NW == R, "rows must split evenly over the waves");
+  v4i rsrc;
   uint32_t voff[NQ];
-  uint32_t cbyte;  // byte offset of this lane's logical chunk within a row
+  uint32_t cb[NQ];  // byte offset of this lane's logical chunk within its row
 
   __device__ __forceinline__ void setup(const char* tile_base, int64_t ld_bytes, int valid_rows,
                                         int wave, int lane) {
-    const int rsub = lane >> 3;
-    const int c = (lane & 7) ^ (rsub & 7);
-    cbyte = (uint32_t)c * 16u;
-    const uint32_t nrec = (uint32_t)((int64_t)valid_rows * ld_bytes);
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)tile_base, (short)0, (int)nrec, 0x00020000);
+    const int rsub = lane / CF::CH;
+    const int pc = lane % CF::CH;
+    rsrc = make_rsrc(tile_base, (uint32_t)((int64_t)valid_rows * ld_bytes));
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int row = (q * NW + wave) * 8 + rsub;
-      voff[q] = (uint32_t)(row * ld_bytes) + cbyte;
+      const int row = (q * CF::NW + wave) * CF::ROWS_PER_DMA + rsub;
+      cb[q] = (uint32_t)((pc ^ swz<CF>(row)) * 16);
+      voff[q] = (uint32_t)(row * ld_bytes) + cb[q];
     }
   }
 
-  // Issue the loads of K tile kt into the LDS region at byte offset lds_off.
-  // kvalid = bytes of K left from this K tile on (chunks at or past it read 0).
-  __device__ __forceinline__ void issue(char* lds, int lds_off, int wave, int kt, int64_t kvalid) {
-    const uint32_t kofs = (uint32_t)kt * 128u;
-    const bool live = (int64_t)cbyte < kvalid;
+  // Issue instructions [Q0, Q1) of the loads of K tile kt into LDS at byte
+  // address lds_addr (LDS address space).  kvalid = bytes of K left from
+  // this K tile on; chunks at or past it get an out-of-range offset and read
+  // as zero.
+  template <int Q0 = 0, int Q1 = NQ>
+  __device__ __forceinline__ void issue(uint32_t lds_addr, int wave, int kt, int64_t kvalid) {
+    const uint32_t kofs = (uint32_t)kt * (uint32_t)CF::ROWB;
+    if (kvalid >= CF::ROWB) {
+#pragma unroll
+      for (int q = Q0; q < Q1; ++q)
+        dma16(rsrc, lds_addr + (uint32_t)((q * CF::NW + wave) * 1024), voff[q] + kofs);
+    } else {
+#pragma unroll
+      for (int q = Q0; q < Q1; ++q) {
+        const uint32_t vo = (int64_t)cb[q] < kvalid ? voff[q] + kofs : 0x80000000u;
+        dma16(rsrc, lds_addr + (uint32_t)((q * CF::NW + wave) * 1024), vo);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Register-staged K-major operand tile (R rows x ROWB bytes): the same
+// 1 KiB-per-wave-instruction split as the DMA stager, but lane j loads the
+// natural chunk j % CH of its row into VGPRs and writes it to LDS at the
+// swizzled position itself.  Two register stages.
+// ---------------------------------------------------------------------------
+template <class CF, int R>
+struct KMajorRegStager {
+  static constexpr int NQ = R / (CF::ROWS_PER_DMA * CF::NW);
+  static_assert(NQ * CF::ROWS_PER_DMA * CF::NW == R, "rows must split evenly over the waves");
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[NQ];  // global byte offset (row * ld + chunk * 16)
+  uint32_t loff[NQ];  // LDS byte offset within a stage tile (swizzled)
+  uint32_t cb;        // this lane's chunk byte offset within a row
+  v4u buf[2][NQ];
+
+  __device__ __forceinline__ void setup(const char* tile_base, int64_t ld_bytes, int valid_rows,
+                                        int wave, int lane) {
+    const int rsub = lane / CF::CH;
+    const int c = lane % CF::CH;
+    cb = (uint32_t)c * 16u;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)tile_base, (short)0,
+                                             (int)(uint32_t)((int64_t)valid_rows * ld_bytes), 0x00020000);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const uint32_t vo = live ? voff[q] + kofs : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (lds_void_t*)(lds + lds_off + (q * NW + wave) * 1024), 16, vo, 0, 0, 0);
+      const int row = (q * CF::NW + wave) * CF::ROWS_PER_DMA + rsub;
+      voff[q] = (uint32_t)(row * ld_bytes) + cb;
+      loff[q] = (uint32_t)(row * CF::ROWB + ((c ^ swz<CF>(row)) << 4));
     }
+  }
+  // Load instruction Q of K tile kt into register stage BUF (rows past the
+  // tile's valid rows and chunks at or past kvalid bytes read as zero).
+  template <int BUF, int Q>
+  __device__ __forceinline__ void load(int kt, int64_t kvalid) {
+    const uint32_t vo = (int64_t)cb < kvalid ? voff[Q] + (uint32_t)kt * (uint32_t)CF::ROWB : 0x80000000u;
+    buf[BUF][Q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vo, 0, 0));
+  }
+  template <int BUF, int Q>
+  __device__ __forceinline__ void store(char* lds, int tile_off) const {
+    *(v4u*)(lds + tile_off + loff[Q]) = buf[BUF][Q];
   }
 };
 
@@ -191,18 +322,18 @@ __device__ __forceinline__ void tr4x4(uint32_t x0, uint32_t x1, uint32_t x2, uin
 }
 
 // ---------------------------------------------------------------------------
-// Staging of an M-major one-byte A tile: global A[l][k][m], 128 k rows by
+// Staging of an M-major one-byte A tile: global A[l][k][m], ROWB k rows by
 // BM m bytes per stage.  Each thread owns blocks of 8 k x 8 m bytes: eight
-// 8-byte global loads (a wave covers whole 256-byte k rows), an 8x8 byte
+// 8-byte global loads (a wave covers whole k rows of the tile), an 8x8 byte
 // transpose in registers, then eight 8-byte LDS writes into the same
 // K-contiguous swizzled layout the K-major path produces.
 // ---------------------------------------------------------------------------
-template <int BM, int THREADS>
+template <class CF>
 struct MMajorStager8 {
-  static constexpr int MB = BM / 8;                 // m blocks per tile
-  static constexpr int NB = (128 / 8) * MB / THREADS;  // blocks per thread
-  static_assert(NB * THREADS == 16 * MB, "blocks must split evenly");
-  uint2 buf[NB][8];
+  static constexpr int MB = CF::BM / 8;                       // m blocks per tile
+  static constexpr int NB = (CF::ROWB / 8) * MB / CF::THREADS;  // blocks per thread
+  static_assert(NB >= 1 && NB * CF::THREADS == (CF::ROWB / 8) * MB, "blocks must split evenly");
+  v2u buf[NB][8];
   const char* base;  // A + l*M*K (bytes)
   int64_t M, K;
   int m0;
@@ -217,16 +348,16 @@ struct MMajorStager8 {
   __device__ __forceinline__ void load(int kt, int tid) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int id = b * THREADS + tid;
+      const int id = b * CF::THREADS + tid;
       const int bm = id % MB, bk = id / MB;
       const int64_t m = (int64_t)m0 + bm * 8;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const int64_t k = (int64_t)kt * 128 + bk * 8 + r;
+        const int64_t k = (int64_t)kt * CF::ROWB + bk * 8 + r;
         if (k < K && m < M)
-          buf[b][r] = *(const uint2*)(base + k * M + m);
+          buf[b][r] = *(const v2u*)(base + k * M + m);
         else
-          buf[b][r] = make_uint2(0u, 0u);
+          buf[b][r] = v2u{0u, 0u};
       }
     }
   }
@@ -234,7 +365,7 @@ struct MMajorStager8 {
   __device__ __forceinline__ void store(char* lds, int lds_off, int tid) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int id = b * THREADS + tid;
+      const int id = b * CF::THREADS + tid;
       const int bm = id % MB, bk = id / MB;
       uint32_t lo[8], hi[8];
       tr4x4(buf[b][0].x, buf[b][1].x, buf[b][2].x, buf[b][3].x, lo[0], lo[1], lo[2], lo[3]);
@@ -245,58 +376,36 @@ struct MMajorStager8 {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = bm * 8 + i;
-        const int off = lds_off + row * 128 + ((chunk ^ swz(row)) << 4) + sub;
-        *(uint2*)(lds + off) = make_uint2(lo[i], hi[i]);
+        const int off = lds_off + row * CF::ROWB + ((chunk ^ swz<CF>(row)) << 4) + sub;
+        *(v2u*)(lds + off) = v2u{lo[i], hi[i]};
       }
     }
   }
 };
 
 // Fragment read: this lane's half of k step s of LDS row `row`.
-template <int AB>
-__device__ __forceinline__ typename Mma<AB>::frag_t read_frag(const char* lds, int tile_off, int row,
-                                                              int s, int half) {
-  constexpr int KSB = Mma<AB>::KSB;
+template <class CF>
+__device__ __forceinline__ typename Mma<CF::AB>::frag_t read_frag(const char* lds, int tile_off,
+                                                                  int row, int s, int half) {
+  constexpr int KSB = Mma<CF::AB>::KSB;
+  const char* rp = lds + tile_off + row * CF::ROWB;
+  const int sw = swz<CF>(row);
   if constexpr (KSB == 32) {
     const int c = s * 2 + half;
-    return *(const v4i*)(lds + tile_off + row * 128 + ((c ^ swz(row)) << 4));
+    return *(const v4i*)(rp + ((c ^ sw) << 4));
   } else {
     const int c = s * 4 + half * 2;
-    const v4i lo = *(const v4i*)(lds + tile_off + row * 128 + ((c ^ swz(row)) << 4));
-    const v4i hi = *(const v4i*)(lds + tile_off + row * 128 + (((c + 1) ^ swz(row)) << 4));
+    const v4i lo = *(const v4i*)(rp + ((c ^ sw) << 4));
+    const v4i hi = *(const v4i*)(rp + (((c + 1) ^ sw) << 4));
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 }
 
 // ---------------------------------------------------------------------------
-// Fused epilogue (on the accumulator of one wave: rows [mw, mw+WM), columns
-// [nw, nw+WN) of batch l).  Y = acc; D = alpha*acc + beta*C + x_factor*X in
-// fp32 (int32, wrapping, for int8 inputs), rounded to nearest-even into the
-// output type; every load of an element precedes its stores.
+// Fused epilogue of one wave: rows [mw, mw+WM), columns [nw, nw+WN) of batch
+// l.  Y = acc; D = alpha*acc + beta*C + x_factor*X in fp32 (int32, wrapping,
+// for int8 inputs), rounded to nearest-even into the output type.
 // ---------------------------------------------------------------------------
-template <class CF>
-struct EpiLayout {
-  static constexpr int LINES = 64;        // lines per half
-  static constexpr int LINE = 128;        // contiguous elements per line
-  static constexpr int PITCH = LINE + 4;  // words per line in LDS
-  static constexpr int WAVE_BYTES = LINES * PITCH * 4;
-  static constexpr int BYTES = CF::NW * WAVE_BYTES;
-};
-
-__device__ __forceinline__ v4f load4_f(const void* p, int dt, int64_t i) {
-  if (dt == T_F16) {
-    const v2u u = __builtin_nontemporal_load((const v2u*)((const _Float16*)p + i));
-    const _Float16* h = (const _Float16*)&u;
-    return v4f{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-  }
-  if (dt == T_BF16) {
-    const v2u u = __builtin_nontemporal_load((const v2u*)((const uint16_t*)p + i));
-    return v4f{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
-  }
-  return __builtin_nontemporal_load((const v4f*)((const float*)p + i));
-}
-
 __device__ __forceinline__ void store4_f(void* p, int dt, int64_t i, v4f v) {
   if (dt == T_F16) {
     _Float16 h[4] = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
@@ -315,94 +424,164 @@ __device__ __forceinline__ void store4_f(void* p, int dt, int64_t i, v4f v) {
 __device__ __forceinline__ float acc_bits(float v) { return v; }
 __device__ __forceinline__ float acc_bits(int v) { return __int_as_float(v); }
 
+// Element work for four contiguous outputs at flat index o, given the four
+// accumulator values w and the four C and X values already loaded.
+template <class CF>
+__device__ __forceinline__ void epi_finish4(const Params& p, int64_t o, v4f w, v4f c, v4f x) {
+  if constexpr (CF::AB == T_I8) {
+    const v4u a = __builtin_bit_cast(v4u, w);
+    v4u t = a * (unsigned)p.ialpha;
+    if (p.c_dtype) t += __builtin_bit_cast(v4u, c) * (unsigned)p.ibeta;
+    if (p.x_dtype) t += __builtin_bit_cast(v4u, x) * (unsigned)p.ix;
+    __builtin_nontemporal_store(t, (v4u*)((int*)p.D + o));
+    if (p.y_dtype) __builtin_nontemporal_store(a, (v4u*)((int*)p.Y + o));
+  } else {
+    v4f t = w * p.alpha;
+    if (p.c_dtype) {
+      t.x = __builtin_fmaf(p.beta, c.x, t.x);
+      t.y = __builtin_fmaf(p.beta, c.y, t.y);
+      t.z = __builtin_fmaf(p.beta, c.z, t.z);
+      t.w = __builtin_fmaf(p.beta, c.w, t.w);
+    }
+    if (p.x_dtype) {
+      t.x = __builtin_fmaf(p.xf, x.x, t.x);
+      t.y = __builtin_fmaf(p.xf, x.y, t.y);
+      t.z = __builtin_fmaf(p.xf, x.z, t.z);
+      t.w = __builtin_fmaf(p.xf, x.w, t.w);
+    }
+    store4_f(p.D, p.d_dtype, o, t);
+    if (p.y_dtype) store4_f(p.Y, p.y_dtype, o, w);
+  }
+}
+
+// Raw bits of four C (or X) elements at flat index o: 16 bytes for 4-byte
+// types, 8 bytes (in .xy) for 2-byte types.  Only the load sits under the
+// (uniform) size test, so every load of a chunk can be in flight at once.
+__device__ __forceinline__ v4u epi_raw4(const void* ptr, int dt, int64_t o) {
+  if (dt == T_F32 || dt == T_I32)
+    return __builtin_nontemporal_load((const v4u*)((const uint32_t*)ptr + o));
+  const v2u u = __builtin_nontemporal_load((const v2u*)((const uint16_t*)ptr + o));
+  return v4u{u.x, u.y, 0u, 0u};
+}
+
+// Raw bits -> four fp32 values, without branches (all decodings computed,
+// one selected by the uniform type).
+__device__ __forceinline__ v4f epi_decode4(v4u r, int dt) {
+  const v4f f32 = __builtin_bit_cast(v4f, r);
+  const v4f bf = {__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                  __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+  const v2u h2 = {r.x, r.y};
+  const _Float16* h = (const _Float16*)&h2;
+  const v4f f16 = {(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+  return dt == T_F32 ? f32 : (dt == T_BF16 ? bf : f16);
+}
+
+// The accumulator is re-laid out one 32-wide block at a time through a
+// 32-line LDS region private to the wave: for N-major outputs a block row
+// (32 rows x WN columns, lines = rows), for M-major a block column (WM rows x
+// 32 columns, lines = columns).  Then each lane reads 4 contiguous elements
+// (one ds_read_b128) and does the element work for them.
 template <class CF, class ACC>
 __device__ __forceinline__ void epilogue(const Params& p, const ACC (&acc)[CF::FM][CF::FN], char* lds,
                                          int wave, int lane, int l, int mw, int nw) {
-  using EL = EpiLayout<CF>;
   constexpr bool NMAJ = CF::CD_NMAJOR;
-  const int region = wave * EL::WAVE_BYTES;
+  constexpr int LINE = CF::EPI_LINE, PITCH = CF::EPI_PITCH;
+  constexpr int LPL = LINE / 4;        // lanes per line
+  constexpr int LINES_PER_PASS = 64 / LPL;
+  float* region = (float*)(lds + wave * CF::EPI_WAVE_BYTES);
   const int half = lane >> 5, l32 = lane & 31;
   const int64_t obase = (int64_t)l * p.M * p.N;
+  constexpr int NBLK = NMAJ ? CF::FM : CF::FN;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    // -- scatter this half of the accumulator into the wave's LDS region.
-    // N-major: lines are rows (i blocks 2h, 2h+1), elements are columns.
-    // M-major: lines are columns (j blocks 2h, 2h+1), elements are rows.
+  for (int blk = 0; blk < NBLK; ++blk) {
     if constexpr (NMAJ) {
+      // block row blk: lane holds rows 8*(v/4) + 4*half + v%4, column j*32 + l32
+      float* wp = region + (half * 4) * PITCH + l32;
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii)
+      for (int j = 0; j < CF::FN; ++j)
 #pragma unroll
-        for (int j = 0; j < CF::FN; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int line = ii * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
-            const int col = j * 32 + l32;
-            const auto e = acc[2 * h + ii][j][v];
-            *(float*)(lds + region + (line * EL::PITCH + col) * 4) = acc_bits(e);
-          }
+        for (int v = 0; v < 16; ++v) {
+          const auto e = acc[blk][j][v];
+          wp[((v >> 2) * 8 + (v & 3)) * PITCH + j * 32] = acc_bits(e);
+        }
     } else {
+      // block column blk: lane holds column l32, rows i*32 + 8*v4 + 4*half + 0..3
+      float* wp = region + l32 * PITCH + half * 4;
 #pragma unroll
       for (int i = 0; i < CF::FM; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            const int line = jj * 32 + l32;
-            const int row = i * 32 + v4 * 8 + half * 4;
-            const ACC& a = acc[i][2 * h + jj];
-            const auto e0 = a[v4 * 4 + 0], e1 = a[v4 * 4 + 1];
-            const auto e2 = a[v4 * 4 + 2], e3 = a[v4 * 4 + 3];
-            const v4f w = {acc_bits(e0), acc_bits(e1), acc_bits(e2), acc_bits(e3)};
-            *(v4f*)(lds + region + (line * EL::PITCH + row) * 4) = w;
-          }
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const auto e0 = acc[i][blk][v4 * 4 + 0], e1 = acc[i][blk][v4 * 4 + 1];
+          const auto e2 = acc[i][blk][v4 * 4 + 2], e3 = acc[i][blk][v4 * 4 + 3];
+          *(v4f*)(wp + i * 32 + v4 * 8) = v4f{acc_bits(e0), acc_bits(e1), acc_bits(e2), acc_bits(e3)};
+        }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // -- walk the half: lane reads 4 contiguous elements of line it*2+half.
-    for (int it = 0; it < EL::LINES / 2; ++it) {
-      const int line = it * 2 + half;
-      const int e = l32 * 4;
-      const v4f w = *(const v4f*)(lds + region + (line * EL::PITCH + e) * 4);
-      int64_t m, n;
-      if constexpr (NMAJ) {
-        m = mw + h * 64 + line;
-        n = nw + e;
-      } else {
-        n = nw + h * 64 + line;
-        m = mw + e;
-      }
-      if (m < p.M && n < p.N) {
-        const int64_t o = obase + (NMAJ ? m * p.N + n : n * p.M + m);
-        if constexpr (CF::AB == T_I8) {
-          const v4u a = __builtin_bit_cast(v4u, w);
-          v4u t = a * (unsigned)p.ialpha;
-          if (p.c_dtype) t += __builtin_nontemporal_load((const v4u*)((const int*)p.C + o)) * (unsigned)p.ibeta;
-          if (p.x_dtype) t += __builtin_nontemporal_load((const v4u*)((const int*)p.X + o)) * (unsigned)p.ix;
-          __builtin_nontemporal_store(t, (v4u*)((int*)p.D + o));
-          if (p.y_dtype) __builtin_nontemporal_store(a, (v4u*)((int*)p.Y + o));
+    const int sub = lane / LPL;
+    const int e = (lane % LPL) * 4;
+    // Passes are done in chunks: all loads of a chunk (accumulator values
+    // from LDS, C and X from memory) are issued before any of its math, so a
+    // chunk costs one memory round trip instead of one per pass.
+    constexpr int PASSES = 32 / LINES_PER_PASS;
+    constexpr int CMAX = CF::NW > 4 ? 4 : 8;  // two waves per SIMD: half the registers
+    constexpr int CHUNK = PASSES < CMAX ? PASSES : CMAX;
+#pragma unroll
+    for (int c0 = 0; c0 < PASSES; c0 += CHUNK) {
+      v4f w[CHUNK];
+      v4u cr[CHUNK], xr[CHUNK];
+      int64_t off[CHUNK];
+      bool ok[CHUNK];
+#pragma unroll
+      for (int q = 0; q < CHUNK; ++q) {
+        const int line = (c0 + q) * LINES_PER_PASS + sub;
+        w[q] = *(const v4f*)(region + line * PITCH + e);
+        int64_t m, n;
+        if constexpr (NMAJ) {
+          m = mw + blk * 32 + line;
+          n = nw + e;
         } else {
-          v4f t = w * p.alpha;
-          if (p.c_dtype) {
-            const v4f c = load4_f(p.C, p.c_dtype, o);
-            t.x = __builtin_fmaf(p.beta, c.x, t.x);
-            t.y = __builtin_fmaf(p.beta, c.y, t.y);
-            t.z = __builtin_fmaf(p.beta, c.z, t.z);
-            t.w = __builtin_fmaf(p.beta, c.w, t.w);
-          }
-          if (p.x_dtype) {
-            const v4f x = load4_f(p.X, p.x_dtype, o);
-            t.x = __builtin_fmaf(p.xf, x.x, t.x);
-            t.y = __builtin_fmaf(p.xf, x.y, t.y);
-            t.z = __builtin_fmaf(p.xf, x.z, t.z);
-            t.w = __builtin_fmaf(p.xf, x.w, t.w);
-          }
-          store4_f(p.D, p.d_dtype, o, t);
-          if (p.y_dtype) store4_f(p.Y, p.y_dtype, o, w);
+          n = nw + blk * 32 + line;
+          m = mw + e;
         }
+        ok[q] = m < p.M && n < p.N;
+        off[q] = obase + (NMAJ ? m * p.N + n : n * p.M + m);
+        cr[q] = v4u{};
+        xr[q] = v4u{};
+        if (ok[q]) {
+          if (p.c_dtype) cr[q] = epi_raw4(p.C, p.c_dtype, off[q]);
+          if (p.x_dtype) xr[q] = epi_raw4(p.X, p.x_dtype, off[q]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < CHUNK; ++q) {
+        v4f cv, xv;
+        if constexpr (CF::AB == T_I8) {
+          cv = __builtin_bit_cast(v4f, cr[q]);
+          xv = __builtin_bit_cast(v4f, xr[q]);
+        } else {
+          cv = epi_decode4(cr[q], p.c_dtype);
+          xv = epi_decode4(xr[q], p.x_dtype);
+        }
+        if (ok[q]) epi_finish4<CF>(p, off[q], w[q], cv, xv);
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
+
+// Scheduling pattern for one k step: READS LDS reads spread evenly over
+// MFMAS matrix instructions ([1 read, MFMAS/READS MFMAs] repeated).
+template <int R, int READS, int MFMAS>
+struct InterleaveHint {
+  static __device__ __forceinline__ void run() {
+    if constexpr (R < READS) {
+      constexpr int n = MFMAS / READS + (R < MFMAS % READS ? 1 : 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+      if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x008, n, 0);  // MFMAs
+      InterleaveHint<R + 1, READS, MFMAS>::run();
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // The kernel
@@ -411,12 +590,14 @@ template <class CF>
 __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
   using MM = Mma<CF::AB>;
   using acc_t = typename MM::acc_t;
+  using frag_t = typename MM::frag_t;
   constexpr int ES = MM::ESIZE;
-  constexpr int BM = CF::BM, BN = CF::BN;
+  constexpr int BM = CF::BM, BN = CF::BN, S = CF::STAGES;
   __shared__ __attribute__((aligned(1024))) char lds[CF::LDS_BYTES];
+  const uint32_t lds_u32 = (uint32_t)(uintptr_t)(lds_void_t*)lds;  // LDS address of the array
 
   const int tid = threadIdx.x;
-  const int lane = lane_id();
+  const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % CF::WAVES_M, wn = wave / CF::WAVES_M;
   const int half = lane >> 5, l32 = lane & 31;
@@ -428,6 +609,10 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
   const int64_t kbytes = p.K * ES;
   const int KT = (int)((kbytes + CF::ROWB - 1) / CF::ROWB);
   const int64_t tiles_mn = (int64_t)p.tiles_m * p.tiles_n;
+
+  // DMA instructions per wave per stage (for the counted waits)
+  constexpr int NQ_A = CF::A_KMAJOR ? KMajorStager<CF, BM>::NQ : 0;
+  constexpr int NQ_STAGE = NQ_A + KMajorStager<CF, BN>::NQ;
 
   for (int64_t t = g; t < p.tiles_total; t += G) {
     // ---- tile coordinates: grouped raster inside each batch -------------
@@ -445,14 +630,30 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     // ---- staging set-up --------------------------------------------------
     const char* Ab = (const char*)p.A + (int64_t)l * p.M * kbytes;
     const char* Bb = (const char*)p.B + (int64_t)l * p.N * kbytes;
-    KMajorStager<BN, CF::NW> sb;
+    KMajorStager<CF, BN> sb;
     sb.setup(Bb + (int64_t)n0 * kbytes, kbytes, (int)min((int64_t)BN, p.N - n0), wave, lane);
-    KMajorStager<BM, CF::NW> sa_k;
-    MMajorStager8<BM, CF::THREADS> sa_m;
+    KMajorStager<CF, BM> sa_k;
     if constexpr (CF::A_KMAJOR)
       sa_k.setup(Ab + (int64_t)m0 * kbytes, kbytes, (int)min((int64_t)BM, p.M - m0), wave, lane);
-    else
-      sa_m.setup(Ab, p.M, p.K, m0);
+
+    auto issue_dma = [&](int k_tile) {
+      const int st = (k_tile % S) * CF::STAGE_BYTES;
+      const int64_t kv = kbytes - (int64_t)k_tile * CF::ROWB;
+      if constexpr (CF::A_KMAJOR) sa_k.issue(lds_u32 + st, wave, k_tile, kv);
+      sb.issue(lds_u32 + st + BM * CF::ROWB, wave, k_tile, kv);
+    };
+    // Part PART of NPARTS of the loads of K tile k_tile (A and B split alike).
+    using SA = KMajorStager<CF, BM>;
+    using SB = KMajorStager<CF, BN>;
+    auto issue_dma_part = [&](auto part_c, auto nparts_c, int k_tile) {
+      constexpr int PART = decltype(part_c)::value, NP = decltype(nparts_c)::value;
+      const int st = (k_tile % S) * CF::STAGE_BYTES;
+      const int64_t kv = kbytes - (int64_t)k_tile * CF::ROWB;
+      if constexpr (CF::A_KMAJOR)
+        sa_k.template issue<PART * SA::NQ / NP, (PART + 1) * SA::NQ / NP>(lds_u32 + st, wave, k_tile, kv);
+      sb.template issue<PART * SB::NQ / NP, (PART + 1) * SB::NQ / NP>(lds_u32 + st + BM * CF::ROWB, wave,
+                                                                      k_tile, kv);
+    };
 
     acc_t acc[CF::FM][CF::FN];
 #pragma unroll
@@ -460,59 +661,259 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < CF::FN; ++j) acc[i][j] = acc_t{};
 
-    // ---- prologue: K tile 0 into stage 0 --------------------------------
-    if constexpr (CF::A_KMAJOR) {
-      sa_k.issue(lds, 0, wave, 0, kbytes);
+    // Fragments of one k step: A blocks then B blocks of this wave.
+    frag_t fa[2][CF::FM], fb[2][CF::FN];
+    auto load_step = [&](frag_t (&ra)[CF::FM], frag_t (&rb)[CF::FN], int st, int s) {
+      const int a_off = st * CF::STAGE_BYTES, b_off = a_off + BM * CF::ROWB;
+#pragma unroll
+      for (int i = 0; i < CF::FM; ++i) ra[i] = read_frag<CF>(lds, a_off, wm * CF::WM + i * 32 + l32, s, half);
+#pragma unroll
+      for (int j = 0; j < CF::FN; ++j) rb[j] = read_frag<CF>(lds, b_off, wn * CF::WN + j * 32 + l32, s, half);
+    };
+    auto mma_step = [&](const frag_t (&ra)[CF::FM], const frag_t (&rb)[CF::FN]) {
+#pragma unroll
+      for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < CF::FN; ++j) acc[i][j] = MM::mma(ra[i], rb[j], acc[i][j]);
+    };
+    // Interleave the next step's LDS reads with this step's MFMAs so each
+    // read's latency hides under MFMAs already queued.
+    auto pipeline_hint = [&]() {
+      constexpr int READS = (CF::FM + CF::FN) * (MM::KSB / 32);
+      constexpr int MFMAS = CF::FM * CF::FN;
+      InterleaveHint<0, READS, MFMAS>::run();
+    };
+    // One K tile from stage st; the last step prefetches step 0 of stage nst.
+    // The DMA of K tile dma_tile (if < KT) is issued in NP parts after the
+    // first NP k steps, so the memory pipeline is fed while MFMAs run rather
+    // than in one burst that stalls the wave's issue.
+    auto compute = [&](int st, int nst, int dma_tile, auto np_c) {
+      constexpr int NP = decltype(np_c)::value;
+      static_for<0, CF::KSTEPS>([&](auto s_c) {
+        constexpr int s = decltype(s_c)::value;
+        constexpr int cur = s & 1;
+        if constexpr (s + 1 < CF::KSTEPS)
+          load_step(fa[cur ^ 1], fb[cur ^ 1], st, s + 1);
+        else
+          load_step(fa[cur ^ 1], fb[cur ^ 1], nst, 0);
+        mma_step(fa[cur], fb[cur]);
+        pipeline_hint();
+        if constexpr (s < NP) {
+          if (dma_tile < KT) issue_dma_part(IntC<s>{}, IntC<NP>{}, dma_tile);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+    };
+    static_assert(CF::KSTEPS % 2 == 0, "fragment double buffer needs an even step count");
+
+    // ---- K-major A: explicitly ordered k steps ---------------------------
+    // Each k step issues its MFMAs in a fixed order (sched_barrier pins it);
+    // after each MFMA come the fragment reads of the next step scheduled
+    // there (ordered by first use: A0, B0.., A1..) and a share of the DMA
+    // instructions of a later K tile, so LDS reads, DMA and MFMAs overlap.
+    constexpr int NREAD = CF::FM + CF::FN;
+    constexpr int MF = CF::FM * CF::FN;
+    auto read_r = [&](auto buf_c, auto r_c, int st, int ks) {
+      constexpr int BUF = decltype(buf_c)::value, R = decltype(r_c)::value;
+      const int a_off = st * CF::STAGE_BYTES, b_off = a_off + BM * CF::ROWB;
+      if constexpr (R == 0)
+        fa[BUF][0] = read_frag<CF>(lds, a_off, wm * CF::WM + l32, ks, half);
+      else if constexpr (R <= CF::FN)
+        fb[BUF][R - 1] = read_frag<CF>(lds, b_off, wn * CF::WN + (R - 1) * 32 + l32, ks, half);
+      else
+        fa[BUF][R - CF::FN] = read_frag<CF>(lds, a_off, wm * CF::WM + (R - CF::FN) * 32 + l32, ks, half);
+    };
+    auto dma_one = [&](auto d_c, int k_tile) {
+      constexpr int D = decltype(d_c)::value;
+      const int st = (k_tile % S) * CF::STAGE_BYTES;
+      const int64_t kv = kbytes - (int64_t)k_tile * CF::ROWB;
+      if constexpr (D < NQ_A)
+        sa_k.template issue<D, D + 1>(lds_u32 + st, wave, k_tile, kv);
+      else
+        sb.template issue<D - NQ_A, D - NQ_A + 1>(lds_u32 + st + BM * CF::ROWB, wave, k_tile, kv);
+    };
+    // One k step on buffer CUR: reads of (stage rst, step rs) into CUR^1 and
+    // NOPS memory operations op(IntC<k>) spread evenly over the MFMAs.
+    auto kstep_ops = [&](auto cur_c, int rst, int rs, auto nops_c, auto&& op) {
+      constexpr int CUR = decltype(cur_c)::value;
+      constexpr int NOPS = decltype(nops_c)::value;
+      static_for<0, MF>([&](auto idx_c) {
+        constexpr int IDX = decltype(idx_c)::value;
+        constexpr int I = IDX / CF::FN, J = IDX % CF::FN;
+        acc[I][J] = MM::mma(fa[CUR][I], fb[CUR][J], acc[I][J]);
+        static_for<0, NREAD>([&](auto r_c) {
+          constexpr int R = decltype(r_c)::value;
+          if constexpr ((R * MF) / NREAD == IDX) read_r(IntC<CUR ^ 1>{}, r_c, rst, rs);
+        });
+        if constexpr (NOPS > 0) {
+          static_for<0, NOPS>([&](auto k_c) {
+            constexpr int KK = decltype(k_c)::value;
+            if constexpr (((2 * KK + 1) * MF) / (2 * NOPS) == IDX) op(k_c);
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    // DMA variant: instructions [D0, D1) of K tile dma_tile (if it exists).
+    auto kstep = [&](auto cur_c, int rst, int rs, auto d0_c, auto d1_c, int dma_tile) {
+      constexpr int D0 = decltype(d0_c)::value, D1 = decltype(d1_c)::value;
+      const bool dma_live = dma_tile < KT;
+      kstep_ops(cur_c, rst, rs, IntC<D1 - D0>{}, [&](auto k_c) {
+        if (dma_live) dma_one(IntC<D0 + decltype(k_c)::value>{}, dma_tile);
+      });
+    };
+    // Wait until at most `pend` DMA groups (K tiles) of this wave are in
+    // flight (loads complete in order).
+    auto wait_pending = [&](int pend) {
+      if constexpr (S >= 4) {
+        if (pend >= 3) wait_vmcnt<3 * NQ_STAGE>();
+        else if (pend == 2) wait_vmcnt<2 * NQ_STAGE>();
+        else if (pend == 1) wait_vmcnt<NQ_STAGE>();
+        else wait_vmcnt<0>();
+      } else if constexpr (S == 3) {
+        if (pend >= 1) wait_vmcnt<NQ_STAGE>();
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    };
+    // DMA of one K tile is spread over the first KSTEPS-1 steps of a tile.
+    constexpr int DSTEPS = CF::KSTEPS - 1;
+    auto steps_before_last = [&](int st, int dma_tile) {
+      static_for<0, DSTEPS>([&](auto s_c) {
+        constexpr int SS = decltype(s_c)::value;
+        kstep(IntC<SS & 1>{}, st, SS + 1, IntC<SS * NQ_STAGE / DSTEPS>{},
+              IntC<(SS + 1) * NQ_STAGE / DSTEPS>{}, dma_tile);
+      });
+    };
+
+    if constexpr (CF::A_KMAJOR && CF::LOADER == 1) {
+      // ---- K-major A, register-staged loads, two LDS stages --------------
+      // Tile kt+2 is loaded to registers during tile kt and written to LDS
+      // (stage kt+2 % 2, free since the barrier of tile kt+1) during tile
+      // kt+1, before that tile's barrier makes it visible.
+      KMajorRegStager<CF, BM> ra_;
+      KMajorRegStager<CF, BN> rb_;
+      ra_.setup(Ab + (int64_t)m0 * kbytes, kbytes, (int)min((int64_t)BM, p.M - m0), wave, lane);
+      rb_.setup(Bb + (int64_t)n0 * kbytes, kbytes, (int)min((int64_t)BN, p.N - n0), wave, lane);
+      constexpr int QA = KMajorRegStager<CF, BM>::NQ, QB = KMajorRegStager<CF, BN>::NQ;
+      auto load_tile = [&](auto buf_c, int k_tile) {
+        constexpr int BUF = decltype(buf_c)::value;
+        const int64_t kv = kbytes - (int64_t)k_tile * CF::ROWB;
+        static_for<0, QA>([&](auto q) { ra_.template load<BUF, decltype(q)::value>(k_tile, kv); });
+        static_for<0, QB>([&](auto q) { rb_.template load<BUF, decltype(q)::value>(k_tile, kv); });
+      };
+      auto store_tile = [&](auto buf_c, int st) {
+        constexpr int BUF = decltype(buf_c)::value;
+        const int off = st * CF::STAGE_BYTES;
+        static_for<0, QA>([&](auto q) { ra_.template store<BUF, decltype(q)::value>(lds, off); });
+        static_for<0, QB>([&](auto q) { rb_.template store<BUF, decltype(q)::value>(lds, off + BM * CF::ROWB); });
+      };
+      // ops of a tile's first step: write tile kt+1 (register stage WBUF) to
+      // LDS stage WST, then load tile kt+2 into register stage LBUF
+      auto first_step_ops = [&](auto wbuf_c, int wst, auto lbuf_c, int ltile, bool lload) {
+        constexpr int WB = decltype(wbuf_c)::value, LB = decltype(lbuf_c)::value;
+        const int woff = wst * CF::STAGE_BYTES;
+        const int64_t kv = kbytes - (int64_t)ltile * CF::ROWB;
+        return [&, woff, kv, lload, ltile](auto k_c) {
+          constexpr int K2 = decltype(k_c)::value;
+          if constexpr (K2 < QA) ra_.template store<WB, K2>(lds, woff);
+          else if constexpr (K2 < QA + QB) rb_.template store<WB, K2 - QA>(lds, woff + BM * CF::ROWB);
+          else if constexpr (K2 < 2 * QA + QB) { if (lload) ra_.template load<LB, K2 - QA - QB>(ltile, kv); }
+          else { if (lload) rb_.template load<LB, K2 - 2 * QA - QB>(ltile, kv); }
+        };
+      };
+      constexpr int NOPS1 = 2 * (QA + QB);
+      // prologue: tile 0 -> regs 0 -> LDS stage 0; tile 1 -> regs 1
+      load_tile(IntC<0>{}, 0);
+      store_tile(IntC<0>{}, 0);
+      if (1 < KT) load_tile(IntC<1>{}, 1);
+      barrier_lds();
+      load_step(fa[0], fb[0], 0, 0);
+      auto tile_iter = [&](auto par_c, int kt) {
+        constexpr int P = decltype(par_c)::value;  // kt % 2
+        const int st = P, nst = P ^ 1;
+        // step 0: write tile kt+1 (regs P^1) to stage kt+1; load tile kt+2 to regs P
+        kstep_ops(IntC<0>{}, st, 1, IntC<NOPS1>{},
+                  first_step_ops(IntC<P ^ 1>{}, nst, IntC<P>{}, kt + 2, kt + 2 < KT));
+        static_for<1, CF::KSTEPS - 1>([&](auto s_c) {
+          constexpr int SS = decltype(s_c)::value;
+          kstep_ops(IntC<SS & 1>{}, st, SS + 1, IntC<0>{}, [](auto) {});
+        });
+        barrier_lds();  // tile kt+1 written and visible; stage kt no longer read
+        kstep_ops(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, [](auto) {});
+      };
+      static_assert(CF::KSTEPS >= 2, "register loader needs two k steps per tile");
+      int kt = 0;
+      for (; kt + 1 < KT; kt += 2) {
+        tile_iter(IntC<0>{}, kt);
+        tile_iter(IntC<1>{}, kt + 1);
+      }
+      if (kt < KT) tile_iter(IntC<0>{}, kt);
+    } else     if constexpr (CF::A_KMAJOR) {
+      // Two stages: K tile kt+2 is issued in the last step of tile kt (just
+      // after the barrier frees stage kt), so it has a whole K tile of
+      // slack.  Deep ring (S >= 3): tile kt+S-1 refills stage kt-1 during
+      // the first steps of tile kt.
+      if constexpr (S == 2) {
+        issue_dma(0);
+        if (1 < KT) {
+          issue_dma(1);
+          wait_vmcnt<NQ_STAGE>();
+        } else {
+          wait_vmcnt<0>();
+        }
+      } else {
+        // K tiles 0 .. S-2 in flight; tile 0 must be complete.
+#pragma unroll
+        for (int k = 0; k < S - 1; ++k)
+          if (k < KT) issue_dma(k);
+        wait_pending(min(S - 1, KT) - 1);
+      }
+      barrier_lds();
+      load_step(fa[0], fb[0], 0, 0);
+      for (int kt = 0; kt < KT; ++kt) {
+        const int st = kt % S, nst = (kt + 1) % S;
+        steps_before_last(st, S == 2 ? KT : kt + S - 1);
+        // Tile kt+1 (read by the last step) must be complete; the groups
+        // issued after it (deep ring: min(S-2, KT-2-kt)) may still pend.
+        if constexpr (S == 2) wait_vmcnt<0>();
+        else wait_pending(min(S - 2, KT - 2 - kt));
+        barrier_lds();  // tile kt+1 visible; every wave is done reading stage kt
+        // Last step: its fragments are in registers; read step 0 of tile kt+1
+        // meanwhile (two stages: and refill stage kt with tile kt+2).
+        if constexpr (S == 2)
+          kstep(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, IntC<NQ_STAGE>{}, kt + 2);
+        else
+          kstep(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, IntC<0>{}, KT);
+      }
+      wait_vmcnt<0>();
     } else {
+      // ---- M-major one-byte A: registers + transpose, B by DMA -----------
+      MMajorStager8<CF> sa_m;
+      sa_m.setup(Ab, p.M, p.K, m0);
       sa_m.load(0, tid);
       sa_m.store(lds, 0, tid);
-    }
-    sb.issue(lds, BM * 128, wave, 0, kbytes);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    // ---- mainloop ---------------------------------------------------------
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = (kt & 1) * CF::STAGE_BYTES;
-      const int nxt = ((kt + 1) & 1) * CF::STAGE_BYTES;
-      const bool more = kt + 1 < KT;
-      if (more) {
-        const int64_t kv = kbytes - (int64_t)(kt + 1) * 128;
-        if constexpr (CF::A_KMAJOR)
-          sa_k.issue(lds, nxt, wave, kt + 1, kv);
-        else
+      sb.issue(lds_u32 + BM * CF::ROWB, wave, 0, kbytes);
+      for (int kt = 0; kt < KT; ++kt) {
+        wait_vmcnt<0>();
+        barrier_lds();  // stage kt complete; stage kt+1 free
+        const bool more = kt + 1 < KT;
+        const int nxt = ((kt + 1) % S) * CF::STAGE_BYTES;
+        if (more) {
           sa_m.load(kt + 1, tid);
-        sb.issue(lds, nxt + BM * 128, wave, kt + 1, kv);
-      }
-#pragma unroll
-      for (int s = 0; s < CF::KSTEPS; ++s) {
-        typename MM::frag_t fa[CF::FM], fb[CF::FN];
-#pragma unroll
-        for (int i = 0; i < CF::FM; ++i)
-          fa[i] = read_frag<CF::AB>(lds, cur, wm * CF::WM + i * 32 + l32, s, half);
-#pragma unroll
-        for (int j = 0; j < CF::FN; ++j)
-          fb[j] = read_frag<CF::AB>(lds, cur + BM * 128, wn * CF::WN + j * 32 + l32, s, half);
-#pragma unroll
-        for (int i = 0; i < CF::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < CF::FN; ++j) acc[i][j] = MM::mma(fa[i], fb[j], acc[i][j]);
-      }
-      if constexpr (!CF::A_KMAJOR) {
+          sb.issue(lds_u32 + nxt + BM * CF::ROWB, wave, kt + 1, kbytes - (int64_t)(kt + 1) * CF::ROWB);
+        }
+        load_step(fa[0], fb[0], kt % S, 0);
+        compute(kt % S, kt % S, KT, IntC<0>{});
         if (more) sa_m.store(lds, nxt, tid);
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
     }
+    barrier_lds();  // every wave is done reading the ring
 
     // ---- fused epilogue ---------------------------------------------------
-    // Each wave re-lays its 128x128 accumulator quarter out through a private
-    // LDS region, half at a time (64 lines of 128 contiguous elements, lines
-    // padded to 132 words), then walks it with one 16-byte LDS read per lane:
-    // 32 lanes cover one 128-element line, so C/X loads and D/Y stores move 4
-    // contiguous elements per lane and whole lines per half-wave.
     epilogue<CF>(p, acc, lds, wave, lane, l, m0 + wm * CF::WM, n0 + wn * CF::WN);
-    __syncthreads();  // LDS is reused by the next tile's prologue
+    barrier_lds();  // LDS is reused by the next tile's prologue
   }
 }
 
