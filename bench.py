@@ -93,8 +93,8 @@ def cpu_baseline(p, ins, target_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2,
                     help="workload index 0..4 (2 = 8192^3 fp16 with C, X, D, Y)")
     ap.add_argument("--variant", type=int, default=-1)

@@ -70,35 +70,40 @@ using namespace gemm_epi;
 // The first variant that fits a problem is its default.
 #define V(AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, NAME) \
   make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S>>(NAME)
+#define VD(AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, DS, NAME) \
+  make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, 0, DS>>(NAME)
 #define VR(AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, NAME) \
   make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, 1>>(NAME)
 const Variant kVariants[] = {
-    V(T_F16, true, true, true, 256, 256, 64, 2, 2, 4, "f16_kk_n_256x256_r64_w4_s4"),
-    V(T_F16, true, true, true, 256, 256, 128, 2, 2, 2, "f16_kk_n_256x256_r128_w4_s2"),
-    V(T_F16, true, true, true, 256, 256, 64, 2, 2, 3, "f16_kk_n_256x256_r64_w4_s3"),
+    // f16, K-major A/B: default first
     V(T_F16, true, true, true, 256, 256, 128, 2, 4, 2, "f16_kk_n_256x256_r128_w8_s2"),
+    V(T_F16, true, true, false, 256, 256, 128, 2, 4, 2, "f16_kk_m_256x256_r128_w8_s2"),
+    V(T_F16, true, true, true, 256, 256, 128, 2, 2, 2, "f16_kk_n_256x256_r128_w4_s2"),
     V(T_F16, true, true, true, 256, 256, 64, 2, 4, 4, "f16_kk_n_256x256_r64_w8_s4"),
+    V(T_F16, true, true, true, 256, 256, 64, 2, 2, 4, "f16_kk_n_256x256_r64_w4_s4"),
     V(T_F16, true, true, true, 256, 128, 128, 2, 2, 3, "f16_kk_n_256x128_r128_w4_s3"),
-    V(T_F16, true, true, true, 256, 256, 64, 2, 2, 5, "f16_kk_n_256x256_r64_w4_s5"),
-    V(T_F16, true, true, true, 256, 256, 64, 2, 4, 5, "f16_kk_n_256x256_r64_w8_s5"),
     VR(T_F16, true, true, true, 256, 256, 64, 2, 4, 2, "f16_kk_n_256x256_r64_w8_s2_reg"),
-    VR(T_F16, true, true, true, 256, 256, 64, 2, 2, 2, "f16_kk_n_256x256_r64_w4_s2_reg"),
-    VR(T_F16, true, true, true, 256, 256, 128, 2, 4, 2, "f16_kk_n_256x256_r128_w8_s2_reg"),
-    V(T_F16, true, true, false, 256, 256, 64, 2, 2, 4, "f16_kk_m_256x256_r64_w4_s4"),
-    V(T_BF16, true, true, true, 256, 256, 64, 2, 2, 4, "bf16_kk_n_256x256_r64_w4_s4"),
+    VD(T_F16, true, true, true, 256, 256, 128, 2, 2, 2, 2, "f16_kk_n_256x256_r128_w4_s2_d2"),
+    VD(T_F16, true, true, true, 256, 256, 128, 2, 2, 2, 4, "f16_kk_n_256x256_r128_w4_s2_d4"),
+    VD(T_F16, true, true, true, 256, 256, 128, 2, 4, 2, 2, "f16_kk_n_256x256_r128_w8_s2_d2"),
+    // bf16
+    V(T_BF16, true, true, true, 256, 256, 128, 2, 4, 2, "bf16_kk_n_256x256_r128_w8_s2"),
+    V(T_BF16, true, true, false, 256, 256, 128, 2, 4, 2, "bf16_kk_m_256x256_r128_w8_s2"),
     V(T_BF16, true, true, true, 256, 128, 128, 2, 2, 3, "bf16_kk_n_256x128_r128_w4_s3"),
-    V(T_BF16, true, true, false, 256, 256, 64, 2, 2, 4, "bf16_kk_m_256x256_r64_w4_s4"),
+    // fp8 e4m3
+    V(T_E4M3, true, true, true, 256, 256, 128, 2, 4, 2, "e4m3_kk_n_256x256_r128_w8_s2"),
+    V(T_E4M3, true, true, false, 256, 256, 128, 2, 4, 2, "e4m3_kk_m_256x256_r128_w8_s2"),
     V(T_E4M3, true, true, true, 256, 256, 128, 2, 2, 2, "e4m3_kk_n_256x256_r128_w4_s2"),
-    V(T_E4M3, true, true, true, 256, 128, 128, 2, 2, 3, "e4m3_kk_n_256x128_r128_w4_s3"),
-    V(T_E4M3, true, true, false, 256, 256, 128, 2, 2, 2, "e4m3_kk_m_256x256_r128_w4_s2"),
-    V(T_I8, true, true, true, 256, 256, 64, 2, 2, 4, "i8_kk_n_256x256_r64_w4_s4"),
-    V(T_I8, true, true, false, 256, 256, 64, 2, 2, 4, "i8_kk_m_256x256_r64_w4_s4"),
+    // int8
+    V(T_I8, true, true, true, 256, 256, 128, 2, 4, 2, "i8_kk_n_256x256_r128_w8_s2"),
+    V(T_I8, true, true, false, 256, 256, 128, 2, 4, 2, "i8_kk_m_256x256_r128_w8_s2"),
     V(T_I8, false, true, true, 256, 256, 64, 2, 2, 2, "i8_mk_n_256x256_r64_w4_s2"),
-    V(T_I8, false, true, true, 256, 256, 128, 2, 2, 2, "i8_mk_n_256x256_r128_w4_s2"),
     V(T_I8, false, true, false, 256, 256, 64, 2, 2, 2, "i8_mk_m_256x256_r64_w4_s2"),
+    V(T_I8, false, true, true, 256, 256, 128, 2, 4, 2, "i8_mk_n_256x256_r128_w8_s2"),
 };
 #undef V
 #undef VR
+#undef VD
 constexpr int kNumVariants = (int)(sizeof kVariants / sizeof kVariants[0]);
 
 int elem_bytes(int t) {

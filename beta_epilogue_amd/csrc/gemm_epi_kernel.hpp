@@ -119,9 +119,14 @@ template <> struct Mma<T_E4M3> {
 //   WAVES_M/N   wave grid; each wave owns (BM/WAVES_M) x (BN/WAVES_N)
 //   STAGES      depth of the LDS ring
 //   LOADER      how K-major tiles reach LDS (see below)
+//   DSPREAD     k steps the two-stage ring spreads one K tile's DMA over
 template <int AB_, bool A_KMAJOR_, bool B_KMAJOR_, bool CD_NMAJOR_, int BM_ = 256, int BN_ = 256,
-          int ROWB_ = 128, int WAVES_M_ = 2, int WAVES_N_ = 2, int STAGES_ = 2, int LOADER_ = 0>
+          int ROWB_ = 128, int WAVES_M_ = 2, int WAVES_N_ = 2, int STAGES_ = 2, int LOADER_ = 0,
+          int DSPREAD_ = 1>
 struct Cfg {
+  // Two-stage DMA ring: the loads of K tile kt+2 are spread over DSPREAD
+  // k steps, starting with the last step of tile kt.
+  static constexpr int DSPREAD = DSPREAD_;
   // LOADER 0: K-major tiles go global -> LDS by buffer_load ... lds (DMA).
   // LOADER 1: global -> VGPR by buffer_load_dwordx4, then ds_write_b128
   //           (two register stages in flight; LDS writes use the LDS's own
@@ -782,8 +787,18 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     auto steps_before_last = [&](int st, int dma_tile) {
       static_for<0, DSTEPS>([&](auto s_c) {
         constexpr int SS = decltype(s_c)::value;
-        kstep(IntC<SS & 1>{}, st, SS + 1, IntC<SS * NQ_STAGE / DSTEPS>{},
-              IntC<(SS + 1) * NQ_STAGE / DSTEPS>{}, dma_tile);
+        if constexpr (S == 2) {
+          // parts 1 .. DSPREAD-1 of the tile issued in the previous last step
+          constexpr int DP = CF::DSPREAD;
+          if constexpr (SS < DP - 1)
+            kstep(IntC<SS & 1>{}, st, SS + 1, IntC<(SS + 1) * NQ_STAGE / DP>{},
+                  IntC<(SS + 2) * NQ_STAGE / DP>{}, dma_tile);
+          else
+            kstep(IntC<SS & 1>{}, st, SS + 1, IntC<0>{}, IntC<0>{}, KT);
+        } else {
+          kstep(IntC<SS & 1>{}, st, SS + 1, IntC<SS * NQ_STAGE / DSTEPS>{},
+                IntC<(SS + 1) * NQ_STAGE / DSTEPS>{}, dma_tile);
+        }
       });
     };
 
@@ -874,7 +889,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       load_step(fa[0], fb[0], 0, 0);
       for (int kt = 0; kt < KT; ++kt) {
         const int st = kt % S, nst = (kt + 1) % S;
-        steps_before_last(st, S == 2 ? KT : kt + S - 1);
+        // (two stages: the rest of tile kt+1, unless the prologue issued it)
+        steps_before_last(st, S == 2 ? (kt >= 1 ? kt + 1 : KT) : kt + S - 1);
         // Tile kt+1 (read by the last step) must be complete; the groups
         // issued after it (deep ring: min(S-2, KT-2-kt)) may still pend.
         if constexpr (S == 2) wait_vmcnt<0>();
@@ -883,7 +899,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
         // Last step: its fragments are in registers; read step 0 of tile kt+1
         // meanwhile (two stages: and refill stage kt with tile kt+2).
         if constexpr (S == 2)
-          kstep(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, IntC<NQ_STAGE>{}, kt + 2);
+          kstep(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, IntC<NQ_STAGE / CF::DSPREAD>{}, kt + 2);
         else
           kstep(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, IntC<0>{}, KT);
       }
