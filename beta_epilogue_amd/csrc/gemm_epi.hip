@@ -86,6 +86,9 @@ const Variant kVariants[] = {
     VD(T_F16, true, true, true, 256, 256, 128, 2, 2, 2, 2, "f16_kk_n_256x256_r128_w4_s2_d2"),
     VD(T_F16, true, true, true, 256, 256, 128, 2, 2, 2, 4, "f16_kk_n_256x256_r128_w4_s2_d4"),
     VD(T_F16, true, true, true, 256, 256, 128, 2, 4, 2, 2, "f16_kk_n_256x256_r128_w8_s2_d2"),
+    V(T_F16, true, true, true, 256, 256, 64, 2, 4, 5, "f16_kk_n_256x256_r64_w8_s5"),
+    V(T_F16, true, true, true, 256, 256, 64, 2, 2, 5, "f16_kk_n_256x256_r64_w4_s5"),
+    V(T_F16, true, true, true, 256, 256, 64, 2, 4, 3, "f16_kk_n_256x256_r64_w8_s3"),
     // bf16
     V(T_BF16, true, true, true, 256, 256, 128, 2, 4, 2, "bf16_kk_n_256x256_r128_w8_s2"),
     V(T_BF16, true, true, false, 256, 256, 128, 2, 4, 2, "bf16_kk_m_256x256_r128_w8_s2"),
@@ -309,6 +312,16 @@ extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void*
   p.ibeta = int_path ? (int32_t)beta : 0;
   p.ix = int_path ? (int32_t)x_factor : 0;
   p.xcd_remap = (h->grid % 8 == 0) ? 1 : 0;
+  // Element type shared by every C/X/D/Y in use (typed epilogue), else 0.
+  // The typed epilogue addresses a wave's output region (at most a tile's
+  // BM or BN lines of the leading extent) with 31-bit byte offsets.
+  int kind = d.d_dtype;
+  for (int t : {use_c ? d.c_dtype : 0, use_x ? d.x_dtype : 0, d.y_dtype})
+    if (t != GEMM_EPI_NONE && t != kind) kind = 0;
+  const Variant& v = kVariants[h->variant];
+  const int64_t ld = d.cd_major == GEMM_EPI_MAJOR_N ? d.N : d.M;
+  if ((int64_t)(v.bm > v.bn ? v.bm : v.bn) * ld * 4 >= (int64_t(1) << 31)) kind = 0;
+  p.epi_kind = kind;
 
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   kVariants[h->variant].launch(p, h->grid, (hipStream_t)stream);

@@ -66,6 +66,7 @@ struct Params {
   float alpha, beta, xf;
   int32_t ialpha, ibeta, ix;  // integral scalars for int32 outputs
   int32_t xcd_remap;          // grid is a multiple of 8: remap ids per XCD
+  int32_t epi_kind;           // element type shared by every C/X/D/Y in use (0: mixed)
 };
 
 // ---------------------------------------------------------------------------
@@ -217,6 +218,21 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds_addr, uint32_t voff
       : "memory", "m0");
 }
 
+// The mainloop form: LDS address m0 = sbase + IMM (IMM a compile-time
+// constant folded into the m0 write), global offset voff (per lane) + soff
+// (the K tile's byte offset, a scalar), so one load costs three issue slots
+// and no vector ALU work.
+template <uint32_t IMM>
+__device__ __forceinline__ void dma16s(v4i rsrc, uint32_t sbase, uint32_t voff, uint32_t soff) {
+  asm volatile(
+      "s_add_u32 m0, %0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(sbase), "v"(voff), "s"(rsrc), "s"(soff), "i"(IMM)
+      : "memory", "m0", "scc");
+}
+
 // Raw buffer descriptor: base, stride 0, num_records bytes, default format.
 __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t nbytes) {
   const uint64_t a = (uint64_t)base;
@@ -232,20 +248,25 @@ template <class CF, int R>
 struct KMajorStager {
   static constexpr int NQ = R / (CF::ROWS_PER_DMA * CF::NW);
   static_assert(NQ * CF::ROWS_PER_DMA * CF::NW == R, "rows must split evenly over the waves");
+  // Consecutive instructions of one wave are NW*ROWS_PER_DMA rows apart, a
+  // whole number of swizzle periods, so a lane fetches the same logical
+  // chunk of its row in every instruction.
+  static_assert((CF::NW * CF::ROWS_PER_DMA) % (CF::CH << CF::SWZ_SHIFT) == 0,
+                "one chunk offset per lane for all instructions");
   v4i rsrc;
   uint32_t voff[NQ];
-  uint32_t cb[NQ];  // byte offset of this lane's logical chunk within its row
+  uint32_t cb;  // byte offset of this lane's logical chunk within its row
 
   __device__ __forceinline__ void setup(const char* tile_base, int64_t ld_bytes, int valid_rows,
                                         int wave, int lane) {
     const int rsub = lane / CF::CH;
     const int pc = lane % CF::CH;
     rsrc = make_rsrc(tile_base, (uint32_t)((int64_t)valid_rows * ld_bytes));
+    cb = (uint32_t)((pc ^ swz<CF>(wave * CF::ROWS_PER_DMA + rsub)) * 16);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int row = (q * CF::NW + wave) * CF::ROWS_PER_DMA + rsub;
-      cb[q] = (uint32_t)((pc ^ swz<CF>(row)) * 16);
-      voff[q] = (uint32_t)(row * ld_bytes) + cb[q];
+      voff[q] = (uint32_t)(row * ld_bytes) + cb;
     }
   }
 
@@ -253,6 +274,17 @@ struct KMajorStager {
   // address lds_addr (LDS address space).  kvalid = bytes of K left from
   // this K tile on; chunks at or past it get an out-of-range offset and read
   // as zero.
+  // Instruction Q of a K tile: LDS byte address sbase + REGION + Q*NW KiB
+  // (sbase = the stage's address plus this wave's KiB), global offset kofs
+  // into each row.  GUARD: kvalid = bytes of K left from kofs (> 0); chunks
+  // at or past it read as zero.  Without GUARD the K tile is whole.
+  template <int Q, uint32_t REGION, bool GUARD>
+  __device__ __forceinline__ void issue_one(uint32_t sbase, uint32_t kofs, int kvalid) {
+    uint32_t vo = voff[Q];
+    if constexpr (GUARD) vo = (int)cb < kvalid ? vo : 0x80000000u;
+    dma16s<REGION + (uint32_t)Q * CF::NW * 1024u>(rsrc, sbase, vo, kofs);
+  }
+
   template <int Q0 = 0, int Q1 = NQ>
   __device__ __forceinline__ void issue(uint32_t lds_addr, int wave, int kt, int64_t kvalid) {
     const uint32_t kofs = (uint32_t)kt * (uint32_t)CF::ROWB;
@@ -263,7 +295,7 @@ struct KMajorStager {
     } else {
 #pragma unroll
       for (int q = Q0; q < Q1; ++q) {
-        const uint32_t vo = (int64_t)cb[q] < kvalid ? voff[q] + kofs : 0x80000000u;
+        const uint32_t vo = (int64_t)cb < kvalid ? voff[q] + kofs : 0x80000000u;
         dma16(rsrc, lds_addr + (uint32_t)((q * CF::NW + wave) * 1024), vo);
       }
     }
@@ -486,6 +518,12 @@ __device__ __forceinline__ v4f epi_decode4(v4u r, int dt) {
 // (32 rows x WN columns, lines = rows), for M-major a block column (WM rows x
 // 32 columns, lines = columns).  Then each lane reads 4 contiguous elements
 // (one ds_read_b128) and does the element work for them.
+//
+// The passes of all blocks form one chain of chunks.  The C and X loads of
+// chunk c+1 are issued before the D and Y stores of chunk c: vmcnt retires
+// loads and stores in issue order, so waiting for a chunk's loads then never
+// waits for an earlier chunk's stores to reach memory, and each chunk's load
+// latency hides under the previous chunk's work.
 template <class CF, class ACC>
 __device__ __forceinline__ void epilogue(const Params& p, const ACC (&acc)[CF::FM][CF::FN], char* lds,
                                          int wave, int lane, int l, int mw, int nw) {
@@ -497,8 +535,16 @@ __device__ __forceinline__ void epilogue(const Params& p, const ACC (&acc)[CF::F
   const int half = lane >> 5, l32 = lane & 31;
   const int64_t obase = (int64_t)l * p.M * p.N;
   constexpr int NBLK = NMAJ ? CF::FM : CF::FN;
-#pragma unroll
-  for (int blk = 0; blk < NBLK; ++blk) {
+  constexpr int PASSES = 32 / LINES_PER_PASS;
+  constexpr int CMAX = CF::NW > 4 ? 4 : 8;  // two waves per SIMD: half the registers
+  constexpr int CHUNK = PASSES < CMAX ? PASSES : CMAX;
+  constexpr int CPB = PASSES / CHUNK;      // chunks per block
+  constexpr int NCH = NBLK * CPB;
+  const int sub = lane / LPL;
+  const int e = (lane % LPL) * 4;
+
+  auto write_block = [&](auto blk_c) {
+    constexpr int blk = decltype(blk_c)::value;
     if constexpr (NMAJ) {
       // block row blk: lane holds rows 8*(v/4) + 4*half + v%4, column j*32 + l32
       float* wp = region + (half * 4) * PITCH + l32;
@@ -506,8 +552,8 @@ __device__ __forceinline__ void epilogue(const Params& p, const ACC (&acc)[CF::F
       for (int j = 0; j < CF::FN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const auto e = acc[blk][j][v];
-          wp[((v >> 2) * 8 + (v & 3)) * PITCH + j * 32] = acc_bits(e);
+          const auto x = acc[blk][j][v];
+          wp[((v >> 2) * 8 + (v & 3)) * PITCH + j * 32] = acc_bits(x);
         }
     } else {
       // block column blk: lane holds column l32, rows i*32 + 8*v4 + 4*half + 0..3
@@ -521,57 +567,234 @@ __device__ __forceinline__ void epilogue(const Params& p, const ACC (&acc)[CF::F
           *(v4f*)(wp + i * 32 + v4 * 8) = v4f{acc_bits(e0), acc_bits(e1), acc_bits(e2), acc_bits(e3)};
         }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const int sub = lane / LPL;
-    const int e = (lane % LPL) * 4;
-    // Passes are done in chunks: all loads of a chunk (accumulator values
-    // from LDS, C and X from memory) are issued before any of its math, so a
-    // chunk costs one memory round trip instead of one per pass.
-    constexpr int PASSES = 32 / LINES_PER_PASS;
-    constexpr int CMAX = CF::NW > 4 ? 4 : 8;  // two waves per SIMD: half the registers
-    constexpr int CHUNK = PASSES < CMAX ? PASSES : CMAX;
+  };
+  // Output coordinates of pass `ps` of block `blk` for this lane.
+  auto coords = [&](int blk, int ps, int64_t& o) -> bool {
+    const int line = ps * LINES_PER_PASS + sub;
+    int64_t m, n;
+    if constexpr (NMAJ) {
+      m = mw + blk * 32 + line;
+      n = nw + e;
+    } else {
+      n = nw + blk * 32 + line;
+      m = mw + e;
+    }
+    o = obase + (NMAJ ? m * p.N + n : n * p.M + m);
+    return m < p.M && n < p.N;
+  };
+  v4u cr[2][CHUNK], xr[2][CHUNK];
+  auto load_chunk = [&](auto c_c) {
+    constexpr int c = decltype(c_c)::value, B = c & 1;
 #pragma unroll
-    for (int c0 = 0; c0 < PASSES; c0 += CHUNK) {
-      v4f w[CHUNK];
-      v4u cr[CHUNK], xr[CHUNK];
-      int64_t off[CHUNK];
-      bool ok[CHUNK];
-#pragma unroll
-      for (int q = 0; q < CHUNK; ++q) {
-        const int line = (c0 + q) * LINES_PER_PASS + sub;
-        w[q] = *(const v4f*)(region + line * PITCH + e);
-        int64_t m, n;
-        if constexpr (NMAJ) {
-          m = mw + blk * 32 + line;
-          n = nw + e;
-        } else {
-          n = nw + blk * 32 + line;
-          m = mw + e;
-        }
-        ok[q] = m < p.M && n < p.N;
-        off[q] = obase + (NMAJ ? m * p.N + n : n * p.M + m);
-        cr[q] = v4u{};
-        xr[q] = v4u{};
-        if (ok[q]) {
-          if (p.c_dtype) cr[q] = epi_raw4(p.C, p.c_dtype, off[q]);
-          if (p.x_dtype) xr[q] = epi_raw4(p.X, p.x_dtype, off[q]);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < CHUNK; ++q) {
-        v4f cv, xv;
-        if constexpr (CF::AB == T_I8) {
-          cv = __builtin_bit_cast(v4f, cr[q]);
-          xv = __builtin_bit_cast(v4f, xr[q]);
-        } else {
-          cv = epi_decode4(cr[q], p.c_dtype);
-          xv = epi_decode4(xr[q], p.x_dtype);
-        }
-        if (ok[q]) epi_finish4<CF>(p, off[q], w[q], cv, xv);
+    for (int q = 0; q < CHUNK; ++q) {
+      int64_t o;
+      const bool ok = coords(c / CPB, (c % CPB) * CHUNK + q, o);
+      cr[B][q] = v4u{};
+      xr[B][q] = v4u{};
+      if (ok) {
+        if (p.c_dtype) cr[B][q] = epi_raw4(p.C, p.c_dtype, o);
+        if (p.x_dtype) xr[B][q] = epi_raw4(p.X, p.x_dtype, o);
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  load_chunk(IntC<0>{});
+  static_for<0, NCH>([&](auto c_c) {
+    constexpr int c = decltype(c_c)::value, B = c & 1;
+    constexpr int blk = c / CPB, p0 = (c % CPB) * CHUNK;
+    if constexpr (c % CPB == 0) {
+      // this wave's reads of the previous block are issued before these
+      // writes, and LDS serves one wave's operations in order
+      write_block(IntC<blk>{});
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    v4f w[CHUNK];
+#pragma unroll
+    for (int q = 0; q < CHUNK; ++q)
+      w[q] = *(const v4f*)(region + ((p0 + q) * LINES_PER_PASS + sub) * PITCH + e);
+    if constexpr (c + 1 < NCH) load_chunk(IntC<c + 1>{});
+#pragma unroll
+    for (int q = 0; q < CHUNK; ++q) {
+      int64_t o;
+      const bool ok = coords(blk, p0 + q, o);
+      v4f cv, xv;
+      if constexpr (CF::AB == T_I8) {
+        cv = __builtin_bit_cast(v4f, cr[B][q]);
+        xv = __builtin_bit_cast(v4f, xr[B][q]);
+      } else {
+        cv = epi_decode4(cr[B][q], p.c_dtype);
+        xv = epi_decode4(xr[B][q], p.x_dtype);
+      }
+      if (ok) epi_finish4<CF>(p, o, w[q], cv, xv);
+    }
+  });
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue for one element type T shared by every C, X, D and Y in use (the
+// common case), same re-layout as above.  Each array is addressed through a
+// buffer resource based at this wave's output region with 32-bit offsets:
+// rows (N-major) or columns (M-major) past the matrix fall outside the
+// resource's extent, so their loads read zero and their stores are dropped
+// by the range check; a lane whose 4 elements lie past the other extent gets
+// an offset above 2^31.  A skipped term is an empty resource with a zero
+// scale; a missing Y is an empty resource.  C and X loads run DIST passes
+// ahead of the passes being finished.
+// ---------------------------------------------------------------------------
+template <int T> struct EpiElem;
+template <> struct EpiElem<T_F16> { static constexpr int SIZE = 2; };
+template <> struct EpiElem<T_BF16> { static constexpr int SIZE = 2; };
+template <> struct EpiElem<T_F32> { static constexpr int SIZE = 4; };
+template <> struct EpiElem<T_I32> { static constexpr int SIZE = 4; };
+
+constexpr int EPI_NT = 2;  // cache policy: streaming (non-temporal) access
+
+template <int T>
+__device__ __forceinline__ v4u epi_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (EpiElem<T>::SIZE == 2) {
+    const v2u u = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, EPI_NT));
+    return v4u{u.x, u.y, 0u, 0u};
+  } else {
+    return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, EPI_NT));
   }
+}
+
+template <int T>
+__device__ __forceinline__ v4f epi_dec4(v4u r) {
+  if constexpr (T == T_F16) {
+    const v2u h2 = {r.x, r.y};
+    const _Float16* h = (const _Float16*)&h2;
+    return v4f{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+  } else if constexpr (T == T_BF16) {
+    return v4f{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+               __uint_as_float(r.y & 0xffff0000u)};
+  } else {
+    return __builtin_bit_cast(v4f, r);
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void epi_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, v4f v) {
+  if constexpr (T == T_F16) {
+    _Float16 h[4] = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, h), r, (int)off, 0, EPI_NT);
+  } else if constexpr (T == T_BF16) {
+    __bf16 b[4] = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, b), r, (int)off, 0, EPI_NT);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, (int)off, 0, EPI_NT);
+  }
+}
+
+template <class CF, int T, class ACC>
+__device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)[CF::FM][CF::FN], char* lds,
+                                               int wave, int lane, int l, int mw, int nw) {
+  constexpr bool NMAJ = CF::CD_NMAJOR;
+  constexpr int LINE = CF::EPI_LINE, PITCH = CF::EPI_PITCH;
+  constexpr int LPL = LINE / 4;        // lanes per line
+  constexpr int LINES_PER_PASS = 64 / LPL;
+  constexpr int ES = EpiElem<T>::SIZE;
+  float* region = (float*)(lds + wave * CF::EPI_WAVE_BYTES);
+  const int half = lane >> 5, l32 = lane & 31;
+  constexpr int NBLK = NMAJ ? CF::FM : CF::FN;
+  constexpr int PASSES = 32 / LINES_PER_PASS;
+  constexpr int NP = NBLK * PASSES;
+  constexpr int DIST0 = ES == 2 ? 8 : 4;  // 32 VGPRs of C and X in flight
+  constexpr int DIST = DIST0 < NP ? DIST0 : NP;
+  const int sub = lane / LPL;
+  const int e = (lane % LPL) * 4;
+
+  // The wave's region: N-major rows [mw, mw+WM) (ld = N), M-major columns
+  // [nw, nw+WN) (ld = M); `lines` of them lie inside the matrix.
+  const int64_t ld = NMAJ ? p.N : p.M;
+  const int64_t line0 = NMAJ ? mw : nw;
+  const int64_t nlines = NMAJ ? p.M : p.N;
+  const int64_t lines = min(max(nlines - line0, (int64_t)0), (int64_t)(NMAJ ? CF::WM : CF::WN));
+  const int64_t slab = ((int64_t)l * (NMAJ ? p.M : p.N) + line0) * ld;  // element index of the base
+  const int records = (int)(lines * ld * ES);
+  auto rsrc = [&](const void* base, bool live) {
+    return __builtin_amdgcn_make_buffer_rsrc(live ? (void*)((const char*)base + slab * ES) : (void*)base,
+                                             (short)0, live ? records : 0, 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t rc = rsrc(p.C ? p.C : p.D, p.C != nullptr);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(p.X ? p.X : p.D, p.X != nullptr);
+  const __amdgpu_buffer_rsrc_t rd = rsrc(p.D, true);
+  const __amdgpu_buffer_rsrc_t ry = rsrc(p.Y ? p.Y : p.D, p.Y != nullptr);
+  const float beta = p.C ? p.beta : 0.0f;
+  const float xf = p.X ? p.xf : 0.0f;
+  // along the line: columns (N-major) or rows (M-major) of this lane
+  const int64_t along = (NMAJ ? nw : mw) + e;
+  const bool lane_ok = along < (NMAJ ? p.N : p.M);
+  const uint32_t lane_off = lane_ok ? (uint32_t)((sub * ld + along) * ES) : 0x80000000u;
+  auto off = [&](int i) {  // byte offset of pass i (block i / PASSES)
+    const int line = (i / PASSES) * 32 + (i % PASSES) * LINES_PER_PASS;
+    return lane_off + (uint32_t)(line * ld * ES);
+  };
+
+  auto write_block = [&](auto blk_c) {
+    constexpr int blk = decltype(blk_c)::value;
+    if constexpr (NMAJ) {
+      float* wp = region + (half * 4) * PITCH + l32;
+#pragma unroll
+      for (int j = 0; j < CF::FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const auto x = acc[blk][j][v];
+          wp[((v >> 2) * 8 + (v & 3)) * PITCH + j * 32] = acc_bits(x);
+        }
+    } else {
+      float* wp = region + l32 * PITCH + half * 4;
+#pragma unroll
+      for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const auto e0 = acc[i][blk][v4 * 4 + 0], e1 = acc[i][blk][v4 * 4 + 1];
+          const auto e2 = acc[i][blk][v4 * 4 + 2], e3 = acc[i][blk][v4 * 4 + 3];
+          *(v4f*)(wp + i * 32 + v4 * 8) = v4f{acc_bits(e0), acc_bits(e1), acc_bits(e2), acc_bits(e3)};
+        }
+    }
+  };
+
+  v4u cr[DIST + 1], xr[DIST + 1];
+  static_for<0, DIST>([&](auto i_c) {
+    constexpr int i = decltype(i_c)::value;
+    cr[i] = epi_ld4<T>(rc, off(i));
+    xr[i] = epi_ld4<T>(rx, off(i));
+  });
+  static_for<0, NP>([&](auto i_c) {
+    constexpr int i = decltype(i_c)::value, S = i % (DIST + 1);
+    constexpr int blk = i / PASSES, ps = i % PASSES;
+    // this wave's reads of the previous block are issued before these
+    // writes, and LDS serves one wave's operations in order
+    if constexpr (ps == 0) write_block(IntC<blk>{});
+    const v4f w = *(const v4f*)(region + (ps * LINES_PER_PASS + sub) * PITCH + e);
+    if constexpr (i + DIST < NP) {
+      constexpr int SN = (i + DIST) % (DIST + 1);
+      cr[SN] = epi_ld4<T>(rc, off(i + DIST));
+      xr[SN] = epi_ld4<T>(rx, off(i + DIST));
+    }
+    const uint32_t o = off(i);
+    if constexpr (T == T_I32) {
+      const v4u a = __builtin_bit_cast(v4u, w);
+      const v4u t = a * (unsigned)p.ialpha + cr[S] * (unsigned)p.ibeta + xr[S] * (unsigned)p.ix;
+      epi_st4<T>(rd, o, __builtin_bit_cast(v4f, t));
+      epi_st4<T>(ry, o, w);
+    } else {
+      const v4f c = epi_dec4<T>(cr[S]), x = epi_dec4<T>(xr[S]);
+      v4f t = w * p.alpha;
+      t.x = __builtin_fmaf(beta, c.x, t.x);
+      t.y = __builtin_fmaf(beta, c.y, t.y);
+      t.z = __builtin_fmaf(beta, c.z, t.z);
+      t.w = __builtin_fmaf(beta, c.w, t.w);
+      t.x = __builtin_fmaf(xf, x.x, t.x);
+      t.y = __builtin_fmaf(xf, x.y, t.y);
+      t.z = __builtin_fmaf(xf, x.z, t.z);
+      t.w = __builtin_fmaf(xf, x.w, t.w);
+      epi_st4<T>(rd, o, t);
+      epi_st4<T>(ry, o, w);
+    }
+  });
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 // Scheduling pattern for one k step: READS LDS reads spread evenly over
@@ -728,14 +951,21 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       else
         fa[BUF][R - CF::FN] = read_frag<CF>(lds, a_off, wm * CF::WM + (R - CF::FN) * 32 + l32, ks, half);
     };
-    auto dma_one = [&](auto d_c, int k_tile) {
+    // DMA instruction D of K tile k_tile into stage stg.  GUARD: the tile
+    // may not exist (k_tile >= KT) or may be cut by the end of K; without
+    // it the tile is whole and no check is made.
+    const uint32_t lds_wave = lds_u32 + (uint32_t)wave * 1024u;
+    auto dma_one = [&](auto d_c, auto guard_c, int k_tile, int stg) {
       constexpr int D = decltype(d_c)::value;
-      const int st = (k_tile % S) * CF::STAGE_BYTES;
-      const int64_t kv = kbytes - (int64_t)k_tile * CF::ROWB;
+      constexpr bool GUARD = decltype(guard_c)::value;
+      if (GUARD && k_tile >= KT) return;
+      const uint32_t sbase = lds_wave + (uint32_t)stg * (uint32_t)CF::STAGE_BYTES;
+      const uint32_t kofs = (uint32_t)k_tile * (uint32_t)CF::ROWB;
+      const int kv = GUARD ? (int)min(kbytes - (int64_t)kofs, (int64_t)CF::ROWB) : CF::ROWB;
       if constexpr (D < NQ_A)
-        sa_k.template issue<D, D + 1>(lds_u32 + st, wave, k_tile, kv);
+        sa_k.template issue_one<D, 0u, GUARD>(sbase, kofs, kv);
       else
-        sb.template issue<D - NQ_A, D - NQ_A + 1>(lds_u32 + st + BM * CF::ROWB, wave, k_tile, kv);
+        sb.template issue_one<D - NQ_A, (uint32_t)(BM * CF::ROWB), GUARD>(sbase, kofs, kv);
     };
     // One k step on buffer CUR: reads of (stage rst, step rs) into CUR^1 and
     // NOPS memory operations op(IntC<k>) spread evenly over the MFMAs.
@@ -759,12 +989,12 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
         __builtin_amdgcn_sched_barrier(0);
       });
     };
-    // DMA variant: instructions [D0, D1) of K tile dma_tile (if it exists).
-    auto kstep = [&](auto cur_c, int rst, int rs, auto d0_c, auto d1_c, int dma_tile) {
+    // DMA variant: instructions [D0, D1) of K tile dma_tile into stage dst.
+    auto kstep = [&](auto cur_c, int rst, int rs, auto d0_c, auto d1_c, auto guard_c, int dma_tile,
+                     int dst) {
       constexpr int D0 = decltype(d0_c)::value, D1 = decltype(d1_c)::value;
-      const bool dma_live = dma_tile < KT;
       kstep_ops(cur_c, rst, rs, IntC<D1 - D0>{}, [&](auto k_c) {
-        if (dma_live) dma_one(IntC<D0 + decltype(k_c)::value>{}, dma_tile);
+        dma_one(IntC<D0 + decltype(k_c)::value>{}, guard_c, dma_tile, dst);
       });
     };
     // Wait until at most `pend` DMA groups (K tiles) of this wave are in
@@ -782,24 +1012,36 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
         wait_vmcnt<0>();
       }
     };
-    // DMA of one K tile is spread over the first KSTEPS-1 steps of a tile.
-    constexpr int DSTEPS = CF::KSTEPS - 1;
-    auto steps_before_last = [&](int st, int dma_tile) {
-      static_for<0, DSTEPS>([&](auto s_c) {
+    // The DMA of one K tile is split into NPARTS equal parts.  Part 0 goes
+    // into the last step of K tile kt-S (right after the barrier that frees
+    // its stage) and part q into step q-1 of K tile kt-S+1.  Deep ring
+    // (S >= 3): NPARTS = KSTEPS, so the texture path (64 B/clk per CU, about
+    // half of what the MFMAs consume at full rate) is fed evenly and a tile
+    // lands S-2 K tiles before it is read.  Two stages: NPARTS = DSPREAD.
+    constexpr int NPARTS = S == 2 ? CF::DSPREAD : CF::KSTEPS;
+    static_assert(NPARTS >= 1 && NPARTS <= CF::KSTEPS, "DMA parts must fit the k steps of a tile");
+    // K tile kt from stage st; nst = stage of kt+1, pst = stage of kt-1
+    // (which tile t1 = kt+S-1 refills).  GUARD: DMA checks are needed.
+    auto k_tile = [&](auto guard_c, int kt, int st, int nst, int pst, int t1) {
+      constexpr bool GUARD = decltype(guard_c)::value;
+      static_for<0, CF::KSTEPS - 1>([&](auto s_c) {
         constexpr int SS = decltype(s_c)::value;
-        if constexpr (S == 2) {
-          // parts 1 .. DSPREAD-1 of the tile issued in the previous last step
-          constexpr int DP = CF::DSPREAD;
-          if constexpr (SS < DP - 1)
-            kstep(IntC<SS & 1>{}, st, SS + 1, IntC<(SS + 1) * NQ_STAGE / DP>{},
-                  IntC<(SS + 2) * NQ_STAGE / DP>{}, dma_tile);
-          else
-            kstep(IntC<SS & 1>{}, st, SS + 1, IntC<0>{}, IntC<0>{}, KT);
-        } else {
-          kstep(IntC<SS & 1>{}, st, SS + 1, IntC<SS * NQ_STAGE / DSTEPS>{},
-                IntC<(SS + 1) * NQ_STAGE / DSTEPS>{}, dma_tile);
-        }
+        if constexpr (SS + 1 < NPARTS)
+          kstep(IntC<SS & 1>{}, st, SS + 1, IntC<(SS + 1) * NQ_STAGE / NPARTS>{},
+                IntC<(SS + 2) * NQ_STAGE / NPARTS>{}, guard_c, t1, pst);
+        else
+          kstep(IntC<SS & 1>{}, st, SS + 1, IntC<0>{}, IntC<0>{}, guard_c, t1, pst);
       });
+      // Tile kt+1 (read by the last step) must be complete; the groups
+      // issued after it (deep ring: min(S-2, KT-2-kt) whole tiles) may pend.
+      if constexpr (S == 2) wait_vmcnt<0>();
+      else if constexpr (GUARD) wait_pending(min(S - 2, KT - 2 - kt));
+      else wait_vmcnt<(S - 2) * NQ_STAGE>();
+      barrier_lds();  // tile kt+1 visible; every wave is done reading stage kt
+      // Last step: its fragments are in registers; read step 0 of tile kt+1
+      // meanwhile and refill stage kt (free now) with part 0 of tile kt+S.
+      kstep(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, IntC<NQ_STAGE / NPARTS>{}, guard_c, kt + S,
+            st);
     };
 
     if constexpr (CF::A_KMAJOR && CF::LOADER == 1) {
@@ -865,11 +1107,10 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
         tile_iter(IntC<1>{}, kt + 1);
       }
       if (kt < KT) tile_iter(IntC<0>{}, kt);
-    } else     if constexpr (CF::A_KMAJOR) {
-      // Two stages: K tile kt+2 is issued in the last step of tile kt (just
-      // after the barrier frees stage kt), so it has a whole K tile of
-      // slack.  Deep ring (S >= 3): tile kt+S-1 refills stage kt-1 during
-      // the first steps of tile kt.
+    } else if constexpr (CF::A_KMAJOR) {
+      // Prologue: two stages: K tiles 0 and 1 whole, tile 0 complete.  Deep
+      // ring: K tiles 0 .. S-2 whole, tile 0 complete, then part 0 of tile
+      // S-1 (stage S-1 is untouched so far).
       if constexpr (S == 2) {
         issue_dma(0);
         if (1 < KT) {
@@ -879,29 +1120,33 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
           wait_vmcnt<0>();
         }
       } else {
-        // K tiles 0 .. S-2 in flight; tile 0 must be complete.
 #pragma unroll
         for (int k = 0; k < S - 1; ++k)
           if (k < KT) issue_dma(k);
         wait_pending(min(S - 1, KT) - 1);
+        static_for<0, NQ_STAGE / NPARTS>([&](auto d_c) { dma_one(d_c, IntC<1>{}, S - 1, S - 1); });
       }
       barrier_lds();
       load_step(fa[0], fb[0], 0, 0);
-      for (int kt = 0; kt < KT; ++kt) {
-        const int st = kt % S, nst = (kt + 1) % S;
-        // (two stages: the rest of tile kt+1, unless the prologue issued it)
-        steps_before_last(st, S == 2 ? (kt >= 1 ? kt + 1 : KT) : kt + S - 1);
-        // Tile kt+1 (read by the last step) must be complete; the groups
-        // issued after it (deep ring: min(S-2, KT-2-kt)) may still pend.
-        if constexpr (S == 2) wait_vmcnt<0>();
-        else wait_pending(min(S - 2, KT - 2 - kt));
-        barrier_lds();  // tile kt+1 visible; every wave is done reading stage kt
-        // Last step: its fragments are in registers; read step 0 of tile kt+1
-        // meanwhile (two stages: and refill stage kt with tile kt+2).
-        if constexpr (S == 2)
-          kstep(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, IntC<NQ_STAGE / CF::DSPREAD>{}, kt + 2);
-        else
-          kstep(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, IntC<0>{}, KT);
+      // Guarded K tiles: the first one of the two-stage ring (its tile 1 was
+      // issued whole) and every K tile whose loads reach past the last whole
+      // K tile; the rest run without checks.
+      const int kt_whole = (int)(kbytes / CF::ROWB);
+      int kt = 0, st = 0;
+      auto next = [](int x) { return x + 1 == S ? 0 : x + 1; };
+      auto prev = [](int x) { return x == 0 ? S - 1 : x - 1; };
+      if constexpr (S == 2) {
+        k_tile(IntC<1>{}, 0, 0, 1, 1, KT);
+        kt = 1;
+        st = 1;
+      }
+      for (; kt + S < kt_whole; ++kt) {
+        k_tile(IntC<0>{}, kt, st, next(st), prev(st), kt + S - 1);
+        st = next(st);
+      }
+      for (; kt < KT; ++kt) {
+        k_tile(IntC<1>{}, kt, st, next(st), prev(st), kt + S - 1);
+        st = next(st);
       }
       wait_vmcnt<0>();
     } else {
@@ -928,7 +1173,16 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     barrier_lds();  // every wave is done reading the ring
 
     // ---- fused epilogue ---------------------------------------------------
-    epilogue<CF>(p, acc, lds, wave, lane, l, m0 + wm * CF::WM, n0 + wn * CF::WN);
+    const int emw = m0 + wm * CF::WM, enw = n0 + wn * CF::WN;
+    if constexpr (CF::AB == T_I8) {
+      if (p.epi_kind == T_I32) epilogue_typed<CF, T_I32>(p, acc, lds, wave, lane, l, emw, enw);
+      else epilogue<CF>(p, acc, lds, wave, lane, l, emw, enw);
+    } else {
+      if (p.epi_kind == T_F16) epilogue_typed<CF, T_F16>(p, acc, lds, wave, lane, l, emw, enw);
+      else if (p.epi_kind == T_BF16) epilogue_typed<CF, T_BF16>(p, acc, lds, wave, lane, l, emw, enw);
+      else if (p.epi_kind == T_F32) epilogue_typed<CF, T_F32>(p, acc, lds, wave, lane, l, emw, enw);
+      else epilogue<CF>(p, acc, lds, wave, lane, l, emw, enw);
+    }
     barrier_lds();  // LDS is reused by the next tile's prologue
   }
 }

@@ -121,6 +121,24 @@ def test_every_variant_runs():
         assert plan["name"] == name
 
 
+def test_ring_depth_k_extents():
+    """Each multi-stage variant at K extents with fewer, as many and more K
+    tiles than ring stages, and a ragged K tail (the prologue, the counted
+    waits and the refill of a stage in the step after its barrier)."""
+    import beta_epilogue_amd as ge
+    names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
+    for i, name in enumerate(names):
+        parts = name.split("_")
+        if not name.startswith("f16_kk") or not any(q.startswith("s") and q[1:].isdigit()
+                                                   and int(q[1:]) >= 3 for q in parts):
+            continue
+        for K in (8, 40, 72, 136, 168, 200, 520):
+            p = CFG[2].replace(name="ring_%s_K%d" % (name, K), M=264, N=272, K=K, L=1)
+            _say("variant", i, name, "K", K)
+            (ed, ey), plan = parity_full(p, variant=i)
+            assert plan["name"] == name
+
+
 def test_run_rejects_misaligned_pointer():
     import beta_epilogue_amd as ge
     p = CFG[2].replace(M=64, N=64, K=64)
