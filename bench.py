@@ -35,7 +35,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
     for rel in ("beta_epilogue_amd/csrc/gemm_epi_kernel.hpp",
-                "beta_epilogue_amd/csrc/gemm_epi.hip"):
+                "beta_epilogue_amd/csrc/gemm_epi.hip",
+                "beta_epilogue_amd/csrc/gemm_epi_part.hip",
+                "beta_epilogue_amd/csrc/gemm_epi_launch.hpp",
+                "beta_epilogue_amd/csrc/gemm_epi_variants.inc"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -90,6 +93,33 @@ def cpu_baseline(p, ins, target_s: float):
                       "plus the epilogue each), %.1f s" % (rows, rows * p.N, p.K, dt)}
 
 
+def mfma_ceiling(iters: int = 80000, rounds: int = 3, kinds=("constant", "random")):
+    """Steady clock and rate of v_mfma_f32_32x32x16_f16 with no memory traffic,
+    constant vs uniformly random fp16 operands, alternated `rounds` times."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "beta_epilogue_amd", "libmfma_ceiling.so"))
+    fn = lib.mfma_ceiling_run
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
+                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    fn.restype = ctypes.c_int
+    runs = {k: [] for k in kinds}
+    for _ in range(rounds):
+        for kind, rnd in (("constant", 0), ("random", 1)):
+            if kind not in runs:
+                continue
+            ms, ghz, tf = ctypes.c_float(), ctypes.c_double(), ctypes.c_double()
+            rc = fn(rnd, iters, 3, ctypes.byref(ms), ctypes.byref(ghz), ctypes.byref(tf))
+            if rc != 0:
+                raise RuntimeError("mfma_ceiling_run failed with HIP error %d" % rc)
+            runs[kind].append({"ms": round(ms.value, 3), "ghz": round(ghz.value, 3),
+                               "tflops": round(tf.value, 1)})
+    out = {"metric": "register-only v_mfma_f32_32x32x16_f16 stream, 8 waves per CU", "unit": "TFLOP/s"}
+    for kind, r in runs.items():
+        out[kind] = {"tflops": round(sum(x["tflops"] for x in r) / len(r), 1),
+                     "ghz": round(sum(x["ghz"] for x in r) / len(r), 3), "runs": r}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +130,11 @@ def main():
     ap.add_argument("--variant", type=int, default=-1)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only measure a register-only fp16 MFMA stream on every CU with "
+                         "constant and with random operands (steady clock and TFLOP/s)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the MFMA-ceiling measurement of the default run")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes "
                          "--steps times (scales the HBM byte counters)")
@@ -116,6 +151,10 @@ def main():
     import torch
     import synth
     import beta_epilogue_amd as ge
+
+    if args.mfma_ceiling:
+        print(json.dumps(mfma_ceiling()), flush=True)
+        return
 
     if args.copy_calibration:
         src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda")
@@ -173,6 +212,16 @@ def main():
                                          min(launch_ms), max(launch_ms), wall,
                                          plan["name"]), file=sys.stderr, flush=True)
 
+    # The attainable MFMA rate on this machine for fp16 data like the workload's
+    # (random operands; the power cap sets the clock), measured right after.
+    attainable = None
+    if p.ab == "f16" and not args.no_ceiling:
+        c = mfma_ceiling(rounds=2, kinds=("random",))["random"]
+        attainable = {"tflops": c["tflops"], "ghz": c["ghz"],
+                      "frac": round(achieved / c["tflops"], 4),
+                      "how": "register-only v_mfma_f32_32x32x16_f16 stream on every CU, "
+                             "uniformly random fp16 operands, same run (bench.py --mfma-ceiling)"}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(p, ins, args.cpu_seconds)
@@ -199,7 +248,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(p.name),
                      "algorithmic_bytes": p.algorithmic_bytes(),
-                     "kernel": plan["name"], "avg_launch_ms": round(avg_launch_ms, 5)},
+                     "kernel": plan["name"], "avg_launch_ms": round(avg_launch_ms, 5),
+                     "attainable_random_operands": attainable},
         "cpu_baseline": cpu,
         "plan": plan,
     }

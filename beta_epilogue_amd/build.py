@@ -1,45 +1,82 @@
-"""Build step for the HIP library: one hipcc line, gfx950 only, in-tree."""
+"""Build step for the HIP libraries: hipcc, gfx950 only, in-tree.
+
+libgemm_epi.so is linked from gemm_epi.hip (C ABI, variant table) and
+GEMM_EPI_PARTS objects of gemm_epi_part.hip, each compiling the kernel
+variants of gemm_epi_variants.inc assigned to it; the parts compile in
+parallel.  libmfma_ceiling.so is a measurement tool for bench.py.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgemm_epi.so")
-SOURCES = [os.path.join(HERE, "csrc", "gemm_epi.hip")]
-HEADERS = [os.path.join(HERE, "csrc", "gemm_epi_kernel.hpp"),
-           os.path.join(ROOT, "include", "gemm_epi.h")]
+MAIN_SOURCE = os.path.join(CSRC, "gemm_epi.hip")
+PART_SOURCE = os.path.join(CSRC, "gemm_epi_part.hip")
+GEMM_EPI_PARTS = 8
+SOURCES = [MAIN_SOURCE, PART_SOURCE]
+HEADERS = [os.path.join(CSRC, "gemm_epi_kernel.hpp"), os.path.join(CSRC, "gemm_epi_launch.hpp"),
+           os.path.join(CSRC, "gemm_epi_variants.inc"), os.path.join(ROOT, "include", "gemm_epi.h")]
+# measurement tool used by bench.py --mfma-ceiling (not part of the GEMM path)
+CEILING_LIB = os.path.join(HERE, "libmfma_ceiling.so")
+CEILING_SOURCE = os.path.join(CSRC, "mfma_ceiling.hip")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep packed-fp32 instructions out of generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-pass-failed", "-Wno-inline-asm",
 ]
+INCLUDES = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def hipcc_command(out: str, extra=()):
-    return (["hipcc"] + HIPCC_FLAGS + list(extra) +
-            ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-             "-o", out] + SOURCES)
-
-
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile libgemm_epi.so next to this file (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = hipcc_command(tmp, extra)
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(ln for ln in r.stderr.splitlines()
                     if "packed-fp32-ops" not in ln and ln.strip())
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
+        raise RuntimeError("hipcc failed: %s\n%s" % (" ".join(cmd), err))
     if verbose and err:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+
+
+def _jobs() -> int:
+    n = os.cpu_count() or 1
+    env = os.environ.get("MAX_JOBS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, min(n, 16))
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile libgemm_epi.so and libmfma_ceiling.so next to this file
+    (always recompiles)."""
+    extra = list(extra)
+    with tempfile.TemporaryDirectory(prefix="gemm_epi_build_") as tmp:
+        jobs = [(["hipcc"] + HIPCC_FLAGS + extra + INCLUDES +
+                 ["-c", "-DGEMM_EPI_PART=%d" % k, "-o", os.path.join(tmp, "part%d.o" % k), PART_SOURCE])
+                for k in range(GEMM_EPI_PARTS)]
+        jobs.append(["hipcc"] + HIPCC_FLAGS + extra + INCLUDES +
+                    ["-c", "-o", os.path.join(tmp, "main.o"), MAIN_SOURCE])
+        ceil_tmp = CEILING_LIB + ".tmp%d" % os.getpid()
+        jobs.append(["hipcc"] + HIPCC_FLAGS + INCLUDES + ["-shared", "-o", ceil_tmp, CEILING_SOURCE])
+        with ThreadPoolExecutor(max_workers=_jobs()) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in jobs]:
+                f.result()
+        lib_tmp = LIB + ".tmp%d" % os.getpid()
+        objs = [os.path.join(tmp, "main.o")] + [os.path.join(tmp, "part%d.o" % k)
+                                                for k in range(GEMM_EPI_PARTS)]
+        _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib_tmp] + objs, verbose)
+        os.replace(ceil_tmp, CEILING_LIB)
+        os.replace(lib_tmp, LIB)
     return LIB
 
 

@@ -18,6 +18,7 @@
 
 #include "gemm_epi.h"
 #include "gemm_epi_kernel.hpp"
+#include "gemm_epi_launch.hpp"
 
 namespace {
 
@@ -45,10 +46,6 @@ struct Variant {
   launch_fn launch;
 };
 
-template <class CF>
-void launch(const Params& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_epi::gemm_epi_kernel<CF>, dim3(grid), dim3(CF::THREADS), 0, s, p);
-}
 
 template <class CF>
 constexpr Variant make_variant(const char* name) {
@@ -62,48 +59,18 @@ constexpr Variant make_variant(const char* name) {
                  CF::BK,
                  CF::THREADS,
                  CF::LDS_BYTES,
-                 &launch<CF>};
+                 &gemm_epi::launch<CF>};
 }
 
 using namespace gemm_epi;
-// Cfg<ab, A K-major, B K-major, C/D N-major, BM, BN, ROWB, waves M, waves N, stages>
-// The first variant that fits a problem is its default.
-#define V(AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, NAME) \
-  make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S>>(NAME)
-#define VD(AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, DS, NAME) \
-  make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, 0, DS>>(NAME)
-#define VR(AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, NAME) \
-  make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, 1>>(NAME)
+// Variant table (gemm_epi_variants.inc); the kernels are compiled in the
+// gemm_epi_part.hip translation units, this one only refers to them.
+#define X(PART, AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, LD, DS, NAME) \
+  make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, LD, DS>>(NAME),
 const Variant kVariants[] = {
-    // f16, K-major A/B: default first
-    V(T_F16, true, true, true, 256, 256, 128, 2, 4, 2, "f16_kk_n_256x256_r128_w8_s2"),
-    V(T_F16, true, true, false, 256, 256, 128, 2, 4, 2, "f16_kk_m_256x256_r128_w8_s2"),
-    V(T_F16, true, true, true, 256, 256, 128, 2, 2, 2, "f16_kk_n_256x256_r128_w4_s2"),
-    V(T_F16, true, true, true, 256, 256, 64, 2, 4, 4, "f16_kk_n_256x256_r64_w8_s4"),
-    V(T_F16, true, true, true, 256, 256, 64, 2, 2, 4, "f16_kk_n_256x256_r64_w4_s4"),
-    V(T_F16, true, true, true, 256, 128, 128, 2, 2, 3, "f16_kk_n_256x128_r128_w4_s3"),
-    VR(T_F16, true, true, true, 256, 256, 64, 2, 4, 2, "f16_kk_n_256x256_r64_w8_s2_reg"),
-    VD(T_F16, true, true, true, 256, 256, 128, 2, 2, 2, 2, "f16_kk_n_256x256_r128_w4_s2_d2"),
-    VD(T_F16, true, true, true, 256, 256, 128, 2, 2, 2, 4, "f16_kk_n_256x256_r128_w4_s2_d4"),
-    VD(T_F16, true, true, true, 256, 256, 128, 2, 4, 2, 2, "f16_kk_n_256x256_r128_w8_s2_d2"),
-    V(T_F16, true, true, true, 256, 256, 64, 2, 4, 5, "f16_kk_n_256x256_r64_w8_s5"),
-    V(T_F16, true, true, true, 256, 256, 64, 2, 2, 5, "f16_kk_n_256x256_r64_w4_s5"),
-    V(T_F16, true, true, true, 256, 256, 64, 2, 4, 3, "f16_kk_n_256x256_r64_w8_s3"),
-    // bf16
-    V(T_BF16, true, true, true, 256, 256, 128, 2, 4, 2, "bf16_kk_n_256x256_r128_w8_s2"),
-    V(T_BF16, true, true, false, 256, 256, 128, 2, 4, 2, "bf16_kk_m_256x256_r128_w8_s2"),
-    V(T_BF16, true, true, true, 256, 128, 128, 2, 2, 3, "bf16_kk_n_256x128_r128_w4_s3"),
-    // fp8 e4m3
-    V(T_E4M3, true, true, true, 256, 256, 128, 2, 4, 2, "e4m3_kk_n_256x256_r128_w8_s2"),
-    V(T_E4M3, true, true, false, 256, 256, 128, 2, 4, 2, "e4m3_kk_m_256x256_r128_w8_s2"),
-    V(T_E4M3, true, true, true, 256, 256, 128, 2, 2, 2, "e4m3_kk_n_256x256_r128_w4_s2"),
-    // int8
-    V(T_I8, true, true, true, 256, 256, 128, 2, 4, 2, "i8_kk_n_256x256_r128_w8_s2"),
-    V(T_I8, true, true, false, 256, 256, 128, 2, 4, 2, "i8_kk_m_256x256_r128_w8_s2"),
-    V(T_I8, false, true, true, 256, 256, 64, 2, 2, 2, "i8_mk_n_256x256_r64_w4_s2"),
-    V(T_I8, false, true, false, 256, 256, 64, 2, 2, 2, "i8_mk_m_256x256_r64_w4_s2"),
-    V(T_I8, false, true, true, 256, 256, 128, 2, 4, 2, "i8_mk_n_256x256_r128_w8_s2"),
+#include "gemm_epi_variants.inc"
 };
+#undef X
 #undef V
 #undef VR
 #undef VD

@@ -1069,10 +1069,10 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       // ops of a tile's first step: write tile kt+1 (register stage WBUF) to
       // LDS stage WST, then load tile kt+2 into register stage LBUF
       auto first_step_ops = [&](auto wbuf_c, int wst, auto lbuf_c, int ltile, bool lload) {
-        constexpr int WB = decltype(wbuf_c)::value, LB = decltype(lbuf_c)::value;
         const int woff = wst * CF::STAGE_BYTES;
         const int64_t kv = kbytes - (int64_t)ltile * CF::ROWB;
-        return [&, woff, kv, lload, ltile](auto k_c) {
+        return [&ra_, &rb_, woff, kv, lload, ltile, wbuf_c, lbuf_c](auto k_c) {
+          constexpr int WB = decltype(wbuf_c)::value, LB = decltype(lbuf_c)::value;
           constexpr int K2 = decltype(k_c)::value;
           if constexpr (K2 < QA) ra_.template store<WB, K2>(lds, woff);
           else if constexpr (K2 < QA + QB) rb_.template store<WB, K2 - QA>(lds, woff + BM * CF::ROWB);

@@ -1,0 +1,60 @@
+// gemm_epi_part.hip -- compiles the kernel variants of gemm_epi_variants.inc
+// whose `part` equals GEMM_EPI_PART (the build compiles this file once per
+// part, in parallel, and links the objects with gemm_epi.hip).
+#include "gemm_epi_launch.hpp"
+
+#ifndef GEMM_EPI_PART
+#error "GEMM_EPI_PART must be defined (0 .. 7)"
+#endif
+
+namespace gemm_epi {
+
+template <class CF>
+void launch(const Params& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_epi_kernel<CF>, dim3(grid), dim3(CF::THREADS), 0, s, p);
+}
+
+#define GEMM_EPI_INSTANTIATE(...) template void launch<Cfg<__VA_ARGS__>>(const Params&, int, hipStream_t);
+#define GEMM_EPI_SKIP(...)
+#define GEMM_EPI_PICK_0 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_1 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_2 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_3 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_4 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_5 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_6 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_7 GEMM_EPI_SKIP
+#if GEMM_EPI_PART == 0
+#undef GEMM_EPI_PICK_0
+#define GEMM_EPI_PICK_0 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 1
+#undef GEMM_EPI_PICK_1
+#define GEMM_EPI_PICK_1 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 2
+#undef GEMM_EPI_PICK_2
+#define GEMM_EPI_PICK_2 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 3
+#undef GEMM_EPI_PICK_3
+#define GEMM_EPI_PICK_3 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 4
+#undef GEMM_EPI_PICK_4
+#define GEMM_EPI_PICK_4 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 5
+#undef GEMM_EPI_PICK_5
+#define GEMM_EPI_PICK_5 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 6
+#undef GEMM_EPI_PICK_6
+#define GEMM_EPI_PICK_6 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 7
+#undef GEMM_EPI_PICK_7
+#define GEMM_EPI_PICK_7 GEMM_EPI_INSTANTIATE
+#else
+#error "GEMM_EPI_PART out of range"
+#endif
+#define GEMM_EPI_CAT(a, b) a##b
+#define X(PART, AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, LD, DS, NAME) \
+  GEMM_EPI_CAT(GEMM_EPI_PICK_, PART)(AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, LD, DS)
+#include "gemm_epi_variants.inc"
+#undef X
+
+}  // namespace gemm_epi

@@ -27,6 +27,18 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), "missing export " + n
 
 
+def test_measurement_library_exports_its_declared_symbol():
+    """libmfma_ceiling.so (bench.py --mfma-ceiling) exports what
+    include/mfma_ceiling.h declares."""
+    text = open(os.path.join(ROOT, "include", "mfma_ceiling.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(mfma_ceiling_\w+)\s*\(", text)))
+    assert names == ["mfma_ceiling_run"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "beta_epilogue_amd", "libmfma_ceiling.so"))
+    for n in names:
+        assert hasattr(lib, n), "missing export " + n
+
+
 def test_status_strings():
     assert ge.status_string(0) == "success"
     for c in range(1, 6):
