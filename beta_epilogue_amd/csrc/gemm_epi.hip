@@ -65,8 +65,8 @@ constexpr Variant make_variant(const char* name) {
 using namespace gemm_epi;
 // Variant table (gemm_epi_variants.inc); the kernels are compiled in the
 // gemm_epi_part.hip translation units, this one only refers to them.
-#define X(PART, AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, LD, DS, NAME) \
-  make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, LD, DS>>(NAME),
+#define X(PART, AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, LD, DS, BL, NAME) \
+  make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, LD, DS, BL>>(NAME),
 const Variant kVariants[] = {
 #include "gemm_epi_variants.inc"
 };

@@ -70,14 +70,27 @@ struct Params {
 };
 
 // ---------------------------------------------------------------------------
-// MFMA traits per A/B element type.  KSB = bytes of K one MFMA consumes per
-// row; each lane holds half of them (lanes 32..63 take the upper half).  A
-// and B fragments use the same lane -> k assignment, so the contraction is
-// exact whatever order the matrix core walks k in.
+// MFMA traits per A/B element type and block size BLK (32: 32x32 output
+// blocks, 16: 16x16).  KSB = bytes of K one MFMA consumes per row.  Lane l
+// holds row (column) l % BLK of the A (B) block and the (l / BLK)-th equal
+// share of those KSB bytes; A and B fragments use the same lane -> k
+// assignment, so the contraction is exact whatever order the matrix core
+// walks k in.  Accumulator register v of lane l holds output row acc_row(l,
+// v) of the block and column l % BLK; registers 4g .. 4g+3 are four
+// consecutive rows.
 // ---------------------------------------------------------------------------
-template <int AB> struct Mma;
+struct MmaLayout32 {
+  static constexpr int BLK = 32, ACCN = 16;
+  static __device__ __forceinline__ int acc_row(int lane, int v) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+};
+struct MmaLayout16 {
+  static constexpr int BLK = 16, ACCN = 4;
+  static __device__ __forceinline__ int acc_row(int lane, int v) { return 4 * (lane >> 4) + v; }
+};
 
-template <> struct Mma<T_F16> {
+template <int AB, int BLK> struct Mma;
+
+template <> struct Mma<T_F16, 32> : MmaLayout32 {
   typedef v16f acc_t;
   typedef v4i frag_t;
   static constexpr int ESIZE = 2, KSB = 32;
@@ -86,7 +99,16 @@ template <> struct Mma<T_F16> {
                                                   __builtin_bit_cast(v8h, b), c, 0, 0, 0);
   }
 };
-template <> struct Mma<T_BF16> {
+template <> struct Mma<T_F16, 16> : MmaLayout16 {
+  typedef v4f acc_t;
+  typedef v4i frag_t;
+  static constexpr int ESIZE = 2, KSB = 64;
+  static __device__ __forceinline__ acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
+                                                  __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mma<T_BF16, 32> : MmaLayout32 {
   typedef v16f acc_t;
   typedef v4i frag_t;
   static constexpr int ESIZE = 2, KSB = 32;
@@ -95,7 +117,16 @@ template <> struct Mma<T_BF16> {
                                                    __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
   }
 };
-template <> struct Mma<T_I8> {
+template <> struct Mma<T_BF16, 16> : MmaLayout16 {
+  typedef v4f acc_t;
+  typedef v4i frag_t;
+  static constexpr int ESIZE = 2, KSB = 64;
+  static __device__ __forceinline__ acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                   __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mma<T_I8, 32> : MmaLayout32 {
   typedef v16i acc_t;
   typedef v4i frag_t;
   static constexpr int ESIZE = 1, KSB = 32;
@@ -103,14 +134,30 @@ template <> struct Mma<T_I8> {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
   }
 };
-template <> struct Mma<T_E4M3> {
+template <> struct Mma<T_I8, 16> : MmaLayout16 {
+  typedef v4i acc_t;
+  typedef v4i frag_t;
+  static constexpr int ESIZE = 1, KSB = 64;
+  static __device__ __forceinline__ acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+  }
+};
+// Format selectors 0/0 = fp8 e4m3 for both operands; zero scale operands
+// select the unscaled instruction.
+template <> struct Mma<T_E4M3, 32> : MmaLayout32 {
   typedef v16f acc_t;
   typedef v8i frag_t;
   static constexpr int ESIZE = 1, KSB = 64;
-  // Format selectors 0/0 = fp8 e4m3 for both operands; zero scale operands
-  // select the unscaled instruction.
   static __device__ __forceinline__ acc_t mma(frag_t a, frag_t b, acc_t c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+template <> struct Mma<T_E4M3, 16> : MmaLayout16 {
+  typedef v4f acc_t;
+  typedef v8i frag_t;
+  static constexpr int ESIZE = 1, KSB = 128;
+  static __device__ __forceinline__ acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
   }
 };
 
@@ -120,14 +167,17 @@ template <> struct Mma<T_E4M3> {
 //   WAVES_M/N   wave grid; each wave owns (BM/WAVES_M) x (BN/WAVES_N)
 //   STAGES      depth of the LDS ring
 //   LOADER      how K-major tiles reach LDS (see below)
-//   DSPREAD     k steps the two-stage ring spreads one K tile's DMA over
+//   DQ          two-stage ring: quarters of a K tile's DMA issued early in
+//               step 0 of the K tile before its use (see the mainloop)
+//   BLK         MFMA output block: 32 (32x32) or 16 (16x16)
 template <int AB_, bool A_KMAJOR_, bool B_KMAJOR_, bool CD_NMAJOR_, int BM_ = 256, int BN_ = 256,
           int ROWB_ = 128, int WAVES_M_ = 2, int WAVES_N_ = 2, int STAGES_ = 2, int LOADER_ = 0,
-          int DSPREAD_ = 1>
+          int DQ_ = 0, int BLK_ = 32>
 struct Cfg {
-  // Two-stage DMA ring: the loads of K tile kt+2 are spread over DSPREAD
-  // k steps, starting with the last step of tile kt.
-  static constexpr int DSPREAD = DSPREAD_;
+  static constexpr int BLK = BLK_;
+  using MM = Mma<AB_, BLK_>;
+  static constexpr int DQ = DQ_;
+  static_assert(DQ >= 0 && DQ <= 4 && (STAGES_ == 2 || DQ == 0), "DQ: quarters, two-stage rings only");
   // LOADER 0: K-major tiles go global -> LDS by buffer_load ... lds (DMA).
   // LOADER 1: global -> VGPR by buffer_load_dwordx4, then ds_write_b128
   //           (two register stages in flight; LDS writes use the LDS's own
@@ -139,30 +189,37 @@ struct Cfg {
   static constexpr int CH = ROWB / 16;                  // 16-byte chunks per LDS row
   static constexpr int ROWS_PER_DMA = 1024 / ROWB;       // rows one wave DMA writes
   static constexpr int SWZ_SHIFT = CH == 8 ? 1 : 2;      // 16 rows -> 16 bank groups
-  static constexpr int BK = ROWB / Mma<AB>::ESIZE;       // K elements per stage
+  static constexpr int BK = ROWB / MM::ESIZE;            // K elements per stage
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int THREADS = NW * 64;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile
-  static constexpr int FM = WM / 32, FN = WN / 32;           // 32x32 blocks
+  static constexpr int FM = WM / BLK, FN = WN / BLK;         // MFMA output blocks
+  // 16-byte chunks of one k step per lane (lane group l / BLK reads chunks
+  // [q*CPL, q*CPL + CPL) of the step)
+  static constexpr int CPL = (MM::KSB / 16) / (64 / BLK);
   static constexpr int STAGES = STAGES_;
   static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
   static constexpr int PIPE_BYTES = STAGES * STAGE_BYTES;
   // epilogue: per wave, 32 lines of the block being re-laid out
   static constexpr int EPI_LINE = CD_NMAJOR ? WN : WM;
-  static constexpr int EPI_PITCH = EPI_LINE + (CD_NMAJOR ? 8 : 4);  // words
+  // words; N-major: the lane groups of one accumulator write (rows 4 apart)
+  // land on disjoint banks
+  static constexpr int EPI_PITCH = EPI_LINE + (CD_NMAJOR && BLK == 32 ? 8 : 4);
   static constexpr int EPI_WAVE_BYTES = 32 * EPI_PITCH * 4;
   static constexpr int EPI_BYTES = NW * EPI_WAVE_BYTES;
   static constexpr int LDS_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
-  static constexpr int KSTEPS = ROWB / Mma<AB>::KSB;
+  static constexpr int KSTEPS = ROWB / MM::KSB;
   static_assert(KSTEPS >= 1, "a stage must hold at least one MFMA k step");
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(CPL >= 1 && CPL * 16 * (64 / BLK) == MM::KSB, "k step must split evenly over lane groups");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32-line epilogue blocks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
 };
 
 template <int V>
 struct IntC {
   static constexpr int value = V;
+  constexpr operator int() const { return V; }
 };
 
 // Calls f(IntC<I>{}) for I = B .. E-1, in order, at compile time.
@@ -420,21 +477,65 @@ struct MMajorStager8 {
   }
 };
 
-// Fragment read: this lane's half of k step s of LDS row `row`.
+// Fragment read: lane group q's share (CPL chunks) of k step s of LDS row
+// row0 + blk*BLK.  Rows BLK apart share their chunk swizzle (a block spans
+// whole swizzle periods), so the swizzle is taken from row0 and block blk is
+// an immediate offset from block 0's address.
 template <class CF>
-__device__ __forceinline__ typename Mma<CF::AB>::frag_t read_frag(const char* lds, int tile_off,
-                                                                  int row, int s, int half) {
-  constexpr int KSB = Mma<CF::AB>::KSB;
-  const char* rp = lds + tile_off + row * CF::ROWB;
-  const int sw = swz<CF>(row);
-  if constexpr (KSB == 32) {
-    const int c = s * 2 + half;
+__device__ __forceinline__ typename CF::MM::frag_t read_frag(const char* lds, int tile_off, int row0, int blk,
+                                                             int s, int q) {
+  static_assert(CF::BLK % (CF::CH << CF::SWZ_SHIFT) == 0, "block rows span whole swizzle periods");
+  const char* rp = lds + tile_off + row0 * CF::ROWB + blk * (CF::BLK * CF::ROWB);
+  const int sw = swz<CF>(row0);
+  const int c = s * (CF::MM::KSB / 16) + q * CF::CPL;
+  if constexpr (CF::CPL == 1) {
     return *(const v4i*)(rp + ((c ^ sw) << 4));
   } else {
-    const int c = s * 4 + half * 2;
+    static_assert(CF::CPL == 2, "one or two chunks per lane");
     const v4i lo = *(const v4i*)(rp + ((c ^ sw) << 4));
     const v4i hi = *(const v4i*)(rp + (((c + 1) ^ sw) << 4));
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+// Accumulator element as the 32-bit pattern stored in LDS.  (The element is
+// read into a scalar first: bit-casting a vector-element lvalue directly
+// reads element 0 with this compiler.)
+__device__ __forceinline__ float acc_bits(float v) { return v; }
+__device__ __forceinline__ float acc_bits(int v) { return __int_as_float(v); }
+
+// Writes 32-line block `blk` of this wave's accumulator tile into its LDS
+// region (fp32 or int32 bit patterns): for N-major outputs rows blk*32 ..
+// blk*32+31 of the wave tile (line = row, WN columns), for M-major columns
+// (line = column, WM rows).
+template <class CF, class ACC>
+__device__ __forceinline__ void epi_stage_block(const ACC (&acc)[CF::FM][CF::FN], float* region, int lane,
+                                                int blk) {
+  using MM = typename CF::MM;
+  constexpr int BLK = CF::BLK, PITCH = CF::EPI_PITCH, SUB = 32 / BLK;
+  const int lc = lane % BLK;
+  if constexpr (CF::CD_NMAJOR) {
+#pragma unroll
+    for (int b = 0; b < SUB; ++b)
+#pragma unroll
+      for (int j = 0; j < CF::FN; ++j)
+#pragma unroll
+        for (int v = 0; v < MM::ACCN; ++v) {
+          const auto x = acc[blk * SUB + b][j][v];
+          region[(b * BLK + MM::acc_row(lane, v)) * PITCH + j * BLK + lc] = acc_bits(x);
+        }
+  } else {
+#pragma unroll
+    for (int b = 0; b < SUB; ++b)
+#pragma unroll
+      for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+        for (int g = 0; g < MM::ACCN / 4; ++g) {
+          const auto e0 = acc[i][blk * SUB + b][4 * g + 0], e1 = acc[i][blk * SUB + b][4 * g + 1];
+          const auto e2 = acc[i][blk * SUB + b][4 * g + 2], e3 = acc[i][blk * SUB + b][4 * g + 3];
+          *(v4f*)(region + (b * BLK + lc) * PITCH + i * BLK + MM::acc_row(lane, 4 * g)) =
+              v4f{acc_bits(e0), acc_bits(e1), acc_bits(e2), acc_bits(e3)};
+        }
   }
 }
 
@@ -454,12 +555,6 @@ __device__ __forceinline__ void store4_f(void* p, int dt, int64_t i, v4f v) {
     __builtin_nontemporal_store(v, (v4f*)((float*)p + i));
   }
 }
-
-// Accumulator element as the 32-bit pattern stored in LDS.  (The element is
-// read into a scalar first: bit-casting a vector-element lvalue directly
-// reads element 0 with this compiler.)
-__device__ __forceinline__ float acc_bits(float v) { return v; }
-__device__ __forceinline__ float acc_bits(int v) { return __int_as_float(v); }
 
 // Element work for four contiguous outputs at flat index o, given the four
 // accumulator values w and the four C and X values already loaded.
@@ -532,9 +627,8 @@ __device__ __forceinline__ void epilogue(const Params& p, const ACC (&acc)[CF::F
   constexpr int LPL = LINE / 4;        // lanes per line
   constexpr int LINES_PER_PASS = 64 / LPL;
   float* region = (float*)(lds + wave * CF::EPI_WAVE_BYTES);
-  const int half = lane >> 5, l32 = lane & 31;
   const int64_t obase = (int64_t)l * p.M * p.N;
-  constexpr int NBLK = NMAJ ? CF::FM : CF::FN;
+  constexpr int NBLK = (NMAJ ? CF::WM : CF::WN) / 32;
   constexpr int PASSES = 32 / LINES_PER_PASS;
   constexpr int CMAX = CF::NW > 4 ? 4 : 8;  // two waves per SIMD: half the registers
   constexpr int CHUNK = PASSES < CMAX ? PASSES : CMAX;
@@ -543,31 +637,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const ACC (&acc)[CF::F
   const int sub = lane / LPL;
   const int e = (lane % LPL) * 4;
 
-  auto write_block = [&](auto blk_c) {
-    constexpr int blk = decltype(blk_c)::value;
-    if constexpr (NMAJ) {
-      // block row blk: lane holds rows 8*(v/4) + 4*half + v%4, column j*32 + l32
-      float* wp = region + (half * 4) * PITCH + l32;
-#pragma unroll
-      for (int j = 0; j < CF::FN; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const auto x = acc[blk][j][v];
-          wp[((v >> 2) * 8 + (v & 3)) * PITCH + j * 32] = acc_bits(x);
-        }
-    } else {
-      // block column blk: lane holds column l32, rows i*32 + 8*v4 + 4*half + 0..3
-      float* wp = region + l32 * PITCH + half * 4;
-#pragma unroll
-      for (int i = 0; i < CF::FM; ++i)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const auto e0 = acc[i][blk][v4 * 4 + 0], e1 = acc[i][blk][v4 * 4 + 1];
-          const auto e2 = acc[i][blk][v4 * 4 + 2], e3 = acc[i][blk][v4 * 4 + 3];
-          *(v4f*)(wp + i * 32 + v4 * 8) = v4f{acc_bits(e0), acc_bits(e1), acc_bits(e2), acc_bits(e3)};
-        }
-    }
-  };
+  auto write_block = [&](auto blk_c) { epi_stage_block<CF>(acc, region, lane, decltype(blk_c)::value); };
   // Output coordinates of pass `ps` of block `blk` for this lane.
   auto coords = [&](int blk, int ps, int64_t& o) -> bool {
     const int line = ps * LINES_PER_PASS + sub;
@@ -695,8 +765,7 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
   constexpr int LINES_PER_PASS = 64 / LPL;
   constexpr int ES = EpiElem<T>::SIZE;
   float* region = (float*)(lds + wave * CF::EPI_WAVE_BYTES);
-  const int half = lane >> 5, l32 = lane & 31;
-  constexpr int NBLK = NMAJ ? CF::FM : CF::FN;
+  constexpr int NBLK = (NMAJ ? CF::WM : CF::WN) / 32;
   constexpr int PASSES = 32 / LINES_PER_PASS;
   constexpr int NP = NBLK * PASSES;
   constexpr int DIST0 = ES == 2 ? 8 : 4;  // 32 VGPRs of C and X in flight
@@ -731,29 +800,7 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
     return lane_off + (uint32_t)(line * ld * ES);
   };
 
-  auto write_block = [&](auto blk_c) {
-    constexpr int blk = decltype(blk_c)::value;
-    if constexpr (NMAJ) {
-      float* wp = region + (half * 4) * PITCH + l32;
-#pragma unroll
-      for (int j = 0; j < CF::FN; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const auto x = acc[blk][j][v];
-          wp[((v >> 2) * 8 + (v & 3)) * PITCH + j * 32] = acc_bits(x);
-        }
-    } else {
-      float* wp = region + l32 * PITCH + half * 4;
-#pragma unroll
-      for (int i = 0; i < CF::FM; ++i)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const auto e0 = acc[i][blk][v4 * 4 + 0], e1 = acc[i][blk][v4 * 4 + 1];
-          const auto e2 = acc[i][blk][v4 * 4 + 2], e3 = acc[i][blk][v4 * 4 + 3];
-          *(v4f*)(wp + i * 32 + v4 * 8) = v4f{acc_bits(e0), acc_bits(e1), acc_bits(e2), acc_bits(e3)};
-        }
-    }
-  };
+  auto write_block = [&](auto blk_c) { epi_stage_block<CF>(acc, region, lane, decltype(blk_c)::value); };
 
   v4u cr[DIST + 1], xr[DIST + 1];
   static_for<0, DIST>([&](auto i_c) {
@@ -816,7 +863,7 @@ struct InterleaveHint {
 // ---------------------------------------------------------------------------
 template <class CF>
 __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
-  using MM = Mma<CF::AB>;
+  using MM = typename CF::MM;
   using acc_t = typename MM::acc_t;
   using frag_t = typename MM::frag_t;
   constexpr int ES = MM::ESIZE;
@@ -828,7 +875,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % CF::WAVES_M, wn = wave / CF::WAVES_M;
-  const int half = lane >> 5, l32 = lane & 31;
+  const int lq = lane / CF::BLK, lr = lane % CF::BLK;  // k share and row of this lane in a block
+
 
   const int G = gridDim.x;
   const int bid = blockIdx.x;
@@ -894,9 +942,9 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     auto load_step = [&](frag_t (&ra)[CF::FM], frag_t (&rb)[CF::FN], int st, int s) {
       const int a_off = st * CF::STAGE_BYTES, b_off = a_off + BM * CF::ROWB;
 #pragma unroll
-      for (int i = 0; i < CF::FM; ++i) ra[i] = read_frag<CF>(lds, a_off, wm * CF::WM + i * 32 + l32, s, half);
+      for (int i = 0; i < CF::FM; ++i) ra[i] = read_frag<CF>(lds, a_off, wm * CF::WM + lr, i, s, lq);
 #pragma unroll
-      for (int j = 0; j < CF::FN; ++j) rb[j] = read_frag<CF>(lds, b_off, wn * CF::WN + j * 32 + l32, s, half);
+      for (int j = 0; j < CF::FN; ++j) rb[j] = read_frag<CF>(lds, b_off, wn * CF::WN + lr, j, s, lq);
     };
     auto mma_step = [&](const frag_t (&ra)[CF::FM], const frag_t (&rb)[CF::FN]) {
 #pragma unroll
@@ -907,7 +955,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     // Interleave the next step's LDS reads with this step's MFMAs so each
     // read's latency hides under MFMAs already queued.
     auto pipeline_hint = [&]() {
-      constexpr int READS = (CF::FM + CF::FN) * (MM::KSB / 32);
+      constexpr int READS = (CF::FM + CF::FN) * CF::CPL;
       constexpr int MFMAS = CF::FM * CF::FN;
       InterleaveHint<0, READS, MFMAS>::run();
     };
@@ -941,15 +989,16 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     // instructions of a later K tile, so LDS reads, DMA and MFMAs overlap.
     constexpr int NREAD = CF::FM + CF::FN;
     constexpr int MF = CF::FM * CF::FN;
-    auto read_r = [&](auto buf_c, auto r_c, int st, int ks) {
+    auto read_r = [&](auto buf_c, auto r_c, auto st_x, auto ks_x) {
       constexpr int BUF = decltype(buf_c)::value, R = decltype(r_c)::value;
+      const int st = (int)st_x, ks = (int)ks_x;
       const int a_off = st * CF::STAGE_BYTES, b_off = a_off + BM * CF::ROWB;
       if constexpr (R == 0)
-        fa[BUF][0] = read_frag<CF>(lds, a_off, wm * CF::WM + l32, ks, half);
+        fa[BUF][0] = read_frag<CF>(lds, a_off, wm * CF::WM + lr, 0, ks, lq);
       else if constexpr (R <= CF::FN)
-        fb[BUF][R - 1] = read_frag<CF>(lds, b_off, wn * CF::WN + (R - 1) * 32 + l32, ks, half);
+        fb[BUF][R - 1] = read_frag<CF>(lds, b_off, wn * CF::WN + lr, R - 1, ks, lq);
       else
-        fa[BUF][R - CF::FN] = read_frag<CF>(lds, a_off, wm * CF::WM + (R - CF::FN) * 32 + l32, ks, half);
+        fa[BUF][R - CF::FN] = read_frag<CF>(lds, a_off, wm * CF::WM + lr, R - CF::FN, ks, lq);
     };
     // DMA instruction D of K tile k_tile into stage stg.  GUARD: the tile
     // may not exist (k_tile >= KT) or may be cut by the end of K; without
@@ -969,9 +1018,10 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     };
     // One k step on buffer CUR: reads of (stage rst, step rs) into CUR^1 and
     // NOPS memory operations op(IntC<k>) spread evenly over the MFMAs.
-    auto kstep_ops = [&](auto cur_c, int rst, int rs, auto nops_c, auto&& op) {
+    auto kstep_ops = [&](auto cur_c, auto rst, auto rs, auto nops_c, auto&& op, auto win_c) {
       constexpr int CUR = decltype(cur_c)::value;
       constexpr int NOPS = decltype(nops_c)::value;
+      constexpr int WIN = decltype(win_c)::value;  // ops go among the first WIN MFMAs
       static_for<0, MF>([&](auto idx_c) {
         constexpr int IDX = decltype(idx_c)::value;
         constexpr int I = IDX / CF::FN, J = IDX % CF::FN;
@@ -983,19 +1033,20 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
         if constexpr (NOPS > 0) {
           static_for<0, NOPS>([&](auto k_c) {
             constexpr int KK = decltype(k_c)::value;
-            if constexpr (((2 * KK + 1) * MF) / (2 * NOPS) == IDX) op(k_c);
+            if constexpr (((2 * KK + 1) * WIN) / (2 * NOPS) == IDX) op(k_c);
           });
         }
         __builtin_amdgcn_sched_barrier(0);
       });
     };
-    // DMA variant: instructions [D0, D1) of K tile dma_tile into stage dst.
-    auto kstep = [&](auto cur_c, int rst, int rs, auto d0_c, auto d1_c, auto guard_c, int dma_tile,
-                     int dst) {
+    // DMA variant: instructions [D0, D1) of K tile dma_tile into stage dst,
+    // spread over the first WIN MFMAs of the step.
+    auto kstep = [&](auto cur_c, auto rst, auto rs, auto d0_c, auto d1_c, auto guard_c, int dma_tile,
+                     int dst, auto win_c) {
       constexpr int D0 = decltype(d0_c)::value, D1 = decltype(d1_c)::value;
       kstep_ops(cur_c, rst, rs, IntC<D1 - D0>{}, [&](auto k_c) {
         dma_one(IntC<D0 + decltype(k_c)::value>{}, guard_c, dma_tile, dst);
-      });
+      }, win_c);
     };
     // Wait until at most `pend` DMA groups (K tiles) of this wave are in
     // flight (loads complete in order).
@@ -1012,25 +1063,31 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
         wait_vmcnt<0>();
       }
     };
-    // The DMA of one K tile is split into NPARTS equal parts.  Part 0 goes
-    // into the last step of K tile kt-S (right after the barrier that frees
-    // its stage) and part q into step q-1 of K tile kt-S+1.  Deep ring
-    // (S >= 3): NPARTS = KSTEPS, so the texture path (64 B/clk per CU, about
-    // half of what the MFMAs consume at full rate) is fed evenly and a tile
-    // lands S-2 K tiles before it is read.  Two stages: NPARTS = DSPREAD.
-    constexpr int NPARTS = S == 2 ? CF::DSPREAD : CF::KSTEPS;
-    static_assert(NPARTS >= 1 && NPARTS <= CF::KSTEPS, "DMA parts must fit the k steps of a tile");
+    // Where the DMA of one K tile goes.  Deep ring (S >= 3): KSTEPS equal
+    // parts, part 0 in the last step of K tile kt-S (right after the barrier
+    // that frees its stage) and part q in step q-1 of K tile kt-S+1, so the
+    // texture path (64 B/clk per CU, about half of what the MFMAs consume at
+    // full rate) is fed evenly and a tile lands S-2 K tiles before it is
+    // read.  Two stages: the instructions [0, P0) go over the last step of K
+    // tile kt-2 and the remaining DQ quarters [P0, NQ) over the first half
+    // of step 0 of K tile kt-1, so that even the last of them lands with
+    // half a step to spare before the wait that precedes the last step.
+    constexpr int NPARTS = S == 2 ? 1 : CF::KSTEPS;
+    constexpr int P0 = S == 2 ? NQ_STAGE - NQ_STAGE * CF::DQ / 4 : NQ_STAGE / NPARTS;
+    static_assert(S != 2 || CF::KSTEPS >= 2 || CF::DQ == 0, "an early part needs a step before the last");
     // K tile kt from stage st; nst = stage of kt+1, pst = stage of kt-1
     // (which tile t1 = kt+S-1 refills).  GUARD: DMA checks are needed.
     auto k_tile = [&](auto guard_c, int kt, int st, int nst, int pst, int t1) {
       constexpr bool GUARD = decltype(guard_c)::value;
       static_for<0, CF::KSTEPS - 1>([&](auto s_c) {
         constexpr int SS = decltype(s_c)::value;
-        if constexpr (SS + 1 < NPARTS)
-          kstep(IntC<SS & 1>{}, st, SS + 1, IntC<(SS + 1) * NQ_STAGE / NPARTS>{},
-                IntC<(SS + 2) * NQ_STAGE / NPARTS>{}, guard_c, t1, pst);
+        if constexpr (S == 2 && SS == 0 && P0 < NQ_STAGE)
+          kstep(IntC<0>{}, st, IntC<1>{}, IntC<P0>{}, IntC<NQ_STAGE>{}, guard_c, t1, pst, IntC<MF / 2>{});
+        else if constexpr (S != 2)
+          kstep(IntC<SS & 1>{}, st, IntC<SS + 1>{}, IntC<(SS + 1) * NQ_STAGE / NPARTS>{},
+                IntC<(SS + 2) * NQ_STAGE / NPARTS>{}, guard_c, t1, pst, IntC<MF>{});
         else
-          kstep(IntC<SS & 1>{}, st, SS + 1, IntC<0>{}, IntC<0>{}, guard_c, t1, pst);
+          kstep(IntC<SS & 1>{}, st, IntC<SS + 1>{}, IntC<0>{}, IntC<0>{}, guard_c, t1, pst, IntC<MF>{});
       });
       // Tile kt+1 (read by the last step) must be complete; the groups
       // issued after it (deep ring: min(S-2, KT-2-kt) whole tiles) may pend.
@@ -1040,8 +1097,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       barrier_lds();  // tile kt+1 visible; every wave is done reading stage kt
       // Last step: its fragments are in registers; read step 0 of tile kt+1
       // meanwhile and refill stage kt (free now) with part 0 of tile kt+S.
-      kstep(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, IntC<NQ_STAGE / NPARTS>{}, guard_c, kt + S,
-            st);
+      kstep(IntC<(CF::KSTEPS - 1) & 1>{}, nst, IntC<0>{}, IntC<0>{}, IntC<P0>{}, guard_c, kt + S, st, IntC<MF>{});
     };
 
     if constexpr (CF::A_KMAJOR && CF::LOADER == 1) {
@@ -1092,13 +1148,13 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
         const int st = P, nst = P ^ 1;
         // step 0: write tile kt+1 (regs P^1) to stage kt+1; load tile kt+2 to regs P
         kstep_ops(IntC<0>{}, st, 1, IntC<NOPS1>{},
-                  first_step_ops(IntC<P ^ 1>{}, nst, IntC<P>{}, kt + 2, kt + 2 < KT));
+                  first_step_ops(IntC<P ^ 1>{}, nst, IntC<P>{}, kt + 2, kt + 2 < KT), IntC<MF>{});
         static_for<1, CF::KSTEPS - 1>([&](auto s_c) {
           constexpr int SS = decltype(s_c)::value;
-          kstep_ops(IntC<SS & 1>{}, st, SS + 1, IntC<0>{}, [](auto) {});
+          kstep_ops(IntC<SS & 1>{}, st, SS + 1, IntC<0>{}, [](auto) {}, IntC<MF>{});
         });
         barrier_lds();  // tile kt+1 written and visible; stage kt no longer read
-        kstep_ops(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, [](auto) {});
+        kstep_ops(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, [](auto) {}, IntC<MF>{});
       };
       static_assert(CF::KSTEPS >= 2, "register loader needs two k steps per tile");
       int kt = 0;
@@ -1108,6 +1164,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       }
       if (kt < KT) tile_iter(IntC<0>{}, kt);
     } else if constexpr (CF::A_KMAJOR) {
+      static_assert(CF::KSTEPS % 2 == 0, "k steps alternate fragment buffers across K tiles");
       // Prologue: two stages: K tiles 0 and 1 whole, tile 0 complete.  Deep
       // ring: K tiles 0 .. S-2 whole, tile 0 complete, then part 0 of tile
       // S-1 (stage S-1 is untouched so far).
@@ -1124,7 +1181,11 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
         for (int k = 0; k < S - 1; ++k)
           if (k < KT) issue_dma(k);
         wait_pending(min(S - 1, KT) - 1);
-        static_for<0, NQ_STAGE / NPARTS>([&](auto d_c) { dma_one(d_c, IntC<1>{}, S - 1, S - 1); });
+        // (tile numbers known at compile time are hidden from constant
+        // folding: the DMA's scalar offset operand takes no literal)
+        int t_pro = S - 1;
+        asm("" : "+s"(t_pro));
+        static_for<0, P0>([&](auto d_c) { dma_one(d_c, IntC<1>{}, t_pro, S - 1); });
       }
       barrier_lds();
       load_step(fa[0], fb[0], 0, 0);
