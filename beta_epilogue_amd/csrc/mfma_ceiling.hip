@@ -1,7 +1,7 @@
 // mfma_ceiling.hip -- measurement tool (not part of the GEMM path): the
 // steady shader clock and throughput of a register-only stream of
-// v_mfma_f32_32x32x16_f16 on one workgroup per CU, with constant or random
-// operands.  Under the board power cap the clock, and so the attainable MFMA
+// v_mfma_f32_32x32x16_f16 or v_mfma_f32_16x16x32_f16 on one workgroup per
+// CU, with constant or random operands.  Under the board power cap the clock, and so the attainable MFMA
 // rate, depends on how many operand bits toggle; the GEMM's fraction of this
 // rate, measured on data of its own distribution, separates its own losses
 // from the part's power limit.
@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <vector>
 
 #include "mfma_ceiling.h"
@@ -25,6 +26,13 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8, kFrag = 8, kAcc = 8, kUnroll = 8;
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// BLK 32: v_mfma_f32_32x32x16_f16 on kAcc accumulators; BLK 16:
+// v_mfma_f32_16x16x32_f16 (half the FLOP per instruction) on 2 * kAcc
+// accumulators, two instructions per 32x32x16 one, so both shapes do the
+// same FLOP per iteration.
+template <int BLK>
 __global__ __launch_bounds__(kWaves * 64, 1) void mfma_stream(const v4i* src, float* out, long long* clk,
                                                               int iters) {
   const int lane = threadIdx.x & 63;
@@ -32,23 +40,29 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mfma_stream(const v4i* src, fl
   v4i f[kFrag];
 #pragma unroll
   for (int i = 0; i < kFrag; ++i) f[i] = src[(wave * kFrag + i) * 64 + lane];
-  v16f acc[kAcc];
+  constexpr int NACC = BLK == 32 ? kAcc : 2 * kAcc;
+  typedef typename std::conditional<BLK == 32, v16f, v4f>::type acc_t;
+  acc_t acc[NACC];
 #pragma unroll
-  for (int i = 0; i < kAcc; ++i) acc[i] = v16f{};
+  for (int i = 0; i < NACC; ++i) acc[i] = acc_t{};
   const long long c0 = clock64(), w0 = wall_clock64();
   for (int it = 0; it < iters; it += kUnroll) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-      for (int i = 0; i < kAcc; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, f[(i + u) % kFrag]),
-                                                        __builtin_bit_cast(v8h, f[(i + 3 + 2 * u) % kFrag]),
-                                                        acc[i], 0, 0, 0);
+      for (int i = 0; i < NACC; ++i) {
+        const v8h a = __builtin_bit_cast(v8h, f[(i + u) % kFrag]);
+        const v8h b = __builtin_bit_cast(v8h, f[(i + 3 + 2 * u) % kFrag]);
+        if constexpr (BLK == 32)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[i], 0, 0, 0);
+        else
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[i], 0, 0, 0);
+      }
   }
   const long long c1 = clock64(), w1 = wall_clock64();
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kAcc; ++i) s += acc[i][lane & 15];
+  for (int i = 0; i < NACC; ++i) s += acc[i][lane & 3];
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
   if (threadIdx.x == 0) {
     clk[blockIdx.x * 2] = c1 - c0;
@@ -58,13 +72,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mfma_stream(const v4i* src, fl
 
 }  // namespace
 
-// Runs the stream on one workgroup per CU of the current device: a warm-up
+// Runs the stream of block size `block` (32 or 16) on one workgroup per CU
+// of the current device: a warm-up
 // launch, then `reps` timed launches of `iters` (a multiple of 8) MFMAs per
 // accumulator.  Reports the last launch: milliseconds (HIP events), the
 // shader clock of workgroup 0 in GHz (clock64 against the 100 MHz wall
 // clock) and TFLOP/s.  Returns 0, or a HIP error code.
-extern "C" int mfma_ceiling_run(int random_operands, int iters, int reps, float* ms_out, double* ghz_out,
-                                double* tflops_out) {
+extern "C" int mfma_ceiling_run(int block, int random_operands, int iters, int reps, float* ms_out,
+                                double* ghz_out, double* tflops_out) {
+  if (block != 32 && block != 16) return (int)hipErrorInvalidValue;
   int dev = 0;
   hipDeviceProp_t prop;
   hipError_t e = hipGetDevice(&dev);
@@ -106,8 +122,12 @@ extern "C" int mfma_ceiling_run(int random_operands, int iters, int reps, float*
   if (e == hipSuccess) e = hipEventCreate(&e1);
   for (int r = 0; e == hipSuccess && r <= reps; ++r) {
     e = hipEventRecord(e0, 0);
-    hipLaunchKernelGGL(mfma_stream, dim3(blocks), dim3(kWaves * 64), 0, 0, src, out, clk,
-                       r == 0 ? kUnroll * 64 : iters);
+    if (block == 32)
+      hipLaunchKernelGGL(mfma_stream<32>, dim3(blocks), dim3(kWaves * 64), 0, 0, src, out, clk,
+                         r == 0 ? kUnroll * 64 : iters);
+    else
+      hipLaunchKernelGGL(mfma_stream<16>, dim3(blocks), dim3(kWaves * 64), 0, 0, src, out, clk,
+                         r == 0 ? kUnroll * 64 : iters);
     if (e == hipSuccess) e = hipGetLastError();
     if (e == hipSuccess) e = hipEventRecord(e1, 0);
     if (e == hipSuccess) e = hipEventSynchronize(e1);
