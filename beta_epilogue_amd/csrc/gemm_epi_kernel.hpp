@@ -1077,17 +1077,17 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     static_assert(S != 2 || CF::KSTEPS >= 2 || CF::DQ == 0, "an early part needs a step before the last");
     // K tile kt from stage st; nst = stage of kt+1, pst = stage of kt-1
     // (which tile t1 = kt+S-1 refills).  GUARD: DMA checks are needed.
-    auto k_tile = [&](auto guard_c, int kt, int st, int nst, int pst, int t1) {
+    auto k_tile = [&](auto guard_c, int kt, auto st, auto nst, auto pst, int t1) {
       constexpr bool GUARD = decltype(guard_c)::value;
       static_for<0, CF::KSTEPS - 1>([&](auto s_c) {
         constexpr int SS = decltype(s_c)::value;
         if constexpr (S == 2 && SS == 0 && P0 < NQ_STAGE)
-          kstep(IntC<0>{}, st, IntC<1>{}, IntC<P0>{}, IntC<NQ_STAGE>{}, guard_c, t1, pst, IntC<MF / 2>{});
+          kstep(IntC<0>{}, st, IntC<1>{}, IntC<P0>{}, IntC<NQ_STAGE>{}, guard_c, t1, (int)pst, IntC<MF / 2>{});
         else if constexpr (S != 2)
           kstep(IntC<SS & 1>{}, st, IntC<SS + 1>{}, IntC<(SS + 1) * NQ_STAGE / NPARTS>{},
-                IntC<(SS + 2) * NQ_STAGE / NPARTS>{}, guard_c, t1, pst, IntC<MF>{});
+                IntC<(SS + 2) * NQ_STAGE / NPARTS>{}, guard_c, t1, (int)pst, IntC<MF>{});
         else
-          kstep(IntC<SS & 1>{}, st, IntC<SS + 1>{}, IntC<0>{}, IntC<0>{}, guard_c, t1, pst, IntC<MF>{});
+          kstep(IntC<SS & 1>{}, st, IntC<SS + 1>{}, IntC<0>{}, IntC<0>{}, guard_c, t1, (int)pst, IntC<MF>{});
       });
       // Tile kt+1 (read by the last step) must be complete; the groups
       // issued after it (deep ring: min(S-2, KT-2-kt) whole tiles) may pend.
@@ -1097,7 +1097,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       barrier_lds();  // tile kt+1 visible; every wave is done reading stage kt
       // Last step: its fragments are in registers; read step 0 of tile kt+1
       // meanwhile and refill stage kt (free now) with part 0 of tile kt+S.
-      kstep(IntC<(CF::KSTEPS - 1) & 1>{}, nst, IntC<0>{}, IntC<0>{}, IntC<P0>{}, guard_c, kt + S, st, IntC<MF>{});
+      kstep(IntC<(CF::KSTEPS - 1) & 1>{}, nst, IntC<0>{}, IntC<0>{}, IntC<P0>{}, guard_c, kt + S, (int)st,
+            IntC<MF>{});
     };
 
     if constexpr (CF::A_KMAJOR && CF::LOADER == 1) {
@@ -1200,6 +1201,20 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
         k_tile(IntC<1>{}, 0, 0, 1, 1, KT);
         kt = 1;
         st = 1;
+      }
+      if constexpr (S == 2) {
+        // Two stages: K tiles in pairs with the stage a compile-time
+        // constant, so every fragment address is a loop-invariant register
+        // plus an immediate (no address arithmetic between the MFMAs).
+        if (kt + S < kt_whole && st == 1) {
+          k_tile(IntC<0>{}, kt, IntC<1>{}, IntC<0>{}, IntC<0>{}, kt + S - 1);
+          ++kt;
+          st = 0;
+        }
+        for (; kt + 1 + S < kt_whole; kt += 2) {
+          k_tile(IntC<0>{}, kt, IntC<0>{}, IntC<1>{}, IntC<1>{}, kt + S - 1);
+          k_tile(IntC<0>{}, kt + 1, IntC<1>{}, IntC<0>{}, IntC<0>{}, kt + S);
+        }
       }
       for (; kt + S < kt_whole; ++kt) {
         k_tile(IntC<0>{}, kt, st, next(st), prev(st), kt + S - 1);
