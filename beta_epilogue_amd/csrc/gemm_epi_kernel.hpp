@@ -706,8 +706,8 @@ __device__ __forceinline__ void epilogue(const Params& p, const ACC (&acc)[CF::F
 // buffer resource based at this wave's output region with 32-bit offsets:
 // rows (N-major) or columns (M-major) past the matrix fall outside the
 // resource's extent, so their loads read zero and their stores are dropped
-// by the range check; a lane whose 4 elements lie past the other extent gets
-// an offset above 2^31.  A skipped term is an empty resource with a zero
+// by the range check; a lane whose 16 bytes lie past the other extent gets
+// an offset above 2^31 (the 16-byte rule keeps a lane's group whole).  A skipped term is an empty resource with a zero
 // scale; a missing Y is an empty resource.  C and X loads run DIST passes
 // ahead of the passes being finished.
 // ---------------------------------------------------------------------------
@@ -719,41 +719,48 @@ template <> struct EpiElem<T_I32> { static constexpr int SIZE = 4; };
 
 constexpr int EPI_NT = 2;  // cache policy: streaming (non-temporal) access
 
+// One 16-byte access per lane and array: 8 elements of a 2-byte type or 4
+// of a 4-byte type.
 template <int T>
-__device__ __forceinline__ v4u epi_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if constexpr (EpiElem<T>::SIZE == 2) {
-    const v2u u = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, EPI_NT));
-    return v4u{u.x, u.y, 0u, 0u};
-  } else {
-    return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, EPI_NT));
-  }
+__device__ __forceinline__ v4u epi_ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, EPI_NT));
 }
 
+// Elements [4h, 4h+4) of a 16-byte group as floats.
 template <int T>
-__device__ __forceinline__ v4f epi_dec4(v4u r) {
+__device__ __forceinline__ v4f epi_dec(v4u r, int h) {
+  const uint32_t a = h ? r.z : r.x, b = h ? r.w : r.y;
   if constexpr (T == T_F16) {
-    const v2u h2 = {r.x, r.y};
-    const _Float16* h = (const _Float16*)&h2;
-    return v4f{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    const v2u h2 = {a, b};
+    const _Float16* f = (const _Float16*)&h2;
+    return v4f{(float)f[0], (float)f[1], (float)f[2], (float)f[3]};
   } else if constexpr (T == T_BF16) {
-    return v4f{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
-               __uint_as_float(r.y & 0xffff0000u)};
+    return v4f{__uint_as_float(a << 16), __uint_as_float(a & 0xffff0000u), __uint_as_float(b << 16),
+               __uint_as_float(b & 0xffff0000u)};
   } else {
     return __builtin_bit_cast(v4f, r);
   }
 }
 
+// Rounds (to nearest even) and packs 4 (4-byte types: lo only) or 8 values.
 template <int T>
-__device__ __forceinline__ void epi_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, v4f v) {
+__device__ __forceinline__ v4u epi_pack(v4f lo, v4f hi) {
   if constexpr (T == T_F16) {
-    _Float16 h[4] = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, h), r, (int)off, 0, EPI_NT);
+    _Float16 h[8] = {(_Float16)lo.x, (_Float16)lo.y, (_Float16)lo.z, (_Float16)lo.w,
+                     (_Float16)hi.x, (_Float16)hi.y, (_Float16)hi.z, (_Float16)hi.w};
+    return __builtin_bit_cast(v4u, h);
   } else if constexpr (T == T_BF16) {
-    __bf16 b[4] = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, b), r, (int)off, 0, EPI_NT);
+    __bf16 b[8] = {(__bf16)lo.x, (__bf16)lo.y, (__bf16)lo.z, (__bf16)lo.w,
+                   (__bf16)hi.x, (__bf16)hi.y, (__bf16)hi.z, (__bf16)hi.w};
+    return __builtin_bit_cast(v4u, b);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, (int)off, 0, EPI_NT);
+    return __builtin_bit_cast(v4u, lo);
   }
+}
+
+template <int T>
+__device__ __forceinline__ void epi_st(__amdgpu_buffer_rsrc_t r, uint32_t off, v4u v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, EPI_NT);
 }
 
 template <class CF, int T, class ACC>
@@ -761,17 +768,19 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
                                                int wave, int lane, int l, int mw, int nw) {
   constexpr bool NMAJ = CF::CD_NMAJOR;
   constexpr int LINE = CF::EPI_LINE, PITCH = CF::EPI_PITCH;
-  constexpr int LPL = LINE / 4;        // lanes per line
-  constexpr int LINES_PER_PASS = 64 / LPL;
   constexpr int ES = EpiElem<T>::SIZE;
+  constexpr int VEC = 16 / ES;         // elements per lane: one 16-byte access per array
+  constexpr int LPL = LINE / VEC;      // lanes per line
+  constexpr int LINES_PER_PASS = 64 / LPL;
+  static_assert(LPL >= 1 && LPL <= 64 && 32 % LINES_PER_PASS == 0, "line split over the lanes");
   float* region = (float*)(lds + wave * CF::EPI_WAVE_BYTES);
   constexpr int NBLK = (NMAJ ? CF::WM : CF::WN) / 32;
   constexpr int PASSES = 32 / LINES_PER_PASS;
   constexpr int NP = NBLK * PASSES;
-  constexpr int DIST0 = ES == 2 ? 8 : 4;  // 32 VGPRs of C and X in flight
+  constexpr int DIST0 = 8;  // passes of C and X loads in flight: 16 KiB per wave
   constexpr int DIST = DIST0 < NP ? DIST0 : NP;
   const int sub = lane / LPL;
-  const int e = (lane % LPL) * 4;
+  const int e = (lane % LPL) * VEC;
 
   // The wave's region: N-major rows [mw, mw+WM) (ld = N), M-major columns
   // [nw, nw+WN) (ld = M); `lines` of them lie inside the matrix.
@@ -805,8 +814,8 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
   v4u cr[DIST + 1], xr[DIST + 1];
   static_for<0, DIST>([&](auto i_c) {
     constexpr int i = decltype(i_c)::value;
-    cr[i] = epi_ld4<T>(rc, off(i));
-    xr[i] = epi_ld4<T>(rx, off(i));
+    cr[i] = epi_ld<T>(rc, off(i));
+    xr[i] = epi_ld<T>(rx, off(i));
   });
   static_for<0, NP>([&](auto i_c) {
     constexpr int i = decltype(i_c)::value, S = i % (DIST + 1);
@@ -814,31 +823,39 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
     // this wave's reads of the previous block are issued before these
     // writes, and LDS serves one wave's operations in order
     if constexpr (ps == 0) write_block(IntC<blk>{});
-    const v4f w = *(const v4f*)(region + (ps * LINES_PER_PASS + sub) * PITCH + e);
+    const float* wp = region + (ps * LINES_PER_PASS + sub) * PITCH + e;
+    const v4f w0 = *(const v4f*)wp;
+    const v4f w1 = VEC == 8 ? *(const v4f*)(wp + 4) : v4f{};
     if constexpr (i + DIST < NP) {
       constexpr int SN = (i + DIST) % (DIST + 1);
-      cr[SN] = epi_ld4<T>(rc, off(i + DIST));
-      xr[SN] = epi_ld4<T>(rx, off(i + DIST));
+      cr[SN] = epi_ld<T>(rc, off(i + DIST));
+      xr[SN] = epi_ld<T>(rx, off(i + DIST));
     }
     const uint32_t o = off(i);
     if constexpr (T == T_I32) {
-      const v4u a = __builtin_bit_cast(v4u, w);
+      const v4u a = __builtin_bit_cast(v4u, w0);
       const v4u t = a * (unsigned)p.ialpha + cr[S] * (unsigned)p.ibeta + xr[S] * (unsigned)p.ix;
-      epi_st4<T>(rd, o, __builtin_bit_cast(v4f, t));
-      epi_st4<T>(ry, o, w);
+      epi_st<T>(rd, o, t);
+      epi_st<T>(ry, o, a);
     } else {
-      const v4f c = epi_dec4<T>(cr[S]), x = epi_dec4<T>(xr[S]);
-      v4f t = w * p.alpha;
-      t.x = __builtin_fmaf(beta, c.x, t.x);
-      t.y = __builtin_fmaf(beta, c.y, t.y);
-      t.z = __builtin_fmaf(beta, c.z, t.z);
-      t.w = __builtin_fmaf(beta, c.w, t.w);
-      t.x = __builtin_fmaf(xf, x.x, t.x);
-      t.y = __builtin_fmaf(xf, x.y, t.y);
-      t.z = __builtin_fmaf(xf, x.z, t.z);
-      t.w = __builtin_fmaf(xf, x.w, t.w);
-      epi_st4<T>(rd, o, t);
-      epi_st4<T>(ry, o, w);
+      // D = alpha * acc + beta * C + x_factor * X, in this order
+      auto fin = [&](v4f w, int h) {
+        const v4f c = epi_dec<T>(cr[S], h), x = epi_dec<T>(xr[S], h);
+        v4f t = w * p.alpha;
+        t.x = __builtin_fmaf(beta, c.x, t.x);
+        t.y = __builtin_fmaf(beta, c.y, t.y);
+        t.z = __builtin_fmaf(beta, c.z, t.z);
+        t.w = __builtin_fmaf(beta, c.w, t.w);
+        t.x = __builtin_fmaf(xf, x.x, t.x);
+        t.y = __builtin_fmaf(xf, x.y, t.y);
+        t.z = __builtin_fmaf(xf, x.z, t.z);
+        t.w = __builtin_fmaf(xf, x.w, t.w);
+        return t;
+      };
+      const v4f d0 = fin(w0, 0);
+      const v4f d1 = VEC == 8 ? fin(w1, 1) : v4f{};
+      epi_st<T>(rd, o, epi_pack<T>(d0, d1));
+      epi_st<T>(ry, o, epi_pack<T>(w0, w1));
     }
   });
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

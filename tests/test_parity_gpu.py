@@ -78,6 +78,9 @@ EDGE = [
     CFG[3].replace(name="i8_mmajor_cdm", M=272, N=260, K=176, L=2, cd_major="M", seed=6700),
     CFG[3].replace(name="i8_mmajor_ktail", M=48, N=40, K=48, L=1, seed=6800),
     CFG[2].replace(name="f16_large_k", M=256, N=512, K=4104, seed=6900),
+    # N-major f16 C/X/D/Y with both tile extents cut: 8-element lane groups
+    # past N and rows past M
+    CFG[2].replace(name="f16_ragged_mn", M=300, N=392, K=96, seed=7000),
 ]
 
 
