@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOP/s and % of MFMA dense peak, 8192³ fp16 GEMM w/ fused epilogue"
 # MI355X datasheet dense MFMA peaks, TFLOP/s (TOP/s for int8)
 PEAK = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "i8": 5000.0}
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -131,7 +132,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload index 0..4 (2 = 8192^3 fp16 with C, X, D, Y)")
+                    help="workload index 0..4 (2 = 8192^3 fp16 with C, X, D, Y); 5 = the same at K=256 (HBM-bound)")
     ap.add_argument("--variant", type=int, default=-1)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -219,8 +220,10 @@ def main():
 
     # The attainable MFMA rate on this machine for fp16 data like the workload's
     # (random operands; the power cap sets the clock), measured right after.
+    abytes = p.algorithmic_bytes()
+    mfma_bound = flops / abytes >= peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     attainable = None
-    if p.ab == "f16" and not args.no_ceiling:
+    if p.ab == "f16" and mfma_bound and not args.no_ceiling:
         cr = mfma_ceiling(rounds=2, kinds=("random",))
         key, c = max(((k, v) for k, v in cr.items() if k.startswith("random_")),
                      key=lambda kv: kv[1]["tflops"])
@@ -229,6 +232,20 @@ def main():
                       "how": "the faster of register-only v_mfma_f32_32x32x16_f16 and "
                              "v_mfma_f32_16x16x32_f16 streams on every CU, uniformly random fp16 "
                              "operands, same run (bench.py --mfma-ceiling)"}
+
+    # MFMA-bound unless the arithmetic intensity (FLOP per algorithmic byte)
+    # is under the ridge point peak / HBM bandwidth; then GB/s against HBM.
+    common = {"traffic": measured_traffic(p.name), "algorithmic_bytes": abytes,
+              "kernel": plan["name"], "avg_launch_ms": round(avg_launch_ms, 5)}
+    if mfma_bound:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), **common,
+                    "attainable_random_operands": attainable}
+    else:
+        gbs = abytes / (avg_launch_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), **common,
+                    "tflops": round(achieved, 2)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -252,12 +269,7 @@ def main():
                    "cd_major": p.cd_major, "c": p.c, "x": p.x, "d": p.d,
                    "y": p.y, "alpha": p.alpha, "beta": p.beta,
                    "x_factor": p.x_factor, "accumulate": "i32" if p.ab == "i8" else "f32"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(p.name),
-                     "algorithmic_bytes": p.algorithmic_bytes(),
-                     "kernel": plan["name"], "avg_launch_ms": round(avg_launch_ms, 5),
-                     "attainable_random_operands": attainable},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "plan": plan,
     }

@@ -80,7 +80,7 @@ class Problem:
         return total
 
 
-# The five benchmark workloads (index 0..4).
+# The five benchmark workloads (index 0..4) and one HBM-bound extra (5).
 CONFIGS = [
     Problem("int_small_f16_128", 128, 128, 128, 1, "f16", c="f32", d="f32",
             alpha=1.5, beta=0.5, dist_ab="int2", dist_c="int2", seed=1000),
@@ -96,6 +96,12 @@ CONFIGS = [
     Problem("e4m3_8192_f16out", 8192, 8192, 8192, 1, "e4m3", c="f16",
             d="f16", alpha=0.25, beta=1.0, dist_ab="e4m3tab", dist_c="normal",
             seed=5000),
+    # Index 5, a reported extra: the fp16 fused workload at K = 256, where the
+    # epilogue's C, X, D, Y traffic (512 MiB) dwarfs the 34 GFLOP of the
+    # product, so the launch is HBM-bound.
+    Problem("f16_8192x8192_k256_cxdy", 8192, 8192, 256, 1, "f16", c="f16",
+            x="f16", d="f16", y="f16", alpha=2.0, beta=1.0, x_factor=3.0,
+            dist_ab="unif", dist_c="unif", dist_x="unif", seed=7100),
 ]
 
 _E4M3_TABLE = None

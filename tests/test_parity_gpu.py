@@ -44,7 +44,7 @@ def test_parity_small_full_oracle(p, exact):
     _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
 
 
-@pytest.mark.parametrize("i", [1, 2, 3, 4], ids=[c.name for c in CFG[1:]])
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5], ids=[c.name for c in CFG[1:6]])
 def test_parity_full_size_sampled(i):
     """The benchmark shapes, in the launch configuration the bench times."""
     p = CFG[i]
