@@ -11,7 +11,8 @@ dimensions", and its fused epilogue):
 
     Y = A . B^T (per batch)      D = alpha*Y + beta*C + x_factor*X
 
-returning double-precision D, Y and the side sum S = sum_k |a||b| that the
+or, with ``relu=True`` (the form the example's epilogue function builds),
+D = max(0, alpha*Y + beta*C) + x_factor*X, returning double-precision D, Y and the side sum S = sum_k |a||b| that the
 normalised error bound divides by.
 """
 from __future__ import annotations
@@ -64,11 +65,12 @@ class Oracle:
         lib.orc_decode.argtypes = [ctypes.c_int, P, ctypes.c_int64, P]
         lib.orc_gemm_epi_full.argtypes = [ctypes.POINTER(_Desc), P, P, P, P,
                                           ctypes.c_double, ctypes.c_double,
-                                          ctypes.c_double, P, P, P, ctypes.c_int]
+                                          ctypes.c_double, ctypes.c_int, P, P, P,
+                                          ctypes.c_int]
         lib.orc_gemm_epi_points.argtypes = [ctypes.POINTER(_Desc), P, P, P, P,
                                             ctypes.c_double, ctypes.c_double,
-                                            ctypes.c_double, ctypes.c_int64, P,
-                                            P, P, P, ctypes.c_int]
+                                            ctypes.c_double, ctypes.c_int,
+                                            ctypes.c_int64, P, P, P, P, ctypes.c_int]
         self.lib = lib
         self.path = lib_path
 
@@ -156,9 +158,10 @@ def _desc(M, N, K, L, a_major, b_major, cd_major, ab, c, x):
 
 def _gemm_epi(lib, M, N, K, L, A, B, C=None, X=None, *, ab="f16", c=None, x=None,
              a_major="K", b_major="K", cd_major="N", alpha=1.0, beta=0.0,
-             x_factor=0.0, nthreads=None):
+             x_factor=0.0, relu=False, nthreads=None):
     """Full oracle result: (D_ref, Y_ref, S) as flat float64 arrays laid out
-    like C/D (packed batches, L outermost, ``cd_major`` contiguous)."""
+    like C/D (packed batches, L outermost, ``cd_major`` contiguous).  relu:
+    D = max(0, alpha*Y + beta*C) + x_factor*X."""
     d = _desc(M, N, K, L, a_major, b_major, cd_major, ab, c, x)
     a, b = _bits(A, ab), _bits(B, ab)
     cc = _bits(C, c) if c else None
@@ -170,7 +173,8 @@ def _gemm_epi(lib, M, N, K, L, A, B, C=None, X=None, *, ab="f16", c=None, x=None
     S = np.empty(n, np.float64)
     rc = lib.orc_gemm_epi_full(ctypes.byref(d), _ptr(a), _ptr(b), _ptr(cc),
                                    _ptr(xx), float(alpha), float(beta),
-                                   float(x_factor), _ptr(D), _ptr(Y), _ptr(S),
+                                   float(x_factor), int(bool(relu)), _ptr(D),
+                                   _ptr(Y), _ptr(S),
                                    nthreads or host_threads())
     if rc:
         raise ValueError("orc_gemm_epi_full failed (%d)" % rc)
@@ -179,7 +183,7 @@ def _gemm_epi(lib, M, N, K, L, A, B, C=None, X=None, *, ab="f16", c=None, x=None
 
 def _gemm_epi_points(lib, M, N, K, L, A, B, C=None, X=None, *, points, ab="f16",
                     c=None, x=None, a_major="K", b_major="K", cd_major="N",
-                    alpha=1.0, beta=0.0, x_factor=0.0, nthreads=None):
+                    alpha=1.0, beta=0.0, x_factor=0.0, relu=False, nthreads=None):
     """Oracle at listed (l, m, n) points: returns (D_ref, Y_ref, S) per point."""
     d = _desc(M, N, K, L, a_major, b_major, cd_major, ab, c, x)
     a, b = _bits(A, ab), _bits(B, ab)
@@ -193,7 +197,8 @@ def _gemm_epi_points(lib, M, N, K, L, A, B, C=None, X=None, *, points, ab="f16",
     S = np.empty(n, np.float64)
     rc = lib.orc_gemm_epi_points(ctypes.byref(d), _ptr(a), _ptr(b),
                                      _ptr(cc), _ptr(xx), float(alpha),
-                                     float(beta), float(x_factor), n, _ptr(pts),
+                                     float(beta), float(x_factor),
+                                     int(bool(relu)), n, _ptr(pts),
                                      _ptr(D), _ptr(Y), _ptr(S),
                                      nthreads or host_threads())
     if rc:

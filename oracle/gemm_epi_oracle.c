@@ -14,6 +14,12 @@
  *     Y[l,m,n] = sum_k A[l,m,k] * B[l,n,k]
  *     D[l,m,n] = alpha * Y[l,m,n] + beta * C[l,m,n] + x_factor * X[l,m,n]
  *
+ * and, as an option, the form of the example's epilogue function (the code
+ * that builds the epilogue in the same file), which clamps the scaled
+ * accumulator plus the C term at zero before the X term is added:
+ *
+ *     D[l,m,n] = max(0, alpha * Y[l,m,n] + beta * C[l,m,n]) + x_factor * X[l,m,n]
+ *
  * A is M x K x L, B is N x K x L (so the product is A times B-transposed in
  * row-major algebra), C/X/D/Y are M x N x L.  Every stored element is decoded
  * exactly to double, the contraction runs in double in ascending k, and the
@@ -24,7 +30,8 @@
  *
  * Readings of points the pages leave open (each is listed with its reason in
  * the design notes of the repository):
- *   - no ReLU: the module docstring's formula has none;
+ *   - no ReLU by default: the module docstring's formula has none; the
+ *     clamped form is the separate option above;
  *   - D is formed from the accumulator, not from the rounded Y;
  *   - a C (X) term is skipped when C (X) is absent or beta (x_factor) is 0;
  *   - batches are packed, L outermost; the majorness letter names the
@@ -140,6 +147,7 @@ typedef struct {
   const orc_desc* d;
   const void *A, *B, *C, *X;
   double alpha, beta, xf;
+  int relu; /* clamp alpha*Y + beta*C at zero before the X term */
 } orc_problem;
 
 static void element(const orc_problem* p, int64_t l, int64_t m, int64_t n,
@@ -156,6 +164,7 @@ static void element(const orc_problem* p, int64_t l, int64_t m, int64_t n,
   int64_t o = cd_index(d, l, m, n);
   if (p->C && d->c_type != ORC_NONE && p->beta != 0.0)
     out += p->beta * load(p->C, d->c_type, o);
+  if (p->relu && !(out > 0.0)) out = 0.0;
   if (p->X && d->x_type != ORC_NONE && p->xf != 0.0)
     out += p->xf * load(p->X, d->x_type, o);
   if (dref) *dref = out;
@@ -237,17 +246,17 @@ static int check_desc(const orc_desc* d, const void* A, const void* B) {
  * yref, sref may be NULL.  Returns 0 on success. */
 int orc_gemm_epi_full(const orc_desc* d, const void* A, const void* B,
                       const void* C, const void* X, double alpha, double beta,
-                      double xf, double* dref, double* yref, double* sref,
-                      int nthreads) {
+                      double xf, int relu, double* dref, double* yref,
+                      double* sref, int nthreads) {
   if (check_desc(d, A, B)) return 1;
-  orc_problem p = {d, A, B, C, X, alpha, beta, xf};
+  orc_problem p = {d, A, B, C, X, alpha, beta, xf, relu != 0};
   return run_threads(&p, d->L * d->M, 0, 0, dref, yref, sref, nthreads);
 }
 
 /* Listed points: pts holds npts triples (l, m, n); outputs are per point. */
 int orc_gemm_epi_points(const orc_desc* d, const void* A, const void* B,
                         const void* C, const void* X, double alpha,
-                        double beta, double xf, int64_t npts,
+                        double beta, double xf, int relu, int64_t npts,
                         const int64_t* pts, double* dref, double* yref,
                         double* sref, int nthreads) {
   if (check_desc(d, A, B) || npts < 0 || (npts && !pts)) return 1;
@@ -257,6 +266,6 @@ int orc_gemm_epi_points(const orc_desc* d, const void* A, const void* B,
         q[2] >= d->N)
       return 2;
   }
-  orc_problem p = {d, A, B, C, X, alpha, beta, xf};
+  orc_problem p = {d, A, B, C, X, alpha, beta, xf, relu != 0};
   return run_threads(&p, npts, 1, pts, dref, yref, sref, nthreads);
 }

@@ -10,7 +10,8 @@ linearity, the skip rule for absent terms).
 The operation pinned is the one the CuTe DSL example
 ``custom_epilogue_dense_gemm.py`` documents in its module docstring
 ("Tensor dimensions" and the epilogue formula): Y = A.B^T per batch and
-D = alpha*Y + beta*C + x_factor*X.  The same pins are run against copies of
+D = alpha*Y + beta*C + x_factor*X, and the clamped form its epilogue function
+builds, D = max(0, alpha*Y + beta*C) + x_factor*X.  The same pins are run against copies of
 the oracle with planted mistakes (see test_oracle_mutants.py), each of which
 must fail at least one of them.
 """
@@ -71,10 +72,10 @@ def from_cd_layout(flat: np.ndarray, L, M, N, cd: str) -> np.ndarray:
 
 
 def run(orc, A, B, C=None, X=None, *, M, N, K, L, ab, c=None, x=None,
-        a="K", b="K", cd="N", alpha=1.0, beta=0.0, xf=0.0):
+        a="K", b="K", cd="N", alpha=1.0, beta=0.0, xf=0.0, relu=False):
     D, Y, S = orc.gemm_epi(M, N, K, L, A, B, C, X, ab=ab, c=c, x=x,
                            a_major=a, b_major=b, cd_major=cd, alpha=alpha,
-                           beta=beta, x_factor=xf, nthreads=2)
+                           beta=beta, x_factor=xf, relu=relu, nthreads=2)
     return (from_cd_layout(D, L, M, N, cd), from_cd_layout(Y, L, M, N, cd),
             from_cd_layout(S, L, M, N, cd))
 
@@ -428,8 +429,85 @@ def pin_linearity(orc):
         assert np.array_equal(D, al * Y + be * cv + xf * xv), (al, be, xf)
 
 
+# --------------------------------------------------------------------------
+# the clamped epilogue: D = max(0, alpha*Y + beta*C) + x_factor*X (the form
+# the example's epilogue function builds)
+# --------------------------------------------------------------------------
+
+def pin_relu_bruteforce(orc):
+    """Tiny mixed-sign problems: the clamped form equals exact rational
+    arithmetic (clamp at zero of alpha*Y + beta*C, then the X term), both
+    majornesses of C/D/X, floating and integer inputs."""
+    M, N, K, L = 4, 5, 6, 2
+    seed = 95000
+    for ab in ("f16", "i8"):
+        for cd in "NM":
+            seed += 10
+            Al = _rand("int2" if ab == "f16" else "i8full", ab, (L, M, K), seed + 1)
+            Bl = _rand("int2" if ab == "f16" else "i8full", ab, (L, N, K), seed + 2)
+            c = x = "f32" if ab == "f16" else "i32"
+            Cl = _rand("i1000" if ab == "i8" else "normal", c, (L, M, N), seed + 3)
+            Xl = _rand("i1000" if ab == "i8" else "normal", x, (L, M, N), seed + 4)
+            alpha, beta, xf = (1.5, -0.75, 2.0) if ab == "f16" else (3.0, -2.0, 5.0)
+            D, _, _ = run(orc, Al, Bl, store(Cl, "C", cd), store(Xl, "X", cd), M=M, N=N,
+                          K=K, L=L, ab=ab, c=c, x=x, cd=cd, alpha=alpha, beta=beta,
+                          xf=xf, relu=True)
+            av = lib_decode(Al).reshape(L, M, K)
+            bv = lib_decode(Bl).reshape(L, N, K)
+            cv = lib_decode(Cl).reshape(L, M, N)
+            xv = lib_decode(Xl).reshape(L, M, N)
+            clamped = 0
+            for l in range(L):
+                for m in range(M):
+                    for n in range(N):
+                        acc = sum(Fraction(av[l, m, k]) * Fraction(bv[l, n, k]) for k in range(K))
+                        inner = Fraction(alpha) * acc + Fraction(beta) * Fraction(cv[l, m, n])
+                        clamped += inner <= 0
+                        want = max(inner, Fraction(0)) + Fraction(xf) * Fraction(xv[l, m, n])
+                        assert abs(Fraction(D[l, m, n]) - want) <= abs(want) * Fraction(2.0 ** -50), \
+                            (ab, cd, l, m, n)
+            assert 0 < clamped < L * M * N, (ab, cd, clamped)  # both sides of the clamp occur
+
+
+def pin_relu_sign_identity(orc):
+    """max(0, v) + max(0, -v) = |v|: with the X term absent, the clamped form
+    at (alpha, beta) plus the clamped form at (-alpha, -beta) equals the
+    magnitude of the plain form, exactly (negation is exact)."""
+    M, N, K, L = 6, 7, 40, 2
+    Al = _rand("normal", "bf16", (L, M, K), 96001)
+    Bl = _rand("normal", "bf16", (L, N, K), 96002)
+    Cl = _rand("normal", "f32", (L, M, N), 96003)
+    for cd in "NM":
+        Cs = store(Cl, "C", cd)
+        kw = dict(M=M, N=N, K=K, L=L, ab="bf16", c="f32", cd=cd)
+        plain, _, _ = run(orc, Al, Bl, Cs, alpha=1.25, beta=-0.5, **kw)
+        pos, _, _ = run(orc, Al, Bl, Cs, alpha=1.25, beta=-0.5, relu=True, **kw)
+        neg, _, _ = run(orc, Al, Bl, Cs, alpha=-1.25, beta=0.5, relu=True, **kw)
+        assert np.all(pos >= 0) and np.all(neg >= 0), cd
+        assert np.array_equal(pos + neg, np.abs(plain)), cd
+        assert np.array_equal(pos - neg, plain), cd
+
+
+def pin_relu_closed_forms(orc):
+    """Clamped form: a non-positive alpha*Y + beta*C leaves exactly
+    x_factor*X; a non-negative one leaves exactly the plain form."""
+    M, N, K, L = 5, 6, 24, 1
+    Al = torch.from_numpy(np.abs(_rand("int2", "f16", (L, M, K), 97001).numpy()))
+    Bl = torch.from_numpy(np.abs(_rand("int2", "f16", (L, N, K), 97002).numpy()))
+    Cl = torch.from_numpy(np.abs(_rand("int2", "f16", (L, M, N), 97003).numpy()))
+    Xl = _rand("normal", "f16", (L, M, N), 97004)
+    kw = dict(M=M, N=N, K=K, L=L, ab="f16", c="f16", x="f16")
+    xv = lib_decode(Xl).reshape(L, M, N)
+    D, _, _ = run(orc, Al, Bl, Cl, Xl, alpha=-2.0, beta=-1.0, xf=3.0, relu=True, **kw)
+    assert np.array_equal(D, 3.0 * xv)
+    Dr, _, _ = run(orc, Al, Bl, Cl, Xl, alpha=2.0, beta=1.0, xf=3.0, relu=True, **kw)
+    Dp, _, _ = run(orc, Al, Bl, Cl, Xl, alpha=2.0, beta=1.0, xf=3.0, **kw)
+    assert np.array_equal(Dr, Dp)
+
+
 ALL_PINS = [pin_decode_golden, pin_decode_vs_library, pin_bruteforce_exact,
             pin_identity_A, pin_identity_B, pin_all_ones, pin_rank1,
             pin_alpha_zero, pin_skip_and_identity_epilogue, pin_integer_exact,
             pin_library_fp64, pin_majorness_duality, pin_batch_independence,
-            pin_points_match_full, pin_linearity]
+            pin_points_match_full, pin_linearity, pin_relu_bruteforce,
+            pin_relu_sign_identity, pin_relu_closed_forms]

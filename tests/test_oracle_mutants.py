@@ -45,6 +45,19 @@ MUTANTS = [
     ("i8_unsigned", "(double)((const int8_t*)p)[i]", "(double)((const uint8_t*)p)[i]"),
     ("bf16_as_f16", "case ORC_BF16: return dec_bf16(", "case ORC_BF16: return dec_f16("),
     ("points_swap_mn", "element(j->p, q[0], q[1], q[2]", "element(j->p, q[0], q[2], q[1]"),
+    ("relu_ignored", "if (p->relu && !(out > 0.0)) out = 0.0;", "(void)0;"),
+    ("relu_always", "if (p->relu && !(out > 0.0))", "if (!(out > 0.0))"),
+    ("relu_keeps_negatives", "if (p->relu && !(out > 0.0)) out = 0.0;",
+     "if (p->relu && (out > 0.0)) out = 0.0;"),
+    ("relu_after_x",
+     "  if (p->relu && !(out > 0.0)) out = 0.0;\n  if (p->X && d->x_type != ORC_NONE && p->xf != 0.0)\n"
+     "    out += p->xf * load(p->X, d->x_type, o);",
+     "  if (p->X && d->x_type != ORC_NONE && p->xf != 0.0)\n"
+     "    out += p->xf * load(p->X, d->x_type, o);\n  if (p->relu && !(out > 0.0)) out = 0.0;"),
+    ("relu_before_c", "  if (p->C && d->c_type != ORC_NONE && p->beta != 0.0)\n    out += p->beta * load(p->C, d->c_type, o);\n"
+     "  if (p->relu && !(out > 0.0)) out = 0.0;",
+     "  if (p->relu && !(out > 0.0)) out = 0.0;\n"
+     "  if (p->C && d->c_type != ORC_NONE && p->beta != 0.0)\n    out += p->beta * load(p->C, d->c_type, o);"),
 ]
 
 
