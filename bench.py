@@ -80,7 +80,8 @@ def cpu_baseline(p, ins, target_s: float):
                                ins["X"], points=pts, ab=p.ab, c=p.c, x=p.x,
                                a_major=p.a_major, b_major=p.b_major,
                                cd_major=p.cd_major, alpha=p.alpha, beta=p.beta,
-                               x_factor=p.x_factor, nthreads=threads)
+                               x_factor=p.x_factor, relu=p.epilogue == "relu",
+                               nthreads=threads)
         return time.perf_counter() - t0
 
     r0 = max(1, threads)
@@ -133,6 +134,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2,
                     help="workload index 0..4 (2 = 8192^3 fp16 with C, X, D, Y); 5 = the same at K=256 (HBM-bound)")
+    ap.add_argument("--epilogue", choices=("linear", "relu"), default="linear",
+                    help="relu: D = max(0, alpha*A.B^T + beta*C) + x_factor*X")
     ap.add_argument("--variant", type=int, default=-1)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -174,6 +177,8 @@ def main():
         return
 
     p = synth.CONFIGS[args.config]
+    if args.epilogue != "linear":
+        p = p.replace(name=p.name + "_" + args.epilogue, epilogue=args.epilogue)
     print("bench: workload %s M=%d N=%d K=%d L=%d" % (p.name, p.M, p.N, p.K, p.L),
           file=sys.stderr, flush=True)
     ins = synth.make_inputs(p)
@@ -183,7 +188,7 @@ def main():
     Y = torch.empty(shape, dtype=synth.TORCH_DTYPE[p.y], device="cuda") if p.y else None
     g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, a_major=p.a_major,
                      b_major=p.b_major, cd_major=p.cd_major, c=p.c, x=p.x,
-                     d=p.d, y=p.y, variant=args.variant)
+                     d=p.d, y=p.y, variant=args.variant, epilogue=p.epilogue)
     plan = g.plan
     stream = torch.cuda.current_stream()
 
@@ -268,7 +273,8 @@ def main():
                    "ab": p.ab, "a_major": p.a_major, "b_major": p.b_major,
                    "cd_major": p.cd_major, "c": p.c, "x": p.x, "d": p.d,
                    "y": p.y, "alpha": p.alpha, "beta": p.beta,
-                   "x_factor": p.x_factor, "accumulate": "i32" if p.ab == "i8" else "f32"},
+                   "x_factor": p.x_factor, "epilogue": p.epilogue,
+                   "accumulate": "i32" if p.ab == "i8" else "f32"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "plan": plan,

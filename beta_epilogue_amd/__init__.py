@@ -36,7 +36,8 @@ class gemm_epi_desc(ctypes.Structure):
                 ("a_major", ctypes.c_int32), ("b_major", ctypes.c_int32),
                 ("cd_major", ctypes.c_int32), ("ab_dtype", ctypes.c_int32),
                 ("c_dtype", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
-                ("d_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32)]
+                ("d_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32),
+                ("epilogue", ctypes.c_int32)]
 
 
 class gemm_epi_plan(ctypes.Structure):
@@ -103,11 +104,15 @@ def _check(code: int, where: str):
         raise GemmEpiError(code, where, last_error())
 
 
+EPILOGUES = {"linear": 0, "relu": 1}
+
+
 def make_desc(M, N, K, L=1, *, ab="f16", a_major="K", b_major="K",
-              cd_major="N", c=None, x=None, d="f32", y=None) -> gemm_epi_desc:
+              cd_major="N", c=None, x=None, d="f32", y=None,
+              epilogue="linear") -> gemm_epi_desc:
     return gemm_epi_desc(M, N, K, L, MAJOR[a_major], MAJOR[b_major],
                          MAJOR[cd_major], DTYPES[ab], DTYPES[c], DTYPES[x],
-                         DTYPES[d], DTYPES[y])
+                         DTYPES[d], DTYPES[y], EPILOGUES[epilogue])
 
 
 def gemm_epi_create(desc: gemm_epi_desc) -> int:
@@ -163,10 +168,11 @@ class FusedGemm:
     """
 
     def __init__(self, M, N, K, L=1, *, ab="f16", a_major="K", b_major="K",
-                 cd_major="N", c=None, x=None, d="f32", y=None, variant=-1):
+                 cd_major="N", c=None, x=None, d="f32", y=None, variant=-1,
+                 epilogue="linear"):
         self.desc = make_desc(M, N, K, L, ab=ab, a_major=a_major,
                               b_major=b_major, cd_major=cd_major, c=c, x=x,
-                              d=d, y=y)
+                              d=d, y=y, epilogue=epilogue)
         self.shape = (M, N, K, L)
         self.handle = (gemm_epi_create(self.desc) if variant == -1
                        else gemm_epi_create_variant(self.desc, variant))

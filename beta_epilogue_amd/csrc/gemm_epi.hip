@@ -43,6 +43,7 @@ struct Variant {
   int b_major;
   int cd_major;
   int bm, bn, bk, threads, lds;
+  int blk;         // MFMA output block (16 or 32)
   launch_fn launch;
 };
 
@@ -59,6 +60,7 @@ constexpr Variant make_variant(const char* name) {
                  CF::BK,
                  CF::THREADS,
                  CF::LDS_BYTES,
+                 CF::BLK,
                  &gemm_epi::launch<CF>};
 }
 
@@ -126,6 +128,8 @@ static int validate_desc(const gemm_epi_desc* d) {
     return fail(GEMM_EPI_ERR_INVALID_ARG, "b_major must be K or N");
   if (d->cd_major != GEMM_EPI_MAJOR_N && d->cd_major != GEMM_EPI_MAJOR_M)
     return fail(GEMM_EPI_ERR_INVALID_ARG, "cd_major must be N or M");
+  if (d->epilogue != GEMM_EPI_LINEAR && d->epilogue != GEMM_EPI_RELU)
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "epilogue must be LINEAR or RELU (got %d)", d->epilogue);
   const int ab = d->ab_dtype;
   if (ab != GEMM_EPI_F16 && ab != GEMM_EPI_BF16 && ab != GEMM_EPI_E4M3 && ab != GEMM_EPI_I8)
     return fail(GEMM_EPI_ERR_INVALID_ARG, "ab_dtype must be F16, BF16, E4M3 or I8");
@@ -164,6 +168,18 @@ static bool variant_fits(const Variant& v, const gemm_epi_desc* d) {
          v.cd_major == d->cd_major;
 }
 
+// Problems the one-type epilogue cannot take: C/X/D/Y of different element
+// types, or a leading extent too long for its 31-bit offsets.  They run the
+// general epilogue, which is only used with 32x32 MFMA blocks: with 16x16
+// blocks it gave wrong values at a ragged N edge (the cause is not found), so
+// those variants refuse such problems instead.
+static bool needs_general_epilogue(const gemm_epi_desc* d) {
+  for (int t : {d->c_dtype, d->x_dtype, d->y_dtype})
+    if (t != GEMM_EPI_NONE && t != d->d_dtype) return true;
+  const int64_t ld = d->cd_major == GEMM_EPI_MAJOR_N ? d->N : d->M;
+  return (int64_t)256 * ld * 4 >= (int64_t(1) << 31);
+}
+
 extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
                                        gemm_epi_handle** out) {
   g_last_error[0] = 0;
@@ -173,9 +189,10 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   if (rc) return rc;
   if (variant < -1 || variant >= kNumVariants)
     return fail(GEMM_EPI_ERR_INVALID_ARG, "variant %d out of range", variant);
+  const bool general = needs_general_epilogue(desc);
   if (variant == -1) {
     for (int i = 0; i < kNumVariants; ++i)
-      if (variant_fits(kVariants[i], desc)) {
+      if (variant_fits(kVariants[i], desc) && (!general || kVariants[i].blk == 32)) {
         variant = i;
         break;
       }
@@ -185,6 +202,10 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
                   desc->ab_dtype, desc->a_major, desc->b_major, desc->cd_major);
   } else if (!variant_fits(kVariants[variant], desc)) {
     return fail(GEMM_EPI_ERR_UNSUPPORTED, "variant %s cannot run this problem",
+                kVariants[variant].name);
+  } else if (general && kVariants[variant].blk != 32) {
+    return fail(GEMM_EPI_ERR_UNSUPPORTED,
+                "variant %s (16x16 blocks) has no mixed-type epilogue; use a 32x32 variant",
                 kVariants[variant].name);
   }
   const Variant& v = kVariants[variant];
@@ -241,6 +262,11 @@ extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void*
   if (use_x && !X) return fail(GEMM_EPI_ERR_INVALID_ARG, "X is NULL but x_factor != 0");
   if ((d.y_dtype != GEMM_EPI_NONE) != (Y != nullptr))
     return fail(GEMM_EPI_ERR_INVALID_ARG, "Y must be given exactly when y_dtype is set");
+  // In place: D may be C itself (same type); other shared pointers are errors.
+  if (D == C && C && !(use_c && d.c_dtype == d.d_dtype))
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "D may alias C only when C is read and has D's dtype");
+  if ((X && (D == X || Y == X)) || (Y && (Y == C || Y == D)))
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "outputs may not alias X, each other, or C (Y)");
   for (const void* ptr : {A, B, (const void*)D, use_c ? C : nullptr, use_x ? X : nullptr,
                           (const void*)Y})
     if (((uintptr_t)ptr) & 15u) return fail(GEMM_EPI_ERR_ALIGNMENT, "pointer %p is not 16-byte aligned", ptr);
@@ -279,6 +305,7 @@ extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void*
   p.ibeta = int_path ? (int32_t)beta : 0;
   p.ix = int_path ? (int32_t)x_factor : 0;
   p.xcd_remap = (h->grid % 8 == 0) ? 1 : 0;
+  p.relu = d.epilogue == GEMM_EPI_RELU ? 1 : 0;
   // Element type shared by every C/X/D/Y in use (typed epilogue), else 0.
   // The typed epilogue addresses a wave's output region (at most a tile's
   // BM or BN lines of the leading extent) with 31-bit byte offsets.
@@ -289,6 +316,8 @@ extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void*
   const int64_t ld = d.cd_major == GEMM_EPI_MAJOR_N ? d.N : d.M;
   if ((int64_t)(v.bm > v.bn ? v.bm : v.bn) * ld * 4 >= (int64_t(1) << 31)) kind = 0;
   p.epi_kind = kind;
+  if (kind == 0 && v.blk != 32)  // (create() routes these problems elsewhere)
+    return fail(GEMM_EPI_ERR_UNSUPPORTED, "variant %s has no mixed-type epilogue", v.name);
 
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   kVariants[h->variant].launch(p, h->grid, (hipStream_t)stream);

@@ -67,6 +67,7 @@ struct Params {
   int32_t ialpha, ibeta, ix;  // integral scalars for int32 outputs
   int32_t xcd_remap;          // grid is a multiple of 8: remap ids per XCD
   int32_t epi_kind;           // element type shared by every C/X/D/Y in use (0: mixed)
+  int32_t relu;               // D = max(0, alpha*acc + beta*C) + x_factor*X
 };
 
 // ---------------------------------------------------------------------------
@@ -558,12 +559,24 @@ __device__ __forceinline__ void store4_f(void* p, int dt, int64_t i, v4f v) {
 
 // Element work for four contiguous outputs at flat index o, given the four
 // accumulator values w and the four C and X values already loaded.
+// The clamp of the ReLU form: max(0, v), a NaN becoming 0; for int32 the
+// signed value of the wrapped sum.
+__device__ __forceinline__ v4f relu4(v4f t) {
+  return v4f{t.x > 0.0f ? t.x : 0.0f, t.y > 0.0f ? t.y : 0.0f, t.z > 0.0f ? t.z : 0.0f,
+             t.w > 0.0f ? t.w : 0.0f};
+}
+__device__ __forceinline__ v4u relu4(v4u t) {
+  return v4u{(int)t.x > 0 ? t.x : 0u, (int)t.y > 0 ? t.y : 0u, (int)t.z > 0 ? t.z : 0u,
+             (int)t.w > 0 ? t.w : 0u};
+}
+
 template <class CF>
 __device__ __forceinline__ void epi_finish4(const Params& p, int64_t o, v4f w, v4f c, v4f x) {
   if constexpr (CF::AB == T_I8) {
     const v4u a = __builtin_bit_cast(v4u, w);
     v4u t = a * (unsigned)p.ialpha;
     if (p.c_dtype) t += __builtin_bit_cast(v4u, c) * (unsigned)p.ibeta;
+    if (p.relu) t = relu4(t);
     if (p.x_dtype) t += __builtin_bit_cast(v4u, x) * (unsigned)p.ix;
     __builtin_nontemporal_store(t, (v4u*)((int*)p.D + o));
     if (p.y_dtype) __builtin_nontemporal_store(a, (v4u*)((int*)p.Y + o));
@@ -575,6 +588,7 @@ __device__ __forceinline__ void epi_finish4(const Params& p, int64_t o, v4f w, v
       t.z = __builtin_fmaf(p.beta, c.z, t.z);
       t.w = __builtin_fmaf(p.beta, c.w, t.w);
     }
+    if (p.relu) t = relu4(t);
     if (p.x_dtype) {
       t.x = __builtin_fmaf(p.xf, x.x, t.x);
       t.y = __builtin_fmaf(p.xf, x.y, t.y);
@@ -834,11 +848,14 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
     const uint32_t o = off(i);
     if constexpr (T == T_I32) {
       const v4u a = __builtin_bit_cast(v4u, w0);
-      const v4u t = a * (unsigned)p.ialpha + cr[S] * (unsigned)p.ibeta + xr[S] * (unsigned)p.ix;
+      v4u t = a * (unsigned)p.ialpha + cr[S] * (unsigned)p.ibeta;
+      if (p.relu) t = relu4(t);
+      t += xr[S] * (unsigned)p.ix;
       epi_st<T>(rd, o, t);
       epi_st<T>(ry, o, a);
     } else {
-      // D = alpha * acc + beta * C + x_factor * X, in this order
+      // D = alpha * acc + beta * C (clamped at 0 in the ReLU form) + x_factor * X,
+      // in this order
       auto fin = [&](v4f w, int h) {
         const v4f c = epi_dec<T>(cr[S], h), x = epi_dec<T>(xr[S], h);
         v4f t = w * p.alpha;
@@ -846,6 +863,7 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
         t.y = __builtin_fmaf(beta, c.y, t.y);
         t.z = __builtin_fmaf(beta, c.z, t.z);
         t.w = __builtin_fmaf(beta, c.w, t.w);
+        if (p.relu) t = relu4(t);
         t.x = __builtin_fmaf(xf, x.x, t.x);
         t.y = __builtin_fmaf(xf, x.y, t.y);
         t.z = __builtin_fmaf(xf, x.z, t.z);

@@ -10,8 +10,15 @@
  * A is M x K x L, B is N x K x L, C, X, D and Y are M x N x L.  Inputs are
  * fp16, bf16, fp8 (OCP e4m3fn) or int8; accumulation is fp32, or int32 for
  * int8.  The epilogue runs in fp32 (int32 for int8) on the unrounded
- * accumulator and rounds to nearest-even into the output types.  No ReLU is
- * applied: the docstring's formula has none.
+ * accumulator and rounds to nearest-even into the output types.  By default
+ * no ReLU is applied (the docstring's formula has none).  The desc field
+ * `epilogue` selects instead the form the example's epilogue function builds
+ * (same file, the `epilogue` function passed to the GEMM object):
+ *
+ *     D[l] = max(0, alpha * (A[l] . B[l]^T) + beta * C[l]) + x_factor * X[l]
+ *
+ * (a NaN in the clamped sum becomes 0; with int32 outputs the clamp is of the
+ * wrapped int32 sum).
  *
  * Conventions (taken from the Blackwell pipeline API card, "Host side" and
  * "Device side", and the CuTe DSL example's "Constraints"):
@@ -69,6 +76,9 @@ enum {
 /* Majorness: the contiguous mode of a tensor (see the table above). */
 enum { GEMM_EPI_MAJOR_K = 0, GEMM_EPI_MAJOR_M = 1, GEMM_EPI_MAJOR_N = 2 };
 
+/* Epilogue form (see the formulas above). */
+enum { GEMM_EPI_LINEAR = 0, GEMM_EPI_RELU = 1 };
+
 typedef struct gemm_epi_desc {
   int64_t M, N, K, L;  /* all >= 1 */
   int32_t a_major;     /* GEMM_EPI_MAJOR_K or _M */
@@ -79,6 +89,7 @@ typedef struct gemm_epi_desc {
   int32_t x_dtype;     /* as c_dtype */
   int32_t d_dtype;     /* F16/BF16/F32 (float A/B) or I32 (int8 A/B) */
   int32_t y_dtype;     /* NONE, or as d_dtype */
+  int32_t epilogue;    /* GEMM_EPI_LINEAR (0) or GEMM_EPI_RELU */
 } gemm_epi_desc;
 
 typedef struct gemm_epi_handle gemm_epi_handle;
@@ -126,8 +137,11 @@ int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
  * alpha, beta, x_factor : fp32 scalars.  With int32 outputs they must be
  *            integers of magnitude <= 2^24 (the epilogue is then exact int32
  *            arithmetic), else GEMM_EPI_ERR_UNSUPPORTED.
- * Every pointer must be 16-byte aligned.  Outputs must not overlap inputs;
- * C and X are never written.  Checks happen before anything is enqueued;
+ * Every pointer must be 16-byte aligned.  D may be C itself (the same
+ * pointer, with d_dtype == c_dtype): an in-place update, since each output
+ * element's C is read before its D is written by the same lane.  No other
+ * overlap of an output with an input or with the other output is allowed; X
+ * is never written, nor C unless it is D.  Checks happen before anything is enqueued;
  * GEMM_EPI_ERR_LAUNCH reports a failed launch.  Faults inside the kernel
  * surface at the caller's next synchronisation.  Thread-safe.
  */

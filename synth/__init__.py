@@ -47,6 +47,7 @@ class Problem:
     dist_c: str = "normal"
     dist_x: str = "normal"
     seed: int = 0
+    epilogue: str = "linear"  # or "relu": D = max(0, alpha*Y + beta*C) + x_factor*X
 
     @property
     def flops(self) -> int:

@@ -68,7 +68,7 @@ def run_gpu(p: synth.Problem, ins, variant=-1, check_inputs=True):
     keep = {k: v.clone() for k, v in dev.items() if v is not None and k in "CX"}
     g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, a_major=p.a_major,
                      b_major=p.b_major, cd_major=p.cd_major, c=p.c, x=p.x,
-                     d=p.d, y=p.y, variant=variant)
+                     d=p.d, y=p.y, variant=variant, epilogue=p.epilogue)
     shape = p.storage_shape("D")
     D = GuardedOut(p.d, shape)
     Y = GuardedOut(p.y, shape) if p.y else None
@@ -141,7 +141,8 @@ def parity_full(p: synth.Problem, variant=-1, exact=False, ins=None):
                                     ins["C"], ins["X"], ab=p.ab, c=p.c, x=p.x,
                                     a_major=p.a_major, b_major=p.b_major,
                                     cd_major=p.cd_major, alpha=p.alpha,
-                                    beta=p.beta, x_factor=p.x_factor)
+                                    beta=p.beta, x_factor=p.x_factor,
+                                    relu=p.epilogue == "relu")
     cv = to_f64(ins["C"]) if ins["C"] is not None else None
     xv = to_f64(ins["X"]) if ins["X"] is not None else None
     errs = check(p, D.reshape(-1), Y.reshape(-1) if Y is not None else None,
@@ -180,7 +181,8 @@ def parity_sampled(p: synth.Problem, variant=-1, n_random=2048, ins=None):
     Dref, Yref, S = oracle.gemm_epi_points(
         p.M, p.N, p.K, p.L, ins["A"], ins["B"], ins["C"], ins["X"], points=pts,
         ab=p.ab, c=p.c, x=p.x, a_major=p.a_major, b_major=p.b_major,
-        cd_major=p.cd_major, alpha=p.alpha, beta=p.beta, x_factor=p.x_factor)
+        cd_major=p.cd_major, alpha=p.alpha, beta=p.beta, x_factor=p.x_factor,
+        relu=p.epilogue == "relu")
     idx = flat_index(p, pts)
     cv = to_f64(ins["C"])[idx] if ins["C"] is not None else None
     xv = to_f64(ins["X"])[idx] if ins["X"] is not None else None

@@ -81,7 +81,96 @@ EDGE = [
     # N-major f16 C/X/D/Y with both tile extents cut: 8-element lane groups
     # past N and rows past M
     CFG[2].replace(name="f16_ragged_mn", M=300, N=392, K=96, seed=7000),
+    # mixed C/X/D/Y types (general epilogue, routed to 32x32 blocks), ragged N
+    CFG[1].replace(name="mixed_types_ragged", M=300, N=264, K=128, c="f32", x="bf16",
+                   y="bf16", x_factor=0.5, seed=7060),
 ]
+
+
+# The ReLU form D = max(0, alpha*A.B^T + beta*C) + x_factor*X: mixed-sign
+# sums so both sides of the clamp occur; typed epilogues (f16, f32, int32)
+# and the mixed-type one, both majornesses.
+RELU = [
+    small(CFG[2], 600, 520, 392).replace(name="relu_f16_cxdy", epilogue="relu", seed=7200),
+    small(CFG[2], 264, 392, 136).replace(name="relu_f16_mmajor", cd_major="M",
+                                         epilogue="relu", seed=7300),
+    small(CFG[1], 592, 528, 392).replace(name="relu_bf16_f32", alpha=1.0, beta=-1.0,
+                                         epilogue="relu", seed=7400),
+    small(CFG[3], 592, 528, 400, L=2).replace(name="relu_i8_mmajorA", beta=-1.0,
+                                              epilogue="relu", seed=7500),
+    CFG[3].replace(name="relu_i8_kmajor_xy", M=260, N=264, K=160, L=1, a_major="K",
+                   x="i32", y="i32", alpha=-3.0, beta=2.0, x_factor=5.0, dist_x="i1000",
+                   epilogue="relu", seed=7600),
+    CFG[4].replace(name="relu_e4m3_mixed", M=260, N=264, K=256, x="bf16", y="f32",
+                   x_factor=-1.5, beta=-1.0, epilogue="relu", seed=7700),
+]
+
+
+@pytest.mark.parametrize("p", RELU, ids=[e.name for e in RELU])
+def test_parity_relu(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
+    (ed, ey), plan = parity_full(p)
+    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_parity_relu_full_size_sampled():
+    """The 8192^3 fp16 workload in the ReLU form, at the bench's launch."""
+    p = CFG[2].replace(name="f16_8192_fused_cxdy_relu", epilogue="relu")
+    (ed, ey), plan, npts = parity_sampled(p)
+    _say("  plan", plan["name"], "points", npts, "err D %.3g Y %.3g" % (ed, ey))
+
+
+# D == C in place: bit-identical to the out-of-place run and to the oracle's
+# bound, for a typed (f16, int32) and the mixed-type epilogue.
+INPLACE = [
+    small(CFG[2], 600, 520, 392).replace(name="inplace_f16", seed=7800),
+    small(CFG[2], 264, 392, 136).replace(name="inplace_f16_relu_mmajor", cd_major="M",
+                                         epilogue="relu", seed=7850),
+    small(CFG[3], 592, 528, 400, L=2).replace(name="inplace_i32", seed=7900),
+    CFG[1].replace(name="inplace_mixed", M=300, N=264, K=128, d="f32", c="f32", x="bf16",
+                   x_factor=0.5, seed=7950),
+]
+
+
+@pytest.mark.parametrize("p", INPLACE, ids=[e.name for e in INPLACE])
+def test_inplace_d_is_c(p):
+    import beta_epilogue_amd as ge
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
+    ins = synth.make_inputs(p)
+    D_out, Y_out, _ = run_gpu(p, ins)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in ins.items()}
+    g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, a_major=p.a_major, b_major=p.b_major,
+                     cd_major=p.cd_major, c=p.c, x=p.x, d=p.d, y=p.y, epilogue=p.epilogue)
+    CD = dev["C"].clone()
+    Y = torch.empty_like(Y_out, device="cuda") if p.y else None
+    g(dev["A"], dev["B"], CD, dev["X"], D=CD, Y=Y, alpha=p.alpha, beta=p.beta,
+      x_factor=p.x_factor)
+    torch.cuda.synchronize()
+    g.close()
+    assert torch.equal(CD.cpu().view(torch.uint8), D_out.view(torch.uint8)), "in place != out of place"
+    if p.y:
+        assert torch.equal(Y.cpu().view(torch.uint8), Y_out.view(torch.uint8))
+    (ed, ey), _ = parity_full(p, ins=ins)
+    _say("  err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_aliasing_rules():
+    import beta_epilogue_amd as ge
+    p = small(CFG[2], 256, 256, 64)
+    ins = synth.make_inputs(p)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in ins.items()}
+    g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, c=p.c, x=p.x, d=p.d, y=p.y)
+    D = torch.empty_like(dev["C"])
+    for kw in (dict(D=dev["X"], Y=D), dict(D=D, Y=dev["C"]), dict(D=D, Y=D)):
+        with pytest.raises(ge.GemmEpiError) as e:
+            g(dev["A"], dev["B"], dev["C"], dev["X"], alpha=p.alpha, beta=p.beta,
+              x_factor=p.x_factor, **kw)
+        assert e.value.code == ge.GEMM_EPI_ERR_INVALID_ARG
+    # D == C with beta == 0 (C not read) is not an in-place update
+    with pytest.raises(ge.GemmEpiError):
+        g(dev["A"], dev["B"], dev["C"], dev["X"], D=dev["C"], Y=D, alpha=1.0, beta=0.0,
+          x_factor=p.x_factor)
+    g.close()
 
 
 @pytest.mark.parametrize("p", EDGE, ids=[e.name for e in EDGE])
@@ -148,9 +237,10 @@ def test_run_rejects_misaligned_pointer():
     g = ge.FusedGemm(p.M, p.N, p.K, ab="f16", c="f16", x="f16", d="f16", y="f16")
     a = torch.zeros(64 * 64 + 8, dtype=torch.float16, device="cuda")
     d = torch.zeros(64 * 64, dtype=torch.float16, device="cuda")
+    y = torch.zeros(64 * 64, dtype=torch.float16, device="cuda")
     with pytest.raises(ge.GemmEpiError) as e:
         ge.gemm_epi_run(g.handle, a.data_ptr() + 2, a.data_ptr(), None, None,
-                        d.data_ptr(), d.data_ptr(), 1.0, 0.0, 0.0, None)
+                        d.data_ptr(), y.data_ptr(), 1.0, 0.0, 0.0, None)
     assert e.value.code == ge.GEMM_EPI_ERR_ALIGNMENT
     with pytest.raises(ge.GemmEpiError) as e:  # Y required: y_dtype is set
         ge.gemm_epi_run(g.handle, a.data_ptr(), a.data_ptr(), None, None,
