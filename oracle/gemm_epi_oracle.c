@@ -20,7 +20,7 @@
  *
  *     D[l,m,n] = max(0, alpha * Y[l,m,n] + beta * C[l,m,n]) + x_factor * X[l,m,n]
  *
- * A is M x K x L, B is N x K x L (so the product is A times B-transposed in
+ * Inputs: fp16, bf16, OCP fp8 E4M3 and E5M2, int8.  A is M x K x L, B is N x K x L (so the product is A times B-transposed in
  * row-major algebra), C/X/D/Y are M x N x L.  Every stored element is decoded
  * exactly to double, the contraction runs in double in ascending k, and the
  * epilogue is applied in double to the unrounded sum.  Nothing is rounded to
@@ -55,7 +55,8 @@ enum {
   ORC_E4M3 = 3, /* OCP fp8 E4M3FN: bias 7, no infinities, S.1111.111 is NaN */
   ORC_I8 = 4,
   ORC_F32 = 5,
-  ORC_I32 = 6
+  ORC_I32 = 6,
+  ORC_E5M2 = 7 /* OCP fp8 E5M2: bias 15, IEEE-like infinities and NaNs */
 };
 
 typedef struct {
@@ -104,6 +105,18 @@ static double dec_e4m3(uint8_t b) {
   return s ? -v : v;
 }
 
+static double dec_e5m2(uint8_t b) {
+  int s = b >> 7, e = (b >> 2) & 31, f = b & 3;
+  double v;
+  if (e == 31)
+    v = (f == 0) ? INFINITY : NAN;
+  else if (e == 0)
+    v = ldexp((double)f, -16); /* f/2^2 * 2^-14 */
+  else
+    v = ldexp((double)(4 + f), e - 17); /* (1+f/2^2) * 2^(e-15) */
+  return s ? -v : v;
+}
+
 static double dec_f32(uint32_t w) {
   float f;
   memcpy(&f, &w, sizeof f);
@@ -115,6 +128,7 @@ static double load(const void* p, int type, int64_t i) {
     case ORC_F16: return dec_f16(((const uint16_t*)p)[i]);
     case ORC_BF16: return dec_bf16(((const uint16_t*)p)[i]);
     case ORC_E4M3: return dec_e4m3(((const uint8_t*)p)[i]);
+    case ORC_E5M2: return dec_e5m2(((const uint8_t*)p)[i]);
     case ORC_I8: return (double)((const int8_t*)p)[i];
     case ORC_F32: return dec_f32(((const uint32_t*)p)[i]);
     case ORC_I32: return (double)((const int32_t*)p)[i];
@@ -124,7 +138,7 @@ static double load(const void* p, int type, int64_t i) {
 
 /* Decode n stored elements to double (exposed so tests can pin decoding). */
 int orc_decode(int type, const void* src, int64_t n, double* out) {
-  if (type < ORC_F16 || type > ORC_I32 || (n > 0 && (!src || !out))) return 1;
+  if (type < ORC_F16 || type > ORC_E5M2 || (n > 0 && (!src || !out))) return 1;
   for (int64_t i = 0; i < n; ++i) out[i] = load(src, type, i);
   return 0;
 }
@@ -238,7 +252,7 @@ static int run_threads(const orc_problem* p, int64_t items, int mode,
 static int check_desc(const orc_desc* d, const void* A, const void* B) {
   if (!d || !A || !B) return 1;
   if (d->M < 0 || d->N < 0 || d->K < 0 || d->L < 0) return 1;
-  if (d->ab_type < ORC_F16 || d->ab_type > ORC_I8) return 1;
+  if ((d->ab_type < ORC_F16 || d->ab_type > ORC_I8) && d->ab_type != ORC_E5M2) return 1;
   return 0;
 }
 

@@ -19,9 +19,10 @@ import torch
 
 TORCH_DTYPE = {
     "f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn,
+    "e5m2": torch.float8_e5m2,
     "i8": torch.int8, "f32": torch.float32, "i32": torch.int32,
 }
-ELEM_BYTES = {"f16": 2, "bf16": 2, "e4m3": 1, "i8": 1, "f32": 4, "i32": 4}
+ELEM_BYTES = {"f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1, "i8": 1, "f32": 4, "i32": 4}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -121,6 +122,22 @@ def e4m3_table() -> torch.Tensor:
     return _E4M3_TABLE
 
 
+_E5M2_TABLE = None
+
+
+def e5m2_table() -> torch.Tensor:
+    """All distinct finite e5m2 values with |v| <= 4 (-0 folded into 0),
+    found by decoding every one of the 256 codes with torch."""
+    global _E5M2_TABLE
+    if _E5M2_TABLE is None:
+        codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+        vals = codes.view(torch.float8_e5m2).to(torch.float32)
+        keep = torch.isfinite(vals) & (vals.abs() <= 4.0)
+        uniq = torch.unique(vals[keep] + 0.0)
+        _E5M2_TABLE = uniq.to(torch.float8_e5m2)
+    return _E5M2_TABLE
+
+
 def draw(dist: str, dtype: str, numel: int, seed: int) -> torch.Tensor:
     """``numel`` stored elements of ``dtype`` from distribution ``dist``."""
     g = torch.Generator(device="cpu")
@@ -147,6 +164,11 @@ def draw(dist: str, dtype: str, numel: int, seed: int) -> torch.Tensor:
         idx = torch.randint(0, tab.numel(), (numel,), generator=g)
         out = tab.view(torch.uint8)[idx].view(torch.float8_e4m3fn)
         return out if td == torch.float8_e4m3fn else out.to(td)
+    if dist == "e5m2tab":  # uniform over the finite e5m2 values with |v| <= 4
+        tab = e5m2_table()
+        idx = torch.randint(0, tab.numel(), (numel,), generator=g)
+        out = tab.view(torch.uint8)[idx].view(torch.float8_e5m2)
+        return out if td == torch.float8_e5m2 else out.to(td)
     if dist == "small":  # integers in [-3, 3] scaled by 1/4: exact everywhere
         v = torch.randint(-3, 4, (numel,), generator=g, dtype=torch.int32)
         return (v.to(torch.float32) * 0.25).to(td)

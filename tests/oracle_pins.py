@@ -28,7 +28,7 @@ import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "number_formats.txt")
 
-FLOAT_AB = ("f16", "bf16", "e4m3")
+FLOAT_AB = ("f16", "bf16", "e4m3", "e5m2")
 ALL_AB = FLOAT_AB + ("i8",)
 LAYOUTS = [(a, b, cd) for a in "KM" for b in "KN" for cd in "NM"]
 
@@ -100,7 +100,7 @@ def _rand(dist, dtype, shape, seed):
 
 
 def _dist_for(ab):
-    return {"f16": "normal", "bf16": "normal", "e4m3": "e4m3tab",
+    return {"f16": "normal", "bf16": "normal", "e4m3": "e4m3tab", "e5m2": "e5m2tab",
             "i8": "i8full"}[ab]
 
 
@@ -117,7 +117,7 @@ def pin_decode_golden(orc):
                 continue
             typ, code, val = line.split()[:3]
             code = int(code, 16)
-            arr = np.array([code], dtype=np.uint16 if typ != "e4m3" else np.uint8)
+            arr = np.array([code], dtype=np.uint8 if typ in ("e4m3", "e5m2") else np.uint16)
             got = orc.decode(typ, arr)[0]
             want = _parse_value(val)
             if math.isnan(want):
@@ -138,11 +138,13 @@ def pin_decode_vs_library(orc):
         assert np.array_equal(got[~nan], want[~nan]), typ
         assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan])), typ
     codes8 = torch.arange(256, dtype=torch.int32).to(torch.uint8)
-    got = orc.decode("e4m3", codes8.numpy())
-    want = lib_decode(codes8.view(torch.float8_e4m3fn))
-    nan = np.isnan(want)
-    assert np.array_equal(np.isnan(got), nan)
-    assert np.array_equal(got[~nan], want[~nan])
+    for typ, td in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        got = orc.decode(typ, codes8.numpy())
+        want = lib_decode(codes8.view(td))
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan), typ
+        assert np.array_equal(got[~nan], want[~nan]), typ
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan])), typ
     i8 = np.arange(-128, 128, dtype=np.int8)
     assert np.array_equal(orc.decode("i8", i8), i8.astype(np.float64))
     i32 = np.array([0, 1, -1, 2**31 - 1, -2**31, 123456789], dtype=np.int32)
@@ -173,7 +175,7 @@ def pin_bruteforce_exact(orc):
                 alpha, beta, xf = 3.0, -2.0, 5.0
             else:
                 c, x = {"f16": ("f32", "f16"), "bf16": ("bf16", "f32"),
-                        "e4m3": ("f16", "bf16")}[ab]
+                        "e4m3": ("f16", "bf16"), "e5m2": ("bf16", "f16")}[ab]
                 Cl = _rand("normal", c, (L, M, N), seed + 3)
                 Xl = _rand("normal", x, (L, M, N), seed + 4)
                 alpha, beta, xf = 1.75, -0.625, 2.5
@@ -265,10 +267,12 @@ def pin_all_ones(orc):
 
 
 def pin_rank1(orc):
-    """A[m,k] = u_m p_k and B[n,k] = w_n q_k give Y = (p.q) u_m w_n."""
+    """A[m,k] = u_m p_k and B[n,k] = w_n q_k give Y = (p.q) u_m w_n.  u and w
+    are powers of two, so every product is exact in each input format (e5m2
+    has two fraction bits)."""
     M, N, K, L = 4, 6, 9, 1
-    u = torch.tensor([1.0, -2.0, 0.5, 3.0])
-    w = torch.tensor([2.0, 1.0, -1.0, 0.25, -4.0, 1.5])
+    u = torch.tensor([1.0, -2.0, 0.5, 4.0])
+    w = torch.tensor([2.0, 1.0, -1.0, 0.25, -4.0, 0.5])
     p = torch.tensor([1.0, -1.0, 2.0, 0.5, -0.5, 3.0, 1.0, -2.0, 0.25])
     q = torch.tensor([0.5, 2.0, -1.0, 1.0, 4.0, -0.25, 1.0, 0.5, -3.0])
     pq = float((p.double() * q.double()).sum())

@@ -45,6 +45,9 @@ MUTANTS = [
     ("i8_unsigned", "(double)((const int8_t*)p)[i]", "(double)((const uint8_t*)p)[i]"),
     ("bf16_as_f16", "case ORC_BF16: return dec_bf16(", "case ORC_BF16: return dec_f16("),
     ("points_swap_mn", "element(j->p, q[0], q[1], q[2]", "element(j->p, q[0], q[2], q[1]"),
+    ("e5m2_bias", "ldexp((double)(4 + f), e - 17)", "ldexp((double)(4 + f), e - 16)"),
+    ("e5m2_subnormal", "ldexp((double)f, -16)", "ldexp((double)f, -17)"),
+    ("e5m2_as_e4m3_fields", "e = (b >> 2) & 31, f = b & 3", "e = (b >> 3) & 15, f = b & 7"),
     ("relu_ignored", "if (p->relu && !(out > 0.0)) out = 0.0;", "(void)0;"),
     ("relu_always", "if (p->relu && !(out > 0.0))", "if (!(out > 0.0))"),
     ("relu_keeps_negatives", "if (p->relu && !(out > 0.0)) out = 0.0;",
