@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "TFLOP/s and % of MFMA dense peak, 8192³ fp16 GEMM w/ fused epilogue"
 # MI355X datasheet dense MFMA peaks, TFLOP/s (TOP/s for int8)
-PEAK = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "i8": 5000.0}
+PEAK = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "e5m2": 5000.0, "i8": 5000.0}
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 

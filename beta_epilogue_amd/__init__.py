@@ -26,7 +26,7 @@ GEMM_EPI_ERR_DEVICE = 4
 GEMM_EPI_ERR_LAUNCH = 5
 
 DTYPES = {None: 0, "none": 0, "f16": 1, "bf16": 2, "e4m3": 3, "i8": 4,
-          "f32": 5, "i32": 6}
+          "f32": 5, "i32": 6, "e5m2": 7}
 MAJOR = {"K": 0, "M": 1, "N": 2}
 
 

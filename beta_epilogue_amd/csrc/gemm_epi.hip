@@ -83,6 +83,7 @@ int elem_bytes(int t) {
     case GEMM_EPI_F16:
     case GEMM_EPI_BF16: return 2;
     case GEMM_EPI_E4M3:
+    case GEMM_EPI_E5M2:
     case GEMM_EPI_I8: return 1;
     case GEMM_EPI_F32:
     case GEMM_EPI_I32: return 4;
@@ -131,15 +132,16 @@ static int validate_desc(const gemm_epi_desc* d) {
   if (d->epilogue != GEMM_EPI_LINEAR && d->epilogue != GEMM_EPI_RELU)
     return fail(GEMM_EPI_ERR_INVALID_ARG, "epilogue must be LINEAR or RELU (got %d)", d->epilogue);
   const int ab = d->ab_dtype;
-  if (ab != GEMM_EPI_F16 && ab != GEMM_EPI_BF16 && ab != GEMM_EPI_E4M3 && ab != GEMM_EPI_I8)
-    return fail(GEMM_EPI_ERR_INVALID_ARG, "ab_dtype must be F16, BF16, E4M3 or I8");
+  if (ab != GEMM_EPI_F16 && ab != GEMM_EPI_BF16 && ab != GEMM_EPI_E4M3 && ab != GEMM_EPI_E5M2 &&
+      ab != GEMM_EPI_I8)
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "ab_dtype must be F16, BF16, E4M3, E5M2 or I8");
   const bool int_path = ab == GEMM_EPI_I8;
   auto out_ok = [&](int t, bool allow_none) {
     if (t == GEMM_EPI_NONE) return allow_none;
     return int_path ? t == GEMM_EPI_I32 : is_float_out(t);
   };
   for (int t : {d->c_dtype, d->x_dtype, d->d_dtype, d->y_dtype})
-    if (t < GEMM_EPI_NONE || t > GEMM_EPI_I32)
+    if (t < GEMM_EPI_NONE || t > GEMM_EPI_E5M2)
       return fail(GEMM_EPI_ERR_INVALID_ARG, "unknown dtype code %d", t);
   if (!out_ok(d->c_dtype, true) || !out_ok(d->x_dtype, true) || !out_ok(d->d_dtype, false) ||
       !out_ok(d->y_dtype, true))

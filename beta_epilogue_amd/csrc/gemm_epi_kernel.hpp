@@ -37,7 +37,7 @@
 namespace gemm_epi {
 
 // Element type codes; the same numbers as the public header.
-enum : int { T_NONE = 0, T_F16 = 1, T_BF16 = 2, T_E4M3 = 3, T_I8 = 4, T_F32 = 5, T_I32 = 6 };
+enum : int { T_NONE = 0, T_F16 = 1, T_BF16 = 2, T_E4M3 = 3, T_I8 = 4, T_F32 = 5, T_I32 = 6, T_E5M2 = 7 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -159,6 +159,16 @@ template <> struct Mma<T_E4M3, 16> : MmaLayout16 {
   static constexpr int ESIZE = 1, KSB = 128;
   static __device__ __forceinline__ acc_t mma(frag_t a, frag_t b, acc_t c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+
+// Format selectors 1/1 = fp8 e5m2 (bf8) for both operands.
+template <> struct Mma<T_E5M2, 32> : MmaLayout32 {
+  typedef v16f acc_t;
+  typedef v8i frag_t;
+  static constexpr int ESIZE = 1, KSB = 64;
+  static __device__ __forceinline__ acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 1, 1, 0, 0, 0, 0);
   }
 };
 

@@ -8,7 +8,7 @@
  *     D[l] = alpha * (A[l] . B[l]^T) + beta * C[l] + x_factor * X[l]
  *
  * A is M x K x L, B is N x K x L, C, X, D and Y are M x N x L.  Inputs are
- * fp16, bf16, fp8 (OCP e4m3fn) or int8; accumulation is fp32, or int32 for
+ * fp16, bf16, fp8 (OCP e4m3fn or e5m2) or int8; accumulation is fp32, or int32 for
  * int8.  The epilogue runs in fp32 (int32 for int8) on the unrounded
  * accumulator and rounds to nearest-even into the output types.  By default
  * no ReLU is applied (the docstring's formula has none).  The desc field
@@ -70,7 +70,8 @@ enum {
   GEMM_EPI_E4M3 = 3, /* OCP fp8 e4m3fn (A/B only) */
   GEMM_EPI_I8 = 4,   /* int8 (A/B only) */
   GEMM_EPI_F32 = 5,  /* binary32 (C/X/D/Y only) */
-  GEMM_EPI_I32 = 6   /* int32 (C/X/D/Y only, with int8 inputs) */
+  GEMM_EPI_I32 = 6,  /* int32 (C/X/D/Y only, with int8 inputs) */
+  GEMM_EPI_E5M2 = 7  /* OCP fp8 e5m2 (A/B only) */
 };
 
 /* Majorness: the contiguous mode of a tensor (see the table above). */
@@ -84,7 +85,7 @@ typedef struct gemm_epi_desc {
   int32_t a_major;     /* GEMM_EPI_MAJOR_K or _M */
   int32_t b_major;     /* GEMM_EPI_MAJOR_K or _N */
   int32_t cd_major;    /* GEMM_EPI_MAJOR_N or _M: C, X, D and Y alike */
-  int32_t ab_dtype;    /* F16, BF16, E4M3 or I8 */
+  int32_t ab_dtype;    /* F16, BF16, E4M3, E5M2 or I8 */
   int32_t c_dtype;     /* NONE, or F16/BF16/F32 (float A/B), I32 (int8 A/B) */
   int32_t x_dtype;     /* as c_dtype */
   int32_t d_dtype;     /* F16/BF16/F32 (float A/B) or I32 (int8 A/B) */

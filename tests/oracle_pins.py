@@ -39,7 +39,7 @@ LAYOUTS = [(a, b, cd) for a in "KM" for b in "KN" for cd in "NM"]
 
 def lib_decode(t: torch.Tensor) -> np.ndarray:
     """Library decode: torch's own conversion of the stored type to float64."""
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
         return t.to(torch.float32).to(torch.float64).reshape(-1).numpy()
     return t.to(torch.float64).reshape(-1).numpy()
 

@@ -32,7 +32,7 @@ def tolerance(dtype: str, ab: str = "f16") -> float:
     16-bit bar even for fp32 outputs: the fp8 MFMA sums each group of
     products with about 14 fraction bits (measured: 1 + 2^-15 -> 1,
     448^2 + 1 -> 200704), up to ~2.2e-4 of sum|a||b| at K = 64."""
-    if ab == "e4m3" and dtype == "f32":
+    if ab in ("e4m3", "e5m2") and dtype == "f32":
         return 1e-3
     return {"f32": 1e-5, "f16": 1e-3, "bf16": 2.0 ** -8}[dtype]
 
@@ -40,7 +40,7 @@ def tolerance(dtype: str, ab: str = "f16") -> float:
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Library decode of stored values (torch's conversion) to float64."""
     t = t.detach().cpu().reshape(-1)
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
         t = t.to(torch.float32)
     return t.to(torch.float64).numpy()
 

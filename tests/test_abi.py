@@ -73,6 +73,7 @@ BAD = [
     (dict(ab="i8"), ge.GEMM_EPI_ERR_UNSUPPORTED),                 # int8 needs int32 outs
     (dict(ab="f16", d="i32"), ge.GEMM_EPI_ERR_UNSUPPORTED),
     (dict(ab="f16", c="e4m3"), ge.GEMM_EPI_ERR_UNSUPPORTED),
+    (dict(ab="e5m2", d="e5m2"), ge.GEMM_EPI_ERR_UNSUPPORTED),     # fp8 is A/B only
     (dict(d=None), ge.GEMM_EPI_ERR_UNSUPPORTED),                  # D required
     (dict(K=100), ge.GEMM_EPI_ERR_ALIGNMENT),                     # 200 B rows
     (dict(N=100), ge.GEMM_EPI_ERR_ALIGNMENT),                     # f16 C/D rows

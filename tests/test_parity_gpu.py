@@ -173,6 +173,33 @@ def test_aliasing_rules():
     g.close()
 
 
+# fp8 e5m2 A/B (format selectors 1/1 of the f8f6f4 MFMA): the e4m3 workload's
+# shapes and outputs with e5m2 values of |v| <= 4.
+E5M2 = [
+    small(CFG[4], 600, 528, 400).replace(name="e5m2_f16out", ab="e5m2", dist_ab="e5m2tab",
+                                         seed=8100),
+    CFG[4].replace(name="e5m2_mmajor_cd", M=264, N=296, K=160, cd_major="M", ab="e5m2",
+                   dist_ab="e5m2tab", seed=8200),
+    CFG[4].replace(name="e5m2_f32_xy", M=260, N=264, K=256, d="f32", c="f32", x="bf16",
+                   y="f32", x_factor=-1.5, ab="e5m2", dist_ab="e5m2tab", seed=8300),
+    CFG[4].replace(name="e5m2_relu", M=260, N=264, K=256, ab="e5m2", dist_ab="e5m2tab",
+                   beta=-1.0, epilogue="relu", seed=8400),
+]
+
+
+@pytest.mark.parametrize("p", E5M2, ids=[e.name for e in E5M2])
+def test_parity_e5m2(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
+    (ed, ey), plan = parity_full(p)
+    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_parity_e5m2_full_size_sampled():
+    p = CFG[4].replace(name="e5m2_8192_f16out", ab="e5m2", dist_ab="e5m2tab", seed=8500)
+    (ed, ey), plan, npts = parity_sampled(p)
+    _say("  plan", plan["name"], "points", npts, "err D %.3g Y %.3g" % (ed, ey))
+
+
 @pytest.mark.parametrize("p", EDGE, ids=[e.name for e in EDGE])
 def test_parity_edge_cases(p):
     _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
@@ -200,6 +227,7 @@ def test_every_variant_runs():
         "f16": CFG[2].replace(M=264, N=272, K=136, L=2),
         "bf16": CFG[1].replace(M=264, N=272, K=136, L=2),
         "e4m3": CFG[4].replace(M=264, N=272, K=144, L=2),
+        "e5m2": CFG[4].replace(M=264, N=272, K=144, L=2, ab="e5m2", dist_ab="e5m2tab"),
         "i8": CFG[3].replace(M=272, N=264, K=144, L=2),
     }
     for i, name in enumerate(names):
