@@ -152,7 +152,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
-            print("bench.py: this build runs on one GPU only (the GEMM is sharded "
+            print("bench.py runs on one GPU only (the GEMM is sharded "
                   "by output tiles with no exchange; see the design notes); "
                   "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
