@@ -43,7 +43,8 @@ class _Desc(ctypes.Structure):
                 ("K", ctypes.c_int64), ("L", ctypes.c_int64),
                 ("a_mmajor", ctypes.c_int32), ("b_nmajor", ctypes.c_int32),
                 ("cd_mmajor", ctypes.c_int32), ("ab_type", ctypes.c_int32),
-                ("c_type", ctypes.c_int32), ("x_type", ctypes.c_int32)]
+                ("c_type", ctypes.c_int32), ("x_type", ctypes.c_int32),
+                ("b_type", ctypes.c_int32)]
 
 
 def build(force: bool = True) -> str:
@@ -149,22 +150,22 @@ def _decode(lib, type_name: str, stored) -> np.ndarray:
     return out
 
 
-def _desc(M, N, K, L, a_major, b_major, cd_major, ab, c, x):
+def _desc(M, N, K, L, a_major, b_major, cd_major, ab, c, x, b=None):
     if a_major not in "KM" or b_major not in "KN" or cd_major not in "NM":
         raise ValueError("bad majorness")
     return _Desc(M, N, K, L, int(a_major == "M"), int(b_major == "N"),
                  int(cd_major == "M"), TYPES[ab], TYPES[c or "none"],
-                 TYPES[x or "none"])
+                 TYPES[x or "none"], TYPES[b] if b and b != ab else 0)
 
 
-def _gemm_epi(lib, M, N, K, L, A, B, C=None, X=None, *, ab="f16", c=None, x=None,
+def _gemm_epi(lib, M, N, K, L, A, B, C=None, X=None, *, ab="f16", b=None, c=None, x=None,
              a_major="K", b_major="K", cd_major="N", alpha=1.0, beta=0.0,
              x_factor=0.0, relu=False, nthreads=None):
     """Full oracle result: (D_ref, Y_ref, S) as flat float64 arrays laid out
     like C/D (packed batches, L outermost, ``cd_major`` contiguous).  relu:
     D = max(0, alpha*Y + beta*C) + x_factor*X."""
-    d = _desc(M, N, K, L, a_major, b_major, cd_major, ab, c, x)
-    a, b = _bits(A, ab), _bits(B, ab)
+    d = _desc(M, N, K, L, a_major, b_major, cd_major, ab, c, x, b)
+    a, b = _bits(A, ab), _bits(B, b or ab)
     cc = _bits(C, c) if c else None
     xx = _bits(X, x) if x else None
     _check_sizes(M, N, K, L, a, b, cc, xx)
@@ -182,12 +183,12 @@ def _gemm_epi(lib, M, N, K, L, A, B, C=None, X=None, *, ab="f16", c=None, x=None
     return D, Y, S
 
 
-def _gemm_epi_points(lib, M, N, K, L, A, B, C=None, X=None, *, points, ab="f16",
+def _gemm_epi_points(lib, M, N, K, L, A, B, C=None, X=None, *, points, ab="f16", b=None,
                     c=None, x=None, a_major="K", b_major="K", cd_major="N",
                     alpha=1.0, beta=0.0, x_factor=0.0, relu=False, nthreads=None):
     """Oracle at listed (l, m, n) points: returns (D_ref, Y_ref, S) per point."""
-    d = _desc(M, N, K, L, a_major, b_major, cd_major, ab, c, x)
-    a, b = _bits(A, ab), _bits(B, ab)
+    d = _desc(M, N, K, L, a_major, b_major, cd_major, ab, c, x, b)
+    a, b = _bits(A, ab), _bits(B, b or ab)
     cc = _bits(C, c) if c else None
     xx = _bits(X, x) if x else None
     _check_sizes(M, N, K, L, a, b, cc, xx)

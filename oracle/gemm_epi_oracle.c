@@ -20,7 +20,8 @@
  *
  *     D[l,m,n] = max(0, alpha * Y[l,m,n] + beta * C[l,m,n]) + x_factor * X[l,m,n]
  *
- * Inputs: fp16, bf16, OCP fp8 E4M3 and E5M2, int8.  A is M x K x L, B is N x K x L (so the product is A times B-transposed in
+ * Inputs: fp16, bf16, OCP fp8 E4M3 and E5M2, int8; B may have its own type
+ * (the fp8 pairs E4M3 x E5M2 and E5M2 x E4M3).  A is M x K x L, B is N x K x L (so the product is A times B-transposed in
  * row-major algebra), C/X/D/Y are M x N x L.  Every stored element is decoded
  * exactly to double, the contraction runs in double in ascending k, and the
  * epilogue is applied in double to the unrounded sum.  Nothing is rounded to
@@ -65,6 +66,7 @@ typedef struct {
   int32_t b_nmajor;  /* 0: B[l][n][k] (k contiguous); 1: B[l][k][n] */
   int32_t cd_mmajor; /* 0: C/D/X/Y[l][m][n] (n contiguous); 1: [l][n][m] */
   int32_t ab_type, c_type, x_type;
+  int32_t b_type; /* ORC_NONE: B has A's type; else B's own type (fp8 pairs) */
 } orc_desc;
 
 /* ---- exact decoders, written from the format definitions ---------------- */
@@ -170,7 +172,7 @@ static void element(const orc_problem* p, int64_t l, int64_t m, int64_t n,
   double acc = 0.0, s = 0.0;
   for (int64_t k = 0; k < d->K; ++k) {
     double a = load(p->A, d->ab_type, a_index(d, l, m, k));
-    double b = load(p->B, d->ab_type, b_index(d, l, n, k));
+    double b = load(p->B, d->b_type ? d->b_type : d->ab_type, b_index(d, l, n, k));
     acc += a * b;
     s += fabs(a) * fabs(b);
   }
@@ -253,6 +255,8 @@ static int check_desc(const orc_desc* d, const void* A, const void* B) {
   if (!d || !A || !B) return 1;
   if (d->M < 0 || d->N < 0 || d->K < 0 || d->L < 0) return 1;
   if ((d->ab_type < ORC_F16 || d->ab_type > ORC_I8) && d->ab_type != ORC_E5M2) return 1;
+  if (d->b_type != ORC_NONE && (d->b_type < ORC_F16 || d->b_type > ORC_I8) && d->b_type != ORC_E5M2)
+    return 1;
   return 0;
 }
 

@@ -72,8 +72,8 @@ def from_cd_layout(flat: np.ndarray, L, M, N, cd: str) -> np.ndarray:
 
 
 def run(orc, A, B, C=None, X=None, *, M, N, K, L, ab, c=None, x=None,
-        a="K", b="K", cd="N", alpha=1.0, beta=0.0, xf=0.0, relu=False):
-    D, Y, S = orc.gemm_epi(M, N, K, L, A, B, C, X, ab=ab, c=c, x=x,
+        a="K", b="K", cd="N", alpha=1.0, beta=0.0, xf=0.0, relu=False, bt=None):
+    D, Y, S = orc.gemm_epi(M, N, K, L, A, B, C, X, ab=ab, b=bt, c=c, x=x,
                            a_major=a, b_major=b, cd_major=cd, alpha=alpha,
                            beta=beta, x_factor=xf, relu=relu, nthreads=2)
     return (from_cd_layout(D, L, M, N, cd), from_cd_layout(Y, L, M, N, cd),
@@ -433,6 +433,31 @@ def pin_linearity(orc):
         assert np.array_equal(D, al * Y + be * cv + xf * xv), (al, be, xf)
 
 
+def pin_fp8_pairs(orc):
+    """A and B in different fp8 formats (e4m3 x e5m2 and e5m2 x e4m3), every
+    layout: exact rational arithmetic on each operand's own decoding."""
+    M, N, K, L = 3, 4, 6, 1
+    seed = 98000
+    for at, bt in (("e4m3", "e5m2"), ("e5m2", "e4m3")):
+        for (a, b, cd) in LAYOUTS:
+            seed += 10
+            Al = _rand(_dist_for(at), at, (L, M, K), seed + 1)
+            Bl = _rand(_dist_for(bt), bt, (L, N, K), seed + 2)
+            Cl = _rand("normal", "f16", (L, M, N), seed + 3)
+            D, Y, _ = run(orc, store(Al, "A", a), store(Bl, "B", b), store(Cl, "C", cd), M=M,
+                          N=N, K=K, L=L, ab=at, bt=bt, c="f16", a=a, b=b, cd=cd,
+                          alpha=1.0, beta=0.5)
+            av = lib_decode(Al).reshape(L, M, K)
+            bv = lib_decode(Bl).reshape(L, N, K)
+            cv = lib_decode(Cl).reshape(L, M, N)
+            for m in range(M):
+                for n in range(N):
+                    acc = sum(Fraction(av[0, m, k]) * Fraction(bv[0, n, k]) for k in range(K))
+                    assert Fraction(Y[0, m, n]) == acc, (at, bt, a, b, cd, m, n)
+                    assert Fraction(D[0, m, n]) == acc + Fraction(0.5) * Fraction(cv[0, m, n]), \
+                        (at, bt, a, b, cd, m, n)
+
+
 # --------------------------------------------------------------------------
 # the clamped epilogue: D = max(0, alpha*Y + beta*C) + x_factor*X (the form
 # the example's epilogue function builds)
@@ -513,5 +538,5 @@ ALL_PINS = [pin_decode_golden, pin_decode_vs_library, pin_bruteforce_exact,
             pin_identity_A, pin_identity_B, pin_all_ones, pin_rank1,
             pin_alpha_zero, pin_skip_and_identity_epilogue, pin_integer_exact,
             pin_library_fp64, pin_majorness_duality, pin_batch_independence,
-            pin_points_match_full, pin_linearity, pin_relu_bruteforce,
+            pin_points_match_full, pin_linearity, pin_fp8_pairs, pin_relu_bruteforce,
             pin_relu_sign_identity, pin_relu_closed_forms]

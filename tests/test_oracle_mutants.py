@@ -48,6 +48,7 @@ MUTANTS = [
     ("e5m2_bias", "ldexp((double)(4 + f), e - 17)", "ldexp((double)(4 + f), e - 16)"),
     ("e5m2_subnormal", "ldexp((double)f, -16)", "ldexp((double)f, -17)"),
     ("e5m2_as_e4m3_fields", "e = (b >> 2) & 31, f = b & 3", "e = (b >> 3) & 15, f = b & 7"),
+    ("b_uses_a_type", "load(p->B, d->b_type ? d->b_type : d->ab_type,", "load(p->B, d->ab_type,"),
     ("relu_ignored", "if (p->relu && !(out > 0.0)) out = 0.0;", "(void)0;"),
     ("relu_always", "if (p->relu && !(out > 0.0))", "if (!(out > 0.0))"),
     ("relu_keeps_negatives", "if (p->relu && !(out > 0.0)) out = 0.0;",
