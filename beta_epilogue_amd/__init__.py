@@ -37,7 +37,7 @@ class gemm_epi_desc(ctypes.Structure):
                 ("cd_major", ctypes.c_int32), ("ab_dtype", ctypes.c_int32),
                 ("c_dtype", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
                 ("d_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32),
-                ("epilogue", ctypes.c_int32)]
+                ("epilogue", ctypes.c_int32), ("b_dtype", ctypes.c_int32)]
 
 
 class gemm_epi_plan(ctypes.Structure):
@@ -109,10 +109,12 @@ EPILOGUES = {"linear": 0, "relu": 1}
 
 def make_desc(M, N, K, L=1, *, ab="f16", a_major="K", b_major="K",
               cd_major="N", c=None, x=None, d="f32", y=None,
-              epilogue="linear") -> gemm_epi_desc:
+              epilogue="linear", b=None) -> gemm_epi_desc:
+    """b: B's own type when it differs from A's (the fp8 pairs)."""
     return gemm_epi_desc(M, N, K, L, MAJOR[a_major], MAJOR[b_major],
                          MAJOR[cd_major], DTYPES[ab], DTYPES[c], DTYPES[x],
-                         DTYPES[d], DTYPES[y], EPILOGUES[epilogue])
+                         DTYPES[d], DTYPES[y], EPILOGUES[epilogue],
+                         DTYPES[b] if b and b != ab else 0)
 
 
 def gemm_epi_create(desc: gemm_epi_desc) -> int:
@@ -169,10 +171,10 @@ class FusedGemm:
 
     def __init__(self, M, N, K, L=1, *, ab="f16", a_major="K", b_major="K",
                  cd_major="N", c=None, x=None, d="f32", y=None, variant=-1,
-                 epilogue="linear"):
+                 epilogue="linear", b=None):
         self.desc = make_desc(M, N, K, L, ab=ab, a_major=a_major,
                               b_major=b_major, cd_major=cd_major, c=c, x=x,
-                              d=d, y=y, epilogue=epilogue)
+                              d=d, y=y, epilogue=epilogue, b=b)
         self.shape = (M, N, K, L)
         self.handle = (gemm_epi_create(self.desc) if variant == -1
                        else gemm_epi_create_variant(self.desc, variant))

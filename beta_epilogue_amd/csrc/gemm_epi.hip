@@ -129,6 +129,10 @@ static int validate_desc(const gemm_epi_desc* d) {
     return fail(GEMM_EPI_ERR_INVALID_ARG, "b_major must be K or N");
   if (d->cd_major != GEMM_EPI_MAJOR_N && d->cd_major != GEMM_EPI_MAJOR_M)
     return fail(GEMM_EPI_ERR_INVALID_ARG, "cd_major must be N or M");
+  if (d->b_dtype != GEMM_EPI_NONE && d->b_dtype != d->ab_dtype &&
+      !((d->ab_dtype == GEMM_EPI_E4M3 || d->ab_dtype == GEMM_EPI_E5M2) &&
+        (d->b_dtype == GEMM_EPI_E4M3 || d->b_dtype == GEMM_EPI_E5M2)))
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "b_dtype may differ from ab_dtype only as the other fp8 format");
   if (d->epilogue != GEMM_EPI_LINEAR && d->epilogue != GEMM_EPI_RELU)
     return fail(GEMM_EPI_ERR_INVALID_ARG, "epilogue must be LINEAR or RELU (got %d)", d->epilogue);
   const int ab = d->ab_dtype;
@@ -165,8 +169,16 @@ static int validate_desc(const gemm_epi_desc* d) {
   return GEMM_EPI_OK;
 }
 
+// The kernel's A/B code: the common type, or an fp8 pair.
+static int kernel_ab(const gemm_epi_desc* d) {
+  if (d->b_dtype == GEMM_EPI_NONE || d->b_dtype == d->ab_dtype) return d->ab_dtype;
+  if (d->ab_dtype == GEMM_EPI_E4M3 && d->b_dtype == GEMM_EPI_E5M2) return gemm_epi::T_E4M3_E5M2;
+  if (d->ab_dtype == GEMM_EPI_E5M2 && d->b_dtype == GEMM_EPI_E4M3) return gemm_epi::T_E5M2_E4M3;
+  return -1;
+}
+
 static bool variant_fits(const Variant& v, const gemm_epi_desc* d) {
-  return v.ab == d->ab_dtype && v.a_major == d->a_major && v.b_major == d->b_major &&
+  return v.ab == kernel_ab(d) && v.a_major == d->a_major && v.b_major == d->b_major &&
          v.cd_major == d->cd_major;
 }
 

@@ -38,6 +38,8 @@ namespace gemm_epi {
 
 // Element type codes; the same numbers as the public header.
 enum : int { T_NONE = 0, T_F16 = 1, T_BF16 = 2, T_E4M3 = 3, T_I8 = 4, T_F32 = 5, T_I32 = 6, T_E5M2 = 7 };
+// Kernel A/B codes of the fp8 pairs (A's format x B's).
+enum : int { T_E4M3_E5M2 = 8, T_E5M2_E4M3 = 9 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -171,6 +173,20 @@ template <> struct Mma<T_E5M2, 32> : MmaLayout32 {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 1, 1, 0, 0, 0, 0);
   }
 };
+
+// Mixed fp8 pairs: the f8f6f4 MFMA takes one format selector per operand
+// (A first, then B; 0 = e4m3, 1 = e5m2).
+template <int FA, int FB>
+struct MmaF8Pair : MmaLayout32 {
+  typedef v16f acc_t;
+  typedef v8i frag_t;
+  static constexpr int ESIZE = 1, KSB = 64;
+  static __device__ __forceinline__ acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
+  }
+};
+template <> struct Mma<T_E4M3_E5M2, 32> : MmaF8Pair<0, 1> {};
+template <> struct Mma<T_E5M2_E4M3, 32> : MmaF8Pair<1, 0> {};
 
 // Compile-time kernel configuration.
 //   BM x BN     workgroup tile (multiples of 32 per wave)

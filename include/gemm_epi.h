@@ -28,7 +28,8 @@
  *     gemm_epi_create(); nothing ever falls back silently to another path;
  *   - the contiguous extent of every tensor is a multiple of 16 bytes and
  *     every base pointer is 16-byte aligned;
- *   - C, X, D and Y share one majorness; A and B share one element type;
+ *   - C, X, D and Y share one majorness; A and B share one element type,
+ *     except that the two fp8 formats may be paired (b_dtype);
  *   - one immutable handle per problem shape, reusable from any host thread
  *     and on any stream of the device it was created on.
  *
@@ -91,6 +92,9 @@ typedef struct gemm_epi_desc {
   int32_t d_dtype;     /* F16/BF16/F32 (float A/B) or I32 (int8 A/B) */
   int32_t y_dtype;     /* NONE, or as d_dtype */
   int32_t epilogue;    /* GEMM_EPI_LINEAR (0) or GEMM_EPI_RELU */
+  int32_t b_dtype;     /* NONE (0): B has ab_dtype.  Else the other fp8 format
+                          for an fp8 ab_dtype: E4M3 x E5M2 or E5M2 x E4M3
+                          (A's format x B's); N-major C/D/X/Y */
 } gemm_epi_desc;
 
 typedef struct gemm_epi_handle gemm_epi_handle;

@@ -49,6 +49,8 @@ class Problem:
     dist_x: str = "normal"
     seed: int = 0
     epilogue: str = "linear"  # or "relu": D = max(0, alpha*Y + beta*C) + x_factor*X
+    b_ab: Optional[str] = None    # B's own type (fp8 pairs), else ab
+    dist_b: Optional[str] = None  # B's distribution, else dist_ab
 
     @property
     def flops(self) -> int:
@@ -180,7 +182,7 @@ def make_inputs(p: Problem) -> Dict[str, Optional[torch.Tensor]]:
     p.seed + {A: 1, B: 2, C: 3, X: 4}."""
     out: Dict[str, Optional[torch.Tensor]] = {}
     for which, dt, dist, s in (("A", p.ab, p.dist_ab, 1),
-                               ("B", p.ab, p.dist_ab, 2),
+                               ("B", p.b_ab or p.ab, p.dist_b or p.dist_ab, 2),
                                ("C", p.c, p.dist_c, 3),
                                ("X", p.x, p.dist_x, 4)):
         if dt is None:

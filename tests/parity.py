@@ -68,7 +68,7 @@ def run_gpu(p: synth.Problem, ins, variant=-1, check_inputs=True):
     keep = {k: v.clone() for k, v in dev.items() if v is not None and k in "CX"}
     g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, a_major=p.a_major,
                      b_major=p.b_major, cd_major=p.cd_major, c=p.c, x=p.x,
-                     d=p.d, y=p.y, variant=variant, epilogue=p.epilogue)
+                     d=p.d, y=p.y, variant=variant, epilogue=p.epilogue, b=p.b_ab)
     shape = p.storage_shape("D")
     D = GuardedOut(p.d, shape)
     Y = GuardedOut(p.y, shape) if p.y else None
@@ -138,7 +138,7 @@ def parity_full(p: synth.Problem, variant=-1, exact=False, ins=None):
     ins = ins if ins is not None else synth.make_inputs(p)
     D, Y, plan = run_gpu(p, ins, variant)
     Dref, Yref, S = oracle.gemm_epi(p.M, p.N, p.K, p.L, ins["A"], ins["B"],
-                                    ins["C"], ins["X"], ab=p.ab, c=p.c, x=p.x,
+                                    ins["C"], ins["X"], ab=p.ab, b=p.b_ab, c=p.c, x=p.x,
                                     a_major=p.a_major, b_major=p.b_major,
                                     cd_major=p.cd_major, alpha=p.alpha,
                                     beta=p.beta, x_factor=p.x_factor,
@@ -180,7 +180,7 @@ def parity_sampled(p: synth.Problem, variant=-1, n_random=2048, ins=None):
     pts = sample_points(p, n_random)
     Dref, Yref, S = oracle.gemm_epi_points(
         p.M, p.N, p.K, p.L, ins["A"], ins["B"], ins["C"], ins["X"], points=pts,
-        ab=p.ab, c=p.c, x=p.x, a_major=p.a_major, b_major=p.b_major,
+        ab=p.ab, b=p.b_ab, c=p.c, x=p.x, a_major=p.a_major, b_major=p.b_major,
         cd_major=p.cd_major, alpha=p.alpha, beta=p.beta, x_factor=p.x_factor,
         relu=p.epilogue == "relu")
     idx = flat_index(p, pts)

@@ -100,6 +100,9 @@ def test_create_bad_enums():
     desc.d_dtype = 17
     assert ge.lib().gemm_epi_create(ctypes.byref(desc), ctypes.byref(h)) == \
         ge.GEMM_EPI_ERR_INVALID_ARG
+    desc = ge.make_desc(256, 256, 256, 1, ab="f16", d="f16", b="e5m2")
+    assert ge.lib().gemm_epi_create(ctypes.byref(desc), ctypes.byref(h)) == \
+        ge.GEMM_EPI_ERR_INVALID_ARG  # only the fp8 formats pair
     desc = ge.make_desc(256, 256, 256, 1, ab="f16", d="f16")
     desc.epilogue = 2  # only LINEAR (0) and RELU (1)
     assert ge.lib().gemm_epi_create(ctypes.byref(desc), ctypes.byref(h)) == \

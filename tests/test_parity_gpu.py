@@ -194,6 +194,25 @@ def test_parity_e5m2(p):
     _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
 
 
+# fp8 pairs: A e4m3 with B e5m2 and the reverse (per-operand format
+# selectors), N-major outputs.
+F8PAIRS = [
+    small(CFG[4], 600, 528, 400).replace(name="e4m3_x_e5m2", b_ab="e5m2", dist_b="e5m2tab",
+                                         seed=8600),
+    small(CFG[4], 600, 528, 400).replace(name="e5m2_x_e4m3", ab="e5m2", dist_ab="e5m2tab",
+                                         b_ab="e4m3", dist_b="e4m3tab", seed=8700),
+    CFG[4].replace(name="e4m3_x_e5m2_f32_xy", M=260, N=264, K=256, d="f32", c="f32", x="bf16",
+                   y="f32", x_factor=-1.5, b_ab="e5m2", dist_b="e5m2tab", seed=8800),
+]
+
+
+@pytest.mark.parametrize("p", F8PAIRS, ids=[e.name for e in F8PAIRS])
+def test_parity_fp8_pairs(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.ab, p.b_ab)
+    (ed, ey), plan = parity_full(p)
+    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
+
 def test_parity_e5m2_full_size_sampled():
     p = CFG[4].replace(name="e5m2_8192_f16out", ab="e5m2", dist_ab="e5m2tab", seed=8500)
     (ed, ey), plan, npts = parity_sampled(p)
@@ -228,6 +247,9 @@ def test_every_variant_runs():
         "bf16": CFG[1].replace(M=264, N=272, K=136, L=2),
         "e4m3": CFG[4].replace(M=264, N=272, K=144, L=2),
         "e5m2": CFG[4].replace(M=264, N=272, K=144, L=2, ab="e5m2", dist_ab="e5m2tab"),
+        "e4e5": CFG[4].replace(M=264, N=272, K=144, L=2, b_ab="e5m2", dist_b="e5m2tab"),
+        "e5e4": CFG[4].replace(M=264, N=272, K=144, L=2, ab="e5m2", dist_ab="e5m2tab",
+                               b_ab="e4m3", dist_b="e4m3tab"),
         "i8": CFG[3].replace(M=272, N=264, K=144, L=2),
     }
     for i, name in enumerate(names):
