@@ -29,7 +29,8 @@
  *   - the contiguous extent of every tensor is a multiple of 16 bytes and
  *     every base pointer is 16-byte aligned;
  *   - C, X, D and Y share one majorness; A and B share one element type,
- *     except that the two fp8 formats may be paired (b_dtype);
+ *     except that the two fp8 formats may be paired (b_dtype; the pipeline
+ *     API card, "Precision": fp8 e4m3 or e5m2 in any pairing);
  *   - one immutable handle per problem shape, reusable from any host thread
  *     and on any stream of the device it was created on.
  *
