@@ -596,13 +596,25 @@ __device__ __forceinline__ v4u relu4(v4u t) {
              (int)t.w > 0 ? t.w : 0u};
 }
 
+// The same as a per-element select on a uniform flag, without a branch:
+// in the general epilogue (divergent lanes, 16x16 blocks) a branch on the
+// flag here gave wrong results for unclamped lanes at a ragged N edge.
+__device__ __forceinline__ v4f relu4_if(v4f t, bool on) {
+  return v4f{on && !(t.x > 0.0f) ? 0.0f : t.x, on && !(t.y > 0.0f) ? 0.0f : t.y,
+             on && !(t.z > 0.0f) ? 0.0f : t.z, on && !(t.w > 0.0f) ? 0.0f : t.w};
+}
+__device__ __forceinline__ v4u relu4_if(v4u t, bool on) {
+  return v4u{on && (int)t.x <= 0 ? 0u : t.x, on && (int)t.y <= 0 ? 0u : t.y,
+             on && (int)t.z <= 0 ? 0u : t.z, on && (int)t.w <= 0 ? 0u : t.w};
+}
+
 template <class CF>
 __device__ __forceinline__ void epi_finish4(const Params& p, int64_t o, v4f w, v4f c, v4f x) {
   if constexpr (CF::AB == T_I8) {
     const v4u a = __builtin_bit_cast(v4u, w);
     v4u t = a * (unsigned)p.ialpha;
     if (p.c_dtype) t += __builtin_bit_cast(v4u, c) * (unsigned)p.ibeta;
-    if (p.relu) t = relu4(t);
+    t = relu4_if(t, p.relu != 0);
     if (p.x_dtype) t += __builtin_bit_cast(v4u, x) * (unsigned)p.ix;
     __builtin_nontemporal_store(t, (v4u*)((int*)p.D + o));
     if (p.y_dtype) __builtin_nontemporal_store(a, (v4u*)((int*)p.Y + o));
@@ -614,7 +626,7 @@ __device__ __forceinline__ void epi_finish4(const Params& p, int64_t o, v4f w, v
       t.z = __builtin_fmaf(p.beta, c.z, t.z);
       t.w = __builtin_fmaf(p.beta, c.w, t.w);
     }
-    if (p.relu) t = relu4(t);
+    t = relu4_if(t, p.relu != 0);
     if (p.x_dtype) {
       t.x = __builtin_fmaf(p.xf, x.x, t.x);
       t.y = __builtin_fmaf(p.xf, x.y, t.y);

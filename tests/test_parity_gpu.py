@@ -81,10 +81,28 @@ EDGE = [
     # N-major f16 C/X/D/Y with both tile extents cut: 8-element lane groups
     # past N and rows past M
     CFG[2].replace(name="f16_ragged_mn", M=300, N=392, K=96, seed=7000),
-    # mixed C/X/D/Y types (general epilogue, routed to 32x32 blocks), ragged N
+    # mixed C/X/D/Y types (general epilogue), ragged N
     CFG[1].replace(name="mixed_types_ragged", M=300, N=264, K=128, c="f32", x="bf16",
                    y="bf16", x_factor=0.5, seed=7060),
 ]
+
+
+def test_general_epilogue_ragged_n_both_block_shapes():
+    """Mixed C/X/D/Y types run the general epilogue; with 16x16 and 32x32
+    MFMA blocks, linear and ReLU forms, a ragged N tile, with and without Y.
+    (A branch on the ReLU flag inside its per-lane work once dropped the
+    accumulator term of unclamped outputs at such an edge with 16x16 blocks.)"""
+    import beta_epilogue_amd as ge
+    names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
+    for v in (names.index("bf16_kk_n_256x256_r128_w4_s2_b16"),
+              names.index("bf16_kk_n_256x256_r128_w4_s2_q2")):
+        for epi in ("linear", "relu"):
+            for y in (None, "bf16"):
+                p = CFG[1].replace(name="general_%s_%s_%s" % (names[v], epi, y), M=300, N=264,
+                                   K=128, c="f32", x="bf16", y=y, x_factor=0.5,
+                                   beta=-1.0 if epi == "relu" else 1.0, epilogue=epi, seed=7070)
+                _say("case", p.name)
+                parity_full(p, variant=v)
 
 
 # The ReLU form D = max(0, alpha*A.B^T + beta*C) + x_factor*X: mixed-sign
