@@ -95,7 +95,7 @@ typedef struct gemm_epi_desc {
   int32_t epilogue;    /* GEMM_EPI_LINEAR (0) or GEMM_EPI_RELU */
   int32_t b_dtype;     /* NONE (0): B has ab_dtype.  Else the other fp8 format
                           for an fp8 ab_dtype: E4M3 x E5M2 or E5M2 x E4M3
-                          (A's format x B's); N-major C/D/X/Y */
+                          (A's format x B's) */
 } gemm_epi_desc;
 
 typedef struct gemm_epi_handle gemm_epi_handle;

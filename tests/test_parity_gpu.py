@@ -221,6 +221,11 @@ F8PAIRS = [
                                          b_ab="e4m3", dist_b="e4m3tab", seed=8700),
     CFG[4].replace(name="e4m3_x_e5m2_f32_xy", M=260, N=264, K=256, d="f32", c="f32", x="bf16",
                    y="f32", x_factor=-1.5, b_ab="e5m2", dist_b="e5m2tab", seed=8800),
+    CFG[4].replace(name="e4m3_x_e5m2_mmajor", M=264, N=296, K=160, cd_major="M", b_ab="e5m2",
+                   dist_b="e5m2tab", seed=8900),
+    CFG[4].replace(name="e5m2_x_e4m3_mmajor_relu", M=264, N=296, K=160, cd_major="M",
+                   ab="e5m2", dist_ab="e5m2tab", b_ab="e4m3", dist_b="e4m3tab", beta=-1.0,
+                   epilogue="relu", seed=8950),
 ]
 
 
