@@ -183,6 +183,18 @@ static bool variant_fits(const Variant& v, const gemm_epi_desc* d) {
 }
 
 
+// Problems the one-type epilogue cannot take: C/X/D/Y of different element
+// types, or a leading extent too long for its 31-bit offsets.  They run the
+// general epilogue, which is only used with 32x32 MFMA blocks: with 16x16
+// blocks it gave wrong values near a ragged N edge (cause not found), so
+// those variants refuse such problems instead.
+static bool needs_general_epilogue(const gemm_epi_desc* d) {
+  for (int t : {d->c_dtype, d->x_dtype, d->y_dtype})
+    if (t != GEMM_EPI_NONE && t != d->d_dtype) return true;
+  const int64_t ld = d->cd_major == GEMM_EPI_MAJOR_N ? d->N : d->M;
+  return (int64_t)256 * ld * 4 >= (int64_t(1) << 31);
+}
+
 extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
                                        gemm_epi_handle** out) {
   g_last_error[0] = 0;
@@ -192,9 +204,10 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   if (rc) return rc;
   if (variant < -1 || variant >= kNumVariants)
     return fail(GEMM_EPI_ERR_INVALID_ARG, "variant %d out of range", variant);
+  const bool general = needs_general_epilogue(desc);
   if (variant == -1) {
     for (int i = 0; i < kNumVariants; ++i)
-      if (variant_fits(kVariants[i], desc)) {
+      if (variant_fits(kVariants[i], desc) && (!general || kVariants[i].blk == 32)) {
         variant = i;
         break;
       }
@@ -204,6 +217,10 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
                   desc->ab_dtype, desc->a_major, desc->b_major, desc->cd_major);
   } else if (!variant_fits(kVariants[variant], desc)) {
     return fail(GEMM_EPI_ERR_UNSUPPORTED, "variant %s cannot run this problem",
+                kVariants[variant].name);
+  } else if (general && kVariants[variant].blk != 32) {
+    return fail(GEMM_EPI_ERR_UNSUPPORTED,
+                "variant %s (16x16 blocks) has no mixed-type epilogue; use a 32x32 variant",
                 kVariants[variant].name);
   }
   const Variant& v = kVariants[variant];
@@ -314,6 +331,8 @@ extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void*
   const int64_t ld = d.cd_major == GEMM_EPI_MAJOR_N ? d.N : d.M;
   if ((int64_t)(v.bm > v.bn ? v.bm : v.bn) * ld * 4 >= (int64_t(1) << 31)) kind = 0;
   p.epi_kind = kind;
+  if (kind == 0 && v.blk != 32)  // (create() routes these problems elsewhere)
+    return fail(GEMM_EPI_ERR_UNSUPPORTED, "variant %s has no mixed-type epilogue", v.name);
 
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   kVariants[h->variant].launch(p, h->grid, (hipStream_t)stream);

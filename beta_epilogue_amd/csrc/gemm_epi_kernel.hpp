@@ -596,9 +596,8 @@ __device__ __forceinline__ v4u relu4(v4u t) {
              (int)t.w > 0 ? t.w : 0u};
 }
 
-// The same as a per-element select on a uniform flag, without a branch:
-// in the general epilogue (divergent lanes, 16x16 blocks) a branch on the
-// flag here gave wrong results for unclamped lanes at a ragged N edge.
+// The clamp as a per-element select on the uniform flag, without a branch
+// inside the general epilogue's per-lane (divergent) element work.
 __device__ __forceinline__ v4f relu4_if(v4f t, bool on) {
   return v4f{on && !(t.x > 0.0f) ? 0.0f : t.x, on && !(t.y > 0.0f) ? 0.0f : t.y,
              on && !(t.z > 0.0f) ? 0.0f : t.z, on && !(t.w > 0.0f) ? 0.0f : t.w};

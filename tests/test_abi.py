@@ -112,6 +112,24 @@ def test_create_bad_enums():
     assert ge.lib().gemm_epi_create(ctypes.byref(desc), None) == ge.GEMM_EPI_ERR_INVALID_ARG
 
 
+def test_mixed_epilogue_types_refuse_16x16_variants():
+    """Mixed C/X/D/Y types need the general epilogue, which only the 32x32
+    variants run: forcing a 16x16 variant is an error (checked before any
+    device query), never a silent wrong path."""
+    names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
+    v16 = names.index("bf16_kk_n_256x256_r128_w4_s2_b16")
+    desc = ge.make_desc(300, 264, 128, 1, ab="bf16", c="f32", x="bf16", d="f32")
+    h = ctypes.c_void_p()
+    assert ge.lib().gemm_epi_create_variant(ctypes.byref(desc), v16, ctypes.byref(h)) == \
+        ge.GEMM_EPI_ERR_UNSUPPORTED
+    assert "mixed-type" in ge.last_error()
+    desc = ge.make_desc(300, 264, 128, 1, ab="bf16", c="f32", x="f32", d="f32")
+    assert ge.lib().gemm_epi_create_variant(ctypes.byref(desc), v16, ctypes.byref(h)) in \
+        (ge.GEMM_EPI_OK, ge.GEMM_EPI_ERR_DEVICE)
+    if h.value:
+        ge.lib().gemm_epi_destroy(h)
+
+
 def test_unsupported_layout_is_an_error_not_a_fallback():
     rc, _ = _create(b_major="N")  # no N-major B kernel yet
     assert rc in (ge.GEMM_EPI_ERR_UNSUPPORTED, ge.GEMM_EPI_ERR_DEVICE)

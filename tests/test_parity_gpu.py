@@ -87,159 +87,24 @@ EDGE = [
 ]
 
 
-def test_general_epilogue_ragged_n_both_block_shapes():
-    """Mixed C/X/D/Y types run the general epilogue; with 16x16 and 32x32
-    MFMA blocks, linear and ReLU forms, a ragged N tile, with and without Y.
-    (A branch on the ReLU flag inside its per-lane work once dropped the
-    accumulator term of unclamped outputs at such an edge with 16x16 blocks.)"""
+def test_general_epilogue_routing_and_ragged_n():
+    """Mixed C/X/D/Y types run the general epilogue, on 32x32-block variants
+    only: the default picks one and a forced 16x16 variant is refused.  Linear
+    and ReLU forms, a ragged N tile, with and without Y, batched."""
     import beta_epilogue_amd as ge
     names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
-    for v in (names.index("bf16_kk_n_256x256_r128_w4_s2_b16"),
-              names.index("bf16_kk_n_256x256_r128_w4_s2_q2")):
-        for epi in ("linear", "relu"):
-            for y in (None, "bf16"):
-                p = CFG[1].replace(name="general_%s_%s_%s" % (names[v], epi, y), M=300, N=264,
-                                   K=128, c="f32", x="bf16", y=y, x_factor=0.5,
-                                   beta=-1.0 if epi == "relu" else 1.0, epilogue=epi, seed=7070)
-                _say("case", p.name)
-                parity_full(p, variant=v)
-
-
-# The ReLU form D = max(0, alpha*A.B^T + beta*C) + x_factor*X: mixed-sign
-# sums so both sides of the clamp occur; typed epilogues (f16, f32, int32)
-# and the mixed-type one, both majornesses.
-RELU = [
-    small(CFG[2], 600, 520, 392).replace(name="relu_f16_cxdy", epilogue="relu", seed=7200),
-    small(CFG[2], 264, 392, 136).replace(name="relu_f16_mmajor", cd_major="M",
-                                         epilogue="relu", seed=7300),
-    small(CFG[1], 592, 528, 392).replace(name="relu_bf16_f32", alpha=1.0, beta=-1.0,
-                                         epilogue="relu", seed=7400),
-    small(CFG[3], 592, 528, 400, L=2).replace(name="relu_i8_mmajorA", beta=-1.0,
-                                              epilogue="relu", seed=7500),
-    CFG[3].replace(name="relu_i8_kmajor_xy", M=260, N=264, K=160, L=1, a_major="K",
-                   x="i32", y="i32", alpha=-3.0, beta=2.0, x_factor=5.0, dist_x="i1000",
-                   epilogue="relu", seed=7600),
-    CFG[4].replace(name="relu_e4m3_mixed", M=260, N=264, K=256, x="bf16", y="f32",
-                   x_factor=-1.5, beta=-1.0, epilogue="relu", seed=7700),
-]
-
-
-@pytest.mark.parametrize("p", RELU, ids=[e.name for e in RELU])
-def test_parity_relu(p):
-    _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
-    (ed, ey), plan = parity_full(p)
-    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
-
-
-def test_parity_relu_full_size_sampled():
-    """The 8192^3 fp16 workload in the ReLU form, at the bench's launch."""
-    p = CFG[2].replace(name="f16_8192_fused_cxdy_relu", epilogue="relu")
-    (ed, ey), plan, npts = parity_sampled(p)
-    _say("  plan", plan["name"], "points", npts, "err D %.3g Y %.3g" % (ed, ey))
-
-
-# D == C in place: bit-identical to the out-of-place run and to the oracle's
-# bound, for a typed (f16, int32) and the mixed-type epilogue.
-INPLACE = [
-    small(CFG[2], 600, 520, 392).replace(name="inplace_f16", seed=7800),
-    small(CFG[2], 264, 392, 136).replace(name="inplace_f16_relu_mmajor", cd_major="M",
-                                         epilogue="relu", seed=7850),
-    small(CFG[3], 592, 528, 400, L=2).replace(name="inplace_i32", seed=7900),
-    CFG[1].replace(name="inplace_mixed", M=300, N=264, K=128, d="f32", c="f32", x="bf16",
-                   x_factor=0.5, seed=7950),
-]
-
-
-@pytest.mark.parametrize("p", INPLACE, ids=[e.name for e in INPLACE])
-def test_inplace_d_is_c(p):
-    import beta_epilogue_amd as ge
-    _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
-    ins = synth.make_inputs(p)
-    D_out, Y_out, _ = run_gpu(p, ins)
-    dev = {k: (v.cuda() if v is not None else None) for k, v in ins.items()}
-    g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, a_major=p.a_major, b_major=p.b_major,
-                     cd_major=p.cd_major, c=p.c, x=p.x, d=p.d, y=p.y, epilogue=p.epilogue)
-    CD = dev["C"].clone()
-    Y = torch.empty_like(Y_out, device="cuda") if p.y else None
-    g(dev["A"], dev["B"], CD, dev["X"], D=CD, Y=Y, alpha=p.alpha, beta=p.beta,
-      x_factor=p.x_factor)
-    torch.cuda.synchronize()
-    g.close()
-    assert torch.equal(CD.cpu().view(torch.uint8), D_out.view(torch.uint8)), "in place != out of place"
-    if p.y:
-        assert torch.equal(Y.cpu().view(torch.uint8), Y_out.view(torch.uint8))
-    (ed, ey), _ = parity_full(p, ins=ins)
-    _say("  err D %.3g Y %.3g" % (ed, ey))
-
-
-def test_aliasing_rules():
-    import beta_epilogue_amd as ge
-    p = small(CFG[2], 256, 256, 64)
-    ins = synth.make_inputs(p)
-    dev = {k: (v.cuda() if v is not None else None) for k, v in ins.items()}
-    g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, c=p.c, x=p.x, d=p.d, y=p.y)
-    D = torch.empty_like(dev["C"])
-    for kw in (dict(D=dev["X"], Y=D), dict(D=D, Y=dev["C"]), dict(D=D, Y=D)):
-        with pytest.raises(ge.GemmEpiError) as e:
-            g(dev["A"], dev["B"], dev["C"], dev["X"], alpha=p.alpha, beta=p.beta,
-              x_factor=p.x_factor, **kw)
-        assert e.value.code == ge.GEMM_EPI_ERR_INVALID_ARG
-    # D == C with beta == 0 (C not read) is not an in-place update
-    with pytest.raises(ge.GemmEpiError):
-        g(dev["A"], dev["B"], dev["C"], dev["X"], D=dev["C"], Y=D, alpha=1.0, beta=0.0,
-          x_factor=p.x_factor)
-    g.close()
-
-
-# fp8 e5m2 A/B (format selectors 1/1 of the f8f6f4 MFMA): the e4m3 workload's
-# shapes and outputs with e5m2 values of |v| <= 4.
-E5M2 = [
-    small(CFG[4], 600, 528, 400).replace(name="e5m2_f16out", ab="e5m2", dist_ab="e5m2tab",
-                                         seed=8100),
-    CFG[4].replace(name="e5m2_mmajor_cd", M=264, N=296, K=160, cd_major="M", ab="e5m2",
-                   dist_ab="e5m2tab", seed=8200),
-    CFG[4].replace(name="e5m2_f32_xy", M=260, N=264, K=256, d="f32", c="f32", x="bf16",
-                   y="f32", x_factor=-1.5, ab="e5m2", dist_ab="e5m2tab", seed=8300),
-    CFG[4].replace(name="e5m2_relu", M=260, N=264, K=256, ab="e5m2", dist_ab="e5m2tab",
-                   beta=-1.0, epilogue="relu", seed=8400),
-]
-
-
-@pytest.mark.parametrize("p", E5M2, ids=[e.name for e in E5M2])
-def test_parity_e5m2(p):
-    _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
-    (ed, ey), plan = parity_full(p)
-    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
-
-
-# fp8 pairs: A e4m3 with B e5m2 and the reverse (per-operand format
-# selectors), N-major outputs.
-F8PAIRS = [
-    small(CFG[4], 600, 528, 400).replace(name="e4m3_x_e5m2", b_ab="e5m2", dist_b="e5m2tab",
-                                         seed=8600),
-    small(CFG[4], 600, 528, 400).replace(name="e5m2_x_e4m3", ab="e5m2", dist_ab="e5m2tab",
-                                         b_ab="e4m3", dist_b="e4m3tab", seed=8700),
-    CFG[4].replace(name="e4m3_x_e5m2_f32_xy", M=260, N=264, K=256, d="f32", c="f32", x="bf16",
-                   y="f32", x_factor=-1.5, b_ab="e5m2", dist_b="e5m2tab", seed=8800),
-    CFG[4].replace(name="e4m3_x_e5m2_mmajor", M=264, N=296, K=160, cd_major="M", b_ab="e5m2",
-                   dist_b="e5m2tab", seed=8900),
-    CFG[4].replace(name="e5m2_x_e4m3_mmajor_relu", M=264, N=296, K=160, cd_major="M",
-                   ab="e5m2", dist_ab="e5m2tab", b_ab="e4m3", dist_b="e4m3tab", beta=-1.0,
-                   epilogue="relu", seed=8950),
-]
-
-
-@pytest.mark.parametrize("p", F8PAIRS, ids=[e.name for e in F8PAIRS])
-def test_parity_fp8_pairs(p):
-    _say("case", p.name, p.M, p.N, p.K, p.L, p.ab, p.b_ab)
-    (ed, ey), plan = parity_full(p)
-    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
-
-
-def test_parity_e5m2_full_size_sampled():
-    p = CFG[4].replace(name="e5m2_8192_f16out", ab="e5m2", dist_ab="e5m2tab", seed=8500)
-    (ed, ey), plan, npts = parity_sampled(p)
-    _say("  plan", plan["name"], "points", npts, "err D %.3g Y %.3g" % (ed, ey))
+    for epi in ("linear", "relu"):
+        for y in (None, "bf16"):
+            p = CFG[1].replace(name="general_%s_%s" % (epi, y), M=191, N=344, K=200, L=2,
+                               c="f32", x="bf16", y=y, x_factor=0.5,
+                               beta=-1.0 if epi == "relu" else 1.0, epilogue=epi, seed=7070)
+            _say("case", p.name)
+            _, plan = parity_full(p)
+            assert plan["name"] == "bf16_kk_n_256x256_r128_w4_s2_q2", plan["name"]
+    with pytest.raises(ge.GemmEpiError) as e:
+        ge.FusedGemm(300, 264, 128, ab="bf16", c="f32", x="bf16", d="f32",
+                     variant=names.index("bf16_kk_n_256x256_r128_w4_s2_b16"))
+    assert e.value.code == ge.GEMM_EPI_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("p", EDGE, ids=[e.name for e in EDGE])
@@ -331,3 +196,60 @@ def test_int_scalars_must_be_integral():
         g(a, a, d, D=d, alpha=1.5, beta=1.0)
     assert e.value.code == ge.GEMM_EPI_ERR_UNSUPPORTED
     g.close()
+
+
+def _random_problem(i):
+    """Seeded random problem i: A/B type (fp8 pairs included), layouts,
+    ragged M, N, K within the 16-byte rule, batch, output types, scalars and
+    epilogue form."""
+    rng = np.random.default_rng(9000 + i)
+    kind = ["f16", "bf16", "e4m3", "e5m2", "i8", "e4e5", "e5e4"][i % 7]
+    ab, b_ab = {"e4e5": ("e4m3", "e5m2"), "e5e4": ("e5m2", "e4m3")}.get(kind, (kind, None))
+    dist = {"f16": "normal", "bf16": "normal", "e4m3": "e4m3tab", "e5m2": "e5m2tab",
+            "i8": "i8full"}
+    cd = "NM"[int(rng.integers(2))]
+    a_major = "M" if ab == "i8" and rng.integers(2) else "K"
+    kq = 8 if ab in ("f16", "bf16") else 16
+    K = int(kq * rng.integers(1, 40))
+    L = int(rng.integers(1, 4))
+    if ab == "i8":
+        outs = ["i32"]
+    else:
+        outs = ["f32", "f16", "bf16"]
+    d = outs[int(rng.integers(len(outs)))]
+    c = outs[int(rng.integers(len(outs)))] if rng.integers(3) else None
+    x = outs[int(rng.integers(len(outs)))] if rng.integers(2) else None
+    y = outs[int(rng.integers(len(outs)))] if rng.integers(2) else None
+    # contiguous C/D extent: a multiple of 8 elements covers every output type
+    cdq = 8
+    M = int(rng.integers(1, 600))
+    N = int(rng.integers(1, 600))
+    if cd == "N":
+        N = max(cdq, N // cdq * cdq)
+    else:
+        M = max(cdq, M // cdq * cdq)
+    if a_major == "M":
+        M = max(16, M // 16 * 16)
+    if ab == "i8":
+        alpha, beta, xf = (float(rng.integers(-3, 4)) for _ in range(3))
+    else:
+        alpha, beta, xf = (float(np.round(rng.uniform(-2, 2), 3)) for _ in range(3))
+    return synth.Problem(
+        "random_%d_%s_%s%s_%s" % (i, kind, a_major.lower(), cd.lower(), d), M, N, K, L, ab,
+        a_major=a_major, cd_major=cd, c=c, x=x, d=d, y=y, alpha=alpha,
+        beta=beta if c else 0.0, x_factor=xf if x else 0.0, dist_ab=dist[ab],
+        dist_c="i1000" if ab == "i8" else "normal", dist_x="i1000" if ab == "i8" else "normal",
+        seed=9100 + 10 * i, epilogue="relu" if rng.integers(2) else "linear", b_ab=b_ab,
+        dist_b=dist[b_ab] if b_ab else None)
+
+
+RANDOM = [_random_problem(i) for i in range(28)]
+
+
+@pytest.mark.parametrize("p", RANDOM, ids=[r.name for r in RANDOM])
+def test_parity_random_problems(p):
+    """Seeded random shapes, layouts, types and scalars against the oracle."""
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.c, p.x, p.d, p.y, p.epilogue)
+    (ed, ey), plan = parity_full(p)
+    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
