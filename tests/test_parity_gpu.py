@@ -243,7 +243,7 @@ def _random_problem(i):
         dist_b=dist[b_ab] if b_ab else None)
 
 
-RANDOM = [_random_problem(i) for i in range(28)]
+RANDOM = [_random_problem(i) for i in range(64)]
 
 
 @pytest.mark.parametrize("p", RANDOM, ids=[r.name for r in RANDOM])
