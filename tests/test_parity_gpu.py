@@ -253,3 +253,25 @@ def test_parity_random_problems(p):
     (ed, ey), plan = parity_full(p)
     _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
 
+
+def _random_typed(i):
+    """Problem i with one output type for every C/X/D/Y in use (the typed
+    epilogue, which the 16x16-block defaults run), or None for fp8 inputs."""
+    p = _random_problem(i)
+    if p.ab not in ("f16", "bf16", "i8"):
+        return None
+    t = p.d
+    return p.replace(name=p.name + "_typed", c=t if p.c else None, x=t if p.x else None,
+                     y=t if p.y else None)
+
+
+RANDOM_TYPED = [q for q in (_random_typed(i) for i in range(200, 290)) if q is not None]
+
+
+@pytest.mark.parametrize("p", RANDOM_TYPED, ids=[r.name for r in RANDOM_TYPED])
+def test_parity_random_typed(p):
+    """Seeded random problems through the one-type epilogue."""
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.d, p.epilogue)
+    (ed, ey), plan = parity_full(p)
+    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
