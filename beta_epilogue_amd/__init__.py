@@ -24,6 +24,7 @@ GEMM_EPI_ERR_UNSUPPORTED = 2
 GEMM_EPI_ERR_ALIGNMENT = 3
 GEMM_EPI_ERR_DEVICE = 4
 GEMM_EPI_ERR_LAUNCH = 5
+GEMM_EPI_ERR_HOST_ALLOC = 6
 
 DTYPES = {None: 0, "none": 0, "f16": 1, "bf16": 2, "e4m3": 3, "i8": 4,
           "f32": 5, "i32": 6, "e5m2": 7}

@@ -67,8 +67,8 @@ constexpr Variant make_variant(const char* name) {
 using namespace gemm_epi;
 // Variant table (gemm_epi_variants.inc); the kernels are compiled in the
 // gemm_epi_part.hip translation units, this one only refers to them.
-#define X(PART, AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, LD, DS, BL, NAME) \
-  make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, LD, DS, BL>>(NAME),
+#define X(PART, AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, DS, BL, NAME) \
+  make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, DS, BL>>(NAME),
 const Variant kVariants[] = {
 #include "gemm_epi_variants.inc"
 };
@@ -169,11 +169,20 @@ static int validate_desc(const gemm_epi_desc* d) {
   return GEMM_EPI_OK;
 }
 
-// The kernel's A/B code: the common type, or an fp8 pair.
+// The kernel's A/B code: the common type, or an fp8 pair.  fp8 inputs with an
+// fp32 D or Y run the kernels that widen fp8 to fp16 before an f16 MFMA (exact
+// conversion, fp32 sums), so the fp32 outputs keep fp32's precision.
 static int kernel_ab(const gemm_epi_desc* d) {
-  if (d->b_dtype == GEMM_EPI_NONE || d->b_dtype == d->ab_dtype) return d->ab_dtype;
-  if (d->ab_dtype == GEMM_EPI_E4M3 && d->b_dtype == GEMM_EPI_E5M2) return gemm_epi::T_E4M3_E5M2;
-  if (d->ab_dtype == GEMM_EPI_E5M2 && d->b_dtype == GEMM_EPI_E4M3) return gemm_epi::T_E5M2_E4M3;
+  const int a = d->ab_dtype;
+  const int b = d->b_dtype == GEMM_EPI_NONE ? a : d->b_dtype;
+  const bool f8 = (a == GEMM_EPI_E4M3 || a == GEMM_EPI_E5M2) && (b == GEMM_EPI_E4M3 || b == GEMM_EPI_E5M2);
+  if (f8 && (d->d_dtype == GEMM_EPI_F32 || d->y_dtype == GEMM_EPI_F32)) {
+    if (a == b) return a == GEMM_EPI_E4M3 ? gemm_epi::T_W_E4M3 : gemm_epi::T_W_E5M2;
+    return a == GEMM_EPI_E4M3 ? gemm_epi::T_W_E4M3_E5M2 : gemm_epi::T_W_E5M2_E4M3;
+  }
+  if (a == b) return a;
+  if (a == GEMM_EPI_E4M3 && b == GEMM_EPI_E5M2) return gemm_epi::T_E4M3_E5M2;
+  if (a == GEMM_EPI_E5M2 && b == GEMM_EPI_E4M3) return gemm_epi::T_E5M2_E4M3;
   return -1;
 }
 
@@ -182,18 +191,6 @@ static bool variant_fits(const Variant& v, const gemm_epi_desc* d) {
          v.cd_major == d->cd_major;
 }
 
-
-// Problems the one-type epilogue cannot take: C/X/D/Y of different element
-// types, or a leading extent too long for its 31-bit offsets.  They run the
-// general epilogue, which is only used with 32x32 MFMA blocks: with 16x16
-// blocks it gave wrong values near a ragged N edge (cause not found), so
-// those variants refuse such problems instead.
-static bool needs_general_epilogue(const gemm_epi_desc* d) {
-  for (int t : {d->c_dtype, d->x_dtype, d->y_dtype})
-    if (t != GEMM_EPI_NONE && t != d->d_dtype) return true;
-  const int64_t ld = d->cd_major == GEMM_EPI_MAJOR_N ? d->N : d->M;
-  return (int64_t)256 * ld * 4 >= (int64_t(1) << 31);
-}
 
 extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
                                        gemm_epi_handle** out) {
@@ -204,10 +201,9 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   if (rc) return rc;
   if (variant < -1 || variant >= kNumVariants)
     return fail(GEMM_EPI_ERR_INVALID_ARG, "variant %d out of range", variant);
-  const bool general = needs_general_epilogue(desc);
   if (variant == -1) {
     for (int i = 0; i < kNumVariants; ++i)
-      if (variant_fits(kVariants[i], desc) && (!general || kVariants[i].blk == 32)) {
+      if (variant_fits(kVariants[i], desc)) {
         variant = i;
         break;
       }
@@ -218,10 +214,6 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   } else if (!variant_fits(kVariants[variant], desc)) {
     return fail(GEMM_EPI_ERR_UNSUPPORTED, "variant %s cannot run this problem",
                 kVariants[variant].name);
-  } else if (general && kVariants[variant].blk != 32) {
-    return fail(GEMM_EPI_ERR_UNSUPPORTED,
-                "variant %s (16x16 blocks) has no mixed-type epilogue; use a 32x32 variant",
-                kVariants[variant].name);
   }
   const Variant& v = kVariants[variant];
   // Buffer offsets within one tile's rows are 32-bit.
@@ -229,6 +221,12 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   if ((int64_t)v.bm * desc->K * es >= (int64_t(1) << 31) ||
       (int64_t)v.bn * desc->K * es >= (int64_t(1) << 31))
     return fail(GEMM_EPI_ERR_UNSUPPORTED, "K too large for 32-bit tile offsets");
+  // The epilogue addresses a wave's output lines (at most a tile's BM or BN
+  // lines of the leading extent) with 31-bit byte offsets.
+  const int64_t ld = desc->cd_major == GEMM_EPI_MAJOR_N ? desc->N : desc->M;
+  if ((int64_t)(v.bm > v.bn ? v.bm : v.bn) * ld * 4 >= (int64_t(1) << 31))
+    return fail(GEMM_EPI_ERR_UNSUPPORTED, "leading extent %lld of C/X/D/Y too long for 31-bit offsets",
+                (long long)ld);
 
   // Device query (the only part that needs a GPU).
   int dev = 0;
@@ -241,7 +239,7 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
                 prop.gcnArchName);
 
   gemm_epi_handle* h = new (std::nothrow) gemm_epi_handle;
-  if (!h) return fail(GEMM_EPI_ERR_INVALID_ARG, "out of host memory");
+  if (!h) return fail(GEMM_EPI_ERR_HOST_ALLOC, "out of host memory");
   h->desc = *desc;
   h->variant = variant;
   h->device = dev;
@@ -321,18 +319,12 @@ extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void*
   p.ix = int_path ? (int32_t)x_factor : 0;
   p.xcd_remap = (h->grid % 8 == 0) ? 1 : 0;
   p.relu = d.epilogue == GEMM_EPI_RELU ? 1 : 0;
-  // Element type shared by every C/X/D/Y in use (typed epilogue), else 0.
-  // The typed epilogue addresses a wave's output region (at most a tile's
-  // BM or BN lines of the leading extent) with 31-bit byte offsets.
+  // Element type shared by every C/X/D/Y in use (one-type epilogue), else 0
+  // (mixed-type epilogue).
   int kind = d.d_dtype;
   for (int t : {use_c ? d.c_dtype : 0, use_x ? d.x_dtype : 0, d.y_dtype})
     if (t != GEMM_EPI_NONE && t != kind) kind = 0;
-  const Variant& v = kVariants[h->variant];
-  const int64_t ld = d.cd_major == GEMM_EPI_MAJOR_N ? d.N : d.M;
-  if ((int64_t)(v.bm > v.bn ? v.bm : v.bn) * ld * 4 >= (int64_t(1) << 31)) kind = 0;
   p.epi_kind = kind;
-  if (kind == 0 && v.blk != 32)  // (create() routes these problems elsewhere)
-    return fail(GEMM_EPI_ERR_UNSUPPORTED, "variant %s has no mixed-type epilogue", v.name);
 
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   kVariants[h->variant].launch(p, h->grid, (hipStream_t)stream);
@@ -378,6 +370,7 @@ extern "C" const char* gemm_epi_status_string(int code) {
     case GEMM_EPI_ERR_ALIGNMENT: return "alignment requirement not met";
     case GEMM_EPI_ERR_DEVICE: return "device error";
     case GEMM_EPI_ERR_LAUNCH: return "kernel launch failed";
+    case GEMM_EPI_ERR_HOST_ALLOC: return "host allocation failed";
     default: return "unknown status";
   }
 }

@@ -40,11 +40,18 @@ namespace gemm_epi {
 enum : int { T_NONE = 0, T_F16 = 1, T_BF16 = 2, T_E4M3 = 3, T_I8 = 4, T_F32 = 5, T_I32 = 6, T_E5M2 = 7 };
 // Kernel A/B codes of the fp8 pairs (A's format x B's).
 enum : int { T_E4M3_E5M2 = 8, T_E5M2_E4M3 = 9 };
+// Kernel A/B codes of fp8 operands widened to fp16 before the f16 MFMA (A's
+// format x B's), used when an fp32 output is asked for.
+enum : int { T_W_E4M3 = 10, T_W_E5M2 = 11, T_W_E4M3_E5M2 = 12, T_W_E5M2_E4M3 = 13 };
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
@@ -188,28 +195,62 @@ struct MmaF8Pair : MmaLayout32 {
 template <> struct Mma<T_E4M3_E5M2, 32> : MmaF8Pair<0, 1> {};
 template <> struct Mma<T_E5M2_E4M3, 32> : MmaF8Pair<1, 0> {};
 
+// Eight fp8 values (format F: 0 e4m3, 1 e5m2) widened to fp16.  Every finite
+// e4m3 and e5m2 value, subnormals included, is an fp16 value (e4m3: |v| <= 448,
+// steps down to 2^-9; e5m2: |v| <= 57344, steps down to 2^-16), so with a scale
+// of 1 the conversion is exact, and NaN stays NaN.  Byte i of the input is
+// element i of the result.
+template <int F>
+__device__ __forceinline__ v8h widen8(v2i x) {
+  v2h h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned w = (unsigned)(i < 2 ? x.x : x.y);
+    if constexpr (F == 0)
+      h[i] = (i & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+                     : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    else
+      h[i] = (i & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, true)
+                     : __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, false);
+  }
+  return v8h{h[0].x, h[0].y, h[1].x, h[1].y, h[2].x, h[2].y, h[3].x, h[3].y};
+}
+
+// fp8 operands (formats FA x FB) in LDS, widened to fp16 in registers for the
+// 16x16x32 f16 MFMA: the products and their fp32 sums are those of fp16
+// inputs, so fp32 outputs keep fp32's precision (the fp8 MFMA sums a group of
+// products with fewer fraction bits).  A k step is 32 bytes of an LDS row;
+// lane group q = l / 16 takes bytes [8q, 8q + 8).
+template <int FA, int FB>
+struct MmaWiden : MmaLayout16 {
+  typedef v4f acc_t;
+  typedef v2i frag_t;
+  static constexpr int ESIZE = 1, KSB = 32;
+  static __device__ __forceinline__ acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8<FA>(a), widen8<FB>(b), c, 0, 0, 0);
+  }
+};
+template <> struct Mma<T_W_E4M3, 16> : MmaWiden<0, 0> {};
+template <> struct Mma<T_W_E5M2, 16> : MmaWiden<1, 1> {};
+template <> struct Mma<T_W_E4M3_E5M2, 16> : MmaWiden<0, 1> {};
+template <> struct Mma<T_W_E5M2_E4M3, 16> : MmaWiden<1, 0> {};
+
 // Compile-time kernel configuration.
 //   BM x BN     workgroup tile (multiples of 32 per wave)
 //   ROWB        K bytes per LDS row per stage (64 or 128)
 //   WAVES_M/N   wave grid; each wave owns (BM/WAVES_M) x (BN/WAVES_N)
 //   STAGES      depth of the LDS ring
-//   LOADER      how K-major tiles reach LDS (see below)
 //   DQ          two-stage ring: quarters of a K tile's DMA issued early in
 //               step 0 of the K tile before its use (see the mainloop)
 //   BLK         MFMA output block: 32 (32x32) or 16 (16x16)
 template <int AB_, bool A_KMAJOR_, bool B_KMAJOR_, bool CD_NMAJOR_, int BM_ = 256, int BN_ = 256,
-          int ROWB_ = 128, int WAVES_M_ = 2, int WAVES_N_ = 2, int STAGES_ = 2, int LOADER_ = 0,
-          int DQ_ = 0, int BLK_ = 32>
+          int ROWB_ = 128, int WAVES_M_ = 2, int WAVES_N_ = 2, int STAGES_ = 2, int DQ_ = 0,
+          int BLK_ = 32>
 struct Cfg {
   static constexpr int BLK = BLK_;
   using MM = Mma<AB_, BLK_>;
   static constexpr int DQ = DQ_;
   static_assert(DQ >= 0 && DQ <= 4 && (STAGES_ == 2 || DQ == 0), "DQ: quarters, two-stage rings only");
-  // LOADER 0: K-major tiles go global -> LDS by buffer_load ... lds (DMA).
-  // LOADER 1: global -> VGPR by buffer_load_dwordx4, then ds_write_b128
-  //           (two register stages in flight; LDS writes use the LDS's own
-  //           port instead of the texture-data path).
-  static constexpr int LOADER = LOADER_;
   static constexpr int AB = AB_;
   static constexpr bool A_KMAJOR = A_KMAJOR_, B_KMAJOR = B_KMAJOR_, CD_NMAJOR = CD_NMAJOR_;
   static constexpr int BM = BM_, BN = BN_, ROWB = ROWB_;
@@ -222,9 +263,11 @@ struct Cfg {
   static constexpr int THREADS = NW * 64;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile
   static constexpr int FM = WM / BLK, FN = WN / BLK;         // MFMA output blocks
-  // 16-byte chunks of one k step per lane (lane group l / BLK reads chunks
-  // [q*CPL, q*CPL + CPL) of the step)
-  static constexpr int CPL = (MM::KSB / 16) / (64 / BLK);
+  // bytes of one k step per lane: lane group q = l / BLK reads bytes
+  // [q*BPL, q*BPL + BPL) of the step, i.e. CPL whole 16-byte chunks (or, for
+  // BPL = 8, half of chunk q / 2)
+  static constexpr int BPL = MM::KSB / (64 / BLK);
+  static constexpr int CPL = BPL >= 16 ? BPL / 16 : 1;
   static constexpr int STAGES = STAGES_;
   static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
   static constexpr int PIPE_BYTES = STAGES * STAGE_BYTES;
@@ -238,7 +281,8 @@ struct Cfg {
   static constexpr int LDS_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
   static constexpr int KSTEPS = ROWB / MM::KSB;
   static_assert(KSTEPS >= 1, "a stage must hold at least one MFMA k step");
-  static_assert(CPL >= 1 && CPL * 16 * (64 / BLK) == MM::KSB, "k step must split evenly over lane groups");
+  static_assert(BPL * (64 / BLK) == MM::KSB && (BPL == 8 || BPL == 16 || BPL == 32),
+                "k step must split evenly over lane groups");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32-line epilogue blocks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
 };
@@ -386,49 +430,6 @@ struct KMajorStager {
   }
 };
 
-// ---------------------------------------------------------------------------
-// Register-staged K-major operand tile (R rows x ROWB bytes): the same
-// 1 KiB-per-wave-instruction split as the DMA stager, but lane j loads the
-// natural chunk j % CH of its row into VGPRs and writes it to LDS at the
-// swizzled position itself.  Two register stages.
-// ---------------------------------------------------------------------------
-template <class CF, int R>
-struct KMajorRegStager {
-  static constexpr int NQ = R / (CF::ROWS_PER_DMA * CF::NW);
-  static_assert(NQ * CF::ROWS_PER_DMA * CF::NW == R, "rows must split evenly over the waves");
-  __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t voff[NQ];  // global byte offset (row * ld + chunk * 16)
-  uint32_t loff[NQ];  // LDS byte offset within a stage tile (swizzled)
-  uint32_t cb;        // this lane's chunk byte offset within a row
-  v4u buf[2][NQ];
-
-  __device__ __forceinline__ void setup(const char* tile_base, int64_t ld_bytes, int valid_rows,
-                                        int wave, int lane) {
-    const int rsub = lane / CF::CH;
-    const int c = lane % CF::CH;
-    cb = (uint32_t)c * 16u;
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)tile_base, (short)0,
-                                             (int)(uint32_t)((int64_t)valid_rows * ld_bytes), 0x00020000);
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int row = (q * CF::NW + wave) * CF::ROWS_PER_DMA + rsub;
-      voff[q] = (uint32_t)(row * ld_bytes) + cb;
-      loff[q] = (uint32_t)(row * CF::ROWB + ((c ^ swz<CF>(row)) << 4));
-    }
-  }
-  // Load instruction Q of K tile kt into register stage BUF (rows past the
-  // tile's valid rows and chunks at or past kvalid bytes read as zero).
-  template <int BUF, int Q>
-  __device__ __forceinline__ void load(int kt, int64_t kvalid) {
-    const uint32_t vo = (int64_t)cb < kvalid ? voff[Q] + (uint32_t)kt * (uint32_t)CF::ROWB : 0x80000000u;
-    buf[BUF][Q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vo, 0, 0));
-  }
-  template <int BUF, int Q>
-  __device__ __forceinline__ void store(char* lds, int tile_off) const {
-    *(v4u*)(lds + tile_off + loff[Q]) = buf[BUF][Q];
-  }
-};
-
 // 4x4 byte transpose: x_r holds bytes (r,0..3); c_j receives bytes (0..3, j).
 __device__ __forceinline__ void tr4x4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
                                       uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3) {
@@ -504,7 +505,7 @@ struct MMajorStager8 {
   }
 };
 
-// Fragment read: lane group q's share (CPL chunks) of k step s of LDS row
+// Fragment read: lane group q's share (BPL bytes) of k step s of LDS row
 // row0 + blk*BLK.  Rows BLK apart share their chunk swizzle (a block spans
 // whole swizzle periods), so the swizzle is taken from row0 and block blk is
 // an immediate offset from block 0's address.
@@ -514,10 +515,14 @@ __device__ __forceinline__ typename CF::MM::frag_t read_frag(const char* lds, in
   static_assert(CF::BLK % (CF::CH << CF::SWZ_SHIFT) == 0, "block rows span whole swizzle periods");
   const char* rp = lds + tile_off + row0 * CF::ROWB + blk * (CF::BLK * CF::ROWB);
   const int sw = swz<CF>(row0);
-  const int c = s * (CF::MM::KSB / 16) + q * CF::CPL;
-  if constexpr (CF::CPL == 1) {
+  if constexpr (CF::BPL == 8) {
+    const int c = s * (CF::MM::KSB / 16) + (q >> 1);
+    return *(const v2i*)(rp + ((c ^ sw) << 4) + (q & 1) * 8);
+  } else if constexpr (CF::CPL == 1) {
+    const int c = s * (CF::MM::KSB / 16) + q;
     return *(const v4i*)(rp + ((c ^ sw) << 4));
   } else {
+    const int c = s * (CF::MM::KSB / 16) + q * CF::CPL;
     static_assert(CF::CPL == 2, "one or two chunks per lane");
     const v4i lo = *(const v4i*)(rp + ((c ^ sw) << 4));
     const v4i hi = *(const v4i*)(rp + (((c + 1) ^ sw) << 4));
@@ -566,25 +571,6 @@ __device__ __forceinline__ void epi_stage_block(const ACC (&acc)[CF::FM][CF::FN]
   }
 }
 
-// ---------------------------------------------------------------------------
-// Fused epilogue of one wave: rows [mw, mw+WM), columns [nw, nw+WN) of batch
-// l.  Y = acc; D = alpha*acc + beta*C + x_factor*X in fp32 (int32, wrapping,
-// for int8 inputs), rounded to nearest-even into the output type.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void store4_f(void* p, int dt, int64_t i, v4f v) {
-  if (dt == T_F16) {
-    _Float16 h[4] = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
-    __builtin_nontemporal_store(*(const v2u*)h, (v2u*)((_Float16*)p + i));
-  } else if (dt == T_BF16) {
-    __bf16 b[4] = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
-    __builtin_nontemporal_store(*(const v2u*)b, (v2u*)((uint16_t*)p + i));
-  } else {
-    __builtin_nontemporal_store(v, (v4f*)((float*)p + i));
-  }
-}
-
-// Element work for four contiguous outputs at flat index o, given the four
-// accumulator values w and the four C and X values already loaded.
 // The clamp of the ReLU form: max(0, v), a NaN becoming 0; for int32 the
 // signed value of the wrapped sum.
 __device__ __forceinline__ v4f relu4(v4f t) {
@@ -594,161 +580,6 @@ __device__ __forceinline__ v4f relu4(v4f t) {
 __device__ __forceinline__ v4u relu4(v4u t) {
   return v4u{(int)t.x > 0 ? t.x : 0u, (int)t.y > 0 ? t.y : 0u, (int)t.z > 0 ? t.z : 0u,
              (int)t.w > 0 ? t.w : 0u};
-}
-
-// The clamp as a per-element select on the uniform flag, without a branch
-// inside the general epilogue's per-lane (divergent) element work.
-__device__ __forceinline__ v4f relu4_if(v4f t, bool on) {
-  return v4f{on && !(t.x > 0.0f) ? 0.0f : t.x, on && !(t.y > 0.0f) ? 0.0f : t.y,
-             on && !(t.z > 0.0f) ? 0.0f : t.z, on && !(t.w > 0.0f) ? 0.0f : t.w};
-}
-__device__ __forceinline__ v4u relu4_if(v4u t, bool on) {
-  return v4u{on && (int)t.x <= 0 ? 0u : t.x, on && (int)t.y <= 0 ? 0u : t.y,
-             on && (int)t.z <= 0 ? 0u : t.z, on && (int)t.w <= 0 ? 0u : t.w};
-}
-
-template <class CF>
-__device__ __forceinline__ void epi_finish4(const Params& p, int64_t o, v4f w, v4f c, v4f x) {
-  if constexpr (CF::AB == T_I8) {
-    const v4u a = __builtin_bit_cast(v4u, w);
-    v4u t = a * (unsigned)p.ialpha;
-    if (p.c_dtype) t += __builtin_bit_cast(v4u, c) * (unsigned)p.ibeta;
-    t = relu4_if(t, p.relu != 0);
-    if (p.x_dtype) t += __builtin_bit_cast(v4u, x) * (unsigned)p.ix;
-    __builtin_nontemporal_store(t, (v4u*)((int*)p.D + o));
-    if (p.y_dtype) __builtin_nontemporal_store(a, (v4u*)((int*)p.Y + o));
-  } else {
-    v4f t = w * p.alpha;
-    if (p.c_dtype) {
-      t.x = __builtin_fmaf(p.beta, c.x, t.x);
-      t.y = __builtin_fmaf(p.beta, c.y, t.y);
-      t.z = __builtin_fmaf(p.beta, c.z, t.z);
-      t.w = __builtin_fmaf(p.beta, c.w, t.w);
-    }
-    t = relu4_if(t, p.relu != 0);
-    if (p.x_dtype) {
-      t.x = __builtin_fmaf(p.xf, x.x, t.x);
-      t.y = __builtin_fmaf(p.xf, x.y, t.y);
-      t.z = __builtin_fmaf(p.xf, x.z, t.z);
-      t.w = __builtin_fmaf(p.xf, x.w, t.w);
-    }
-    store4_f(p.D, p.d_dtype, o, t);
-    if (p.y_dtype) store4_f(p.Y, p.y_dtype, o, w);
-  }
-}
-
-// Raw bits of four C (or X) elements at flat index o: 16 bytes for 4-byte
-// types, 8 bytes (in .xy) for 2-byte types.  Only the load sits under the
-// (uniform) size test, so every load of a chunk can be in flight at once.
-__device__ __forceinline__ v4u epi_raw4(const void* ptr, int dt, int64_t o) {
-  if (dt == T_F32 || dt == T_I32)
-    return __builtin_nontemporal_load((const v4u*)((const uint32_t*)ptr + o));
-  const v2u u = __builtin_nontemporal_load((const v2u*)((const uint16_t*)ptr + o));
-  return v4u{u.x, u.y, 0u, 0u};
-}
-
-// Raw bits -> four fp32 values, without branches (all decodings computed,
-// one selected by the uniform type).
-__device__ __forceinline__ v4f epi_decode4(v4u r, int dt) {
-  const v4f f32 = __builtin_bit_cast(v4f, r);
-  const v4f bf = {__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
-                  __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
-  const v2u h2 = {r.x, r.y};
-  const _Float16* h = (const _Float16*)&h2;
-  const v4f f16 = {(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-  return dt == T_F32 ? f32 : (dt == T_BF16 ? bf : f16);
-}
-
-// The accumulator is re-laid out one 32-wide block at a time through a
-// 32-line LDS region private to the wave: for N-major outputs a block row
-// (32 rows x WN columns, lines = rows), for M-major a block column (WM rows x
-// 32 columns, lines = columns).  Then each lane reads 4 contiguous elements
-// (one ds_read_b128) and does the element work for them.
-//
-// The passes of all blocks form one chain of chunks.  The C and X loads of
-// chunk c+1 are issued before the D and Y stores of chunk c: vmcnt retires
-// loads and stores in issue order, so waiting for a chunk's loads then never
-// waits for an earlier chunk's stores to reach memory, and each chunk's load
-// latency hides under the previous chunk's work.
-template <class CF, class ACC>
-__device__ __forceinline__ void epilogue(const Params& p, const ACC (&acc)[CF::FM][CF::FN], char* lds,
-                                         int wave, int lane, int l, int mw, int nw) {
-  constexpr bool NMAJ = CF::CD_NMAJOR;
-  constexpr int LINE = CF::EPI_LINE, PITCH = CF::EPI_PITCH;
-  constexpr int LPL = LINE / 4;        // lanes per line
-  constexpr int LINES_PER_PASS = 64 / LPL;
-  float* region = (float*)(lds + wave * CF::EPI_WAVE_BYTES);
-  const int64_t obase = (int64_t)l * p.M * p.N;
-  constexpr int NBLK = (NMAJ ? CF::WM : CF::WN) / 32;
-  constexpr int PASSES = 32 / LINES_PER_PASS;
-  constexpr int CMAX = CF::NW > 4 ? 4 : 8;  // two waves per SIMD: half the registers
-  constexpr int CHUNK = PASSES < CMAX ? PASSES : CMAX;
-  constexpr int CPB = PASSES / CHUNK;      // chunks per block
-  constexpr int NCH = NBLK * CPB;
-  const int sub = lane / LPL;
-  const int e = (lane % LPL) * 4;
-
-  auto write_block = [&](auto blk_c) { epi_stage_block<CF>(acc, region, lane, decltype(blk_c)::value); };
-  // Output coordinates of pass `ps` of block `blk` for this lane.
-  auto coords = [&](int blk, int ps, int64_t& o) -> bool {
-    const int line = ps * LINES_PER_PASS + sub;
-    int64_t m, n;
-    if constexpr (NMAJ) {
-      m = mw + blk * 32 + line;
-      n = nw + e;
-    } else {
-      n = nw + blk * 32 + line;
-      m = mw + e;
-    }
-    o = obase + (NMAJ ? m * p.N + n : n * p.M + m);
-    return m < p.M && n < p.N;
-  };
-  v4u cr[2][CHUNK], xr[2][CHUNK];
-  auto load_chunk = [&](auto c_c) {
-    constexpr int c = decltype(c_c)::value, B = c & 1;
-#pragma unroll
-    for (int q = 0; q < CHUNK; ++q) {
-      int64_t o;
-      const bool ok = coords(c / CPB, (c % CPB) * CHUNK + q, o);
-      cr[B][q] = v4u{};
-      xr[B][q] = v4u{};
-      if (ok) {
-        if (p.c_dtype) cr[B][q] = epi_raw4(p.C, p.c_dtype, o);
-        if (p.x_dtype) xr[B][q] = epi_raw4(p.X, p.x_dtype, o);
-      }
-    }
-  };
-  load_chunk(IntC<0>{});
-  static_for<0, NCH>([&](auto c_c) {
-    constexpr int c = decltype(c_c)::value, B = c & 1;
-    constexpr int blk = c / CPB, p0 = (c % CPB) * CHUNK;
-    if constexpr (c % CPB == 0) {
-      // this wave's reads of the previous block are issued before these
-      // writes, and LDS serves one wave's operations in order
-      write_block(IntC<blk>{});
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
-    v4f w[CHUNK];
-#pragma unroll
-    for (int q = 0; q < CHUNK; ++q)
-      w[q] = *(const v4f*)(region + ((p0 + q) * LINES_PER_PASS + sub) * PITCH + e);
-    if constexpr (c + 1 < NCH) load_chunk(IntC<c + 1>{});
-#pragma unroll
-    for (int q = 0; q < CHUNK; ++q) {
-      int64_t o;
-      const bool ok = coords(blk, p0 + q, o);
-      v4f cv, xv;
-      if constexpr (CF::AB == T_I8) {
-        cv = __builtin_bit_cast(v4f, cr[B][q]);
-        xv = __builtin_bit_cast(v4f, xr[B][q]);
-      } else {
-        cv = epi_decode4(cr[B][q], p.c_dtype);
-        xv = epi_decode4(xr[B][q], p.x_dtype);
-      }
-      if (ok) epi_finish4<CF>(p, o, w[q], cv, xv);
-    }
-  });
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -782,9 +613,8 @@ template <int T>
 __device__ __forceinline__ v4f epi_dec(v4u r, int h) {
   const uint32_t a = h ? r.z : r.x, b = h ? r.w : r.y;
   if constexpr (T == T_F16) {
-    const v2u h2 = {a, b};
-    const _Float16* f = (const _Float16*)&h2;
-    return v4f{(float)f[0], (float)f[1], (float)f[2], (float)f[3]};
+    const v4h f = __builtin_bit_cast(v4h, v2u{a, b});
+    return v4f{(float)f.x, (float)f.y, (float)f.z, (float)f.w};
   } else if constexpr (T == T_BF16) {
     return v4f{__uint_as_float(a << 16), __uint_as_float(a & 0xffff0000u), __uint_as_float(b << 16),
                __uint_as_float(b & 0xffff0000u)};
@@ -912,6 +742,126 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
       epi_st<T>(rd, o, epi_pack<T>(d0, d1));
       epi_st<T>(ry, o, epi_pack<T>(w0, w1));
     }
+  });
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue for C, X, D, Y of different element types (f16, bf16, f32): the
+// same re-layout, addressing and load-ahead as the one-type epilogue, with 4
+// elements per lane (16 bytes of a 4-byte type, 8 of a 2-byte type) and each
+// array's element size, decoding and rounding chosen by its (uniform) type,
+// so no lane takes a branch of its own.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ v4u epi_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off, bool wide) {
+  if (wide) return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, EPI_NT));
+  const v2u u = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, EPI_NT));
+  return v4u{u.x, u.y, 0u, 0u};
+}
+
+// Raw bits of four elements of type dt -> four fp32 values.
+__device__ __forceinline__ v4f epi_decode4(v4u r, int dt) {
+  if (dt == T_F32) return __builtin_bit_cast(v4f, r);
+  if (dt == T_BF16)
+    return v4f{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+               __uint_as_float(r.y & 0xffff0000u)};
+  const v4h h = __builtin_bit_cast(v4h, v2u{r.x, r.y});
+  return v4f{(float)h.x, (float)h.y, (float)h.z, (float)h.w};
+}
+
+// Rounds four fp32 values to nearest-even into type dt and stores them.
+__device__ __forceinline__ void epi_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, int dt, v4f v) {
+  if (dt == T_F16) {
+    const v4h h = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, h), r, (int)off, 0, EPI_NT);
+  } else if (dt == T_BF16) {
+    const v4bf b = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, b), r, (int)off, 0, EPI_NT);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, (int)off, 0, EPI_NT);
+  }
+}
+
+__device__ __forceinline__ int epi_shift(int dt) { return dt == T_F32 || dt == T_I32 ? 2 : 1; }
+
+template <class CF, class ACC>
+__device__ __forceinline__ void epilogue_mixed(const Params& p, const ACC (&acc)[CF::FM][CF::FN], char* lds,
+                                               int wave, int lane, int l, int mw, int nw) {
+  constexpr bool NMAJ = CF::CD_NMAJOR;
+  constexpr int LINE = CF::EPI_LINE, PITCH = CF::EPI_PITCH;
+  constexpr int VEC = 4;
+  constexpr int LPL = LINE / VEC;
+  constexpr int LINES_PER_PASS = 64 / LPL;
+  static_assert(LPL >= 1 && LPL <= 64 && 32 % LINES_PER_PASS == 0, "line split over the lanes");
+  float* region = (float*)(lds + wave * CF::EPI_WAVE_BYTES);
+  constexpr int NBLK = (NMAJ ? CF::WM : CF::WN) / 32;
+  constexpr int PASSES = 32 / LINES_PER_PASS;
+  constexpr int NP = NBLK * PASSES;
+  constexpr int DIST0 = 8;
+  constexpr int DIST = DIST0 < NP ? DIST0 : NP;
+  const int sub = lane / LPL;
+  const int e = (lane % LPL) * VEC;
+
+  const int64_t ld = NMAJ ? p.N : p.M;
+  const int64_t line0 = NMAJ ? mw : nw;
+  const int64_t nlines = NMAJ ? p.M : p.N;
+  const int64_t lines = min(max(nlines - line0, (int64_t)0), (int64_t)(NMAJ ? CF::WM : CF::WN));
+  const int64_t slab = ((int64_t)l * (NMAJ ? p.M : p.N) + line0) * ld;  // element index of the base
+  auto rsrc = [&](const void* base, int dt) {
+    const int sh = epi_shift(dt);
+    return __builtin_amdgcn_make_buffer_rsrc(base ? (void*)((const char*)base + (slab << sh)) : (void*)p.D,
+                                             (short)0, base ? (int)((lines * ld) << sh) : 0, 0x00020000);
+  };
+  const int tc = p.C ? p.c_dtype : T_F32, tx = p.X ? p.x_dtype : T_F32, td = p.d_dtype;
+  const int ty = p.Y ? p.y_dtype : T_F32;
+  const __amdgpu_buffer_rsrc_t rc = rsrc(p.C, tc), rx = rsrc(p.X, tx), rd = rsrc(p.D, td), ry = rsrc(p.Y, ty);
+  const int shc = epi_shift(tc), shx = epi_shift(tx), shd = epi_shift(td), shy = epi_shift(ty);
+  const float beta = p.C ? p.beta : 0.0f;
+  const float xf = p.X ? p.xf : 0.0f;
+  const int64_t along = (NMAJ ? nw : mw) + e;
+  const bool lane_ok = along < (NMAJ ? p.N : p.M);
+  // element offset of this lane in pass i; a lane past the other extent gets
+  // a byte offset above 2^31 in every array (outside every resource)
+  const uint32_t lane_el = (uint32_t)(sub * ld + along);
+  auto el = [&](int i) {
+    const int line = (i / PASSES) * 32 + (i % PASSES) * LINES_PER_PASS;
+    return lane_el + (uint32_t)(line * ld);
+  };
+  auto boff = [&](uint32_t eo, int sh) { return lane_ok ? eo << sh : 0x80000000u; };
+
+  auto write_block = [&](auto blk_c) { epi_stage_block<CF>(acc, region, lane, decltype(blk_c)::value); };
+
+  v4u cr[DIST + 1], xr[DIST + 1];
+  static_for<0, DIST>([&](auto i_c) {
+    constexpr int i = decltype(i_c)::value;
+    cr[i] = epi_ld4(rc, boff(el(i), shc), shc == 2);
+    xr[i] = epi_ld4(rx, boff(el(i), shx), shx == 2);
+  });
+  static_for<0, NP>([&](auto i_c) {
+    constexpr int i = decltype(i_c)::value, S = i % (DIST + 1);
+    constexpr int blk = i / PASSES, ps = i % PASSES;
+    if constexpr (ps == 0) write_block(IntC<blk>{});
+    const v4f w = *(const v4f*)(region + (ps * LINES_PER_PASS + sub) * PITCH + e);
+    if constexpr (i + DIST < NP) {
+      constexpr int SN = (i + DIST) % (DIST + 1);
+      cr[SN] = epi_ld4(rc, boff(el(i + DIST), shc), shc == 2);
+      xr[SN] = epi_ld4(rx, boff(el(i + DIST), shx), shx == 2);
+    }
+    const uint32_t eo = el(i);
+    // D = alpha * acc + beta * C (clamped at 0 in the ReLU form) + x_factor * X
+    const v4f c = epi_decode4(cr[S], tc), x = epi_decode4(xr[S], tx);
+    v4f t = w * p.alpha;
+    t.x = __builtin_fmaf(beta, c.x, t.x);
+    t.y = __builtin_fmaf(beta, c.y, t.y);
+    t.z = __builtin_fmaf(beta, c.z, t.z);
+    t.w = __builtin_fmaf(beta, c.w, t.w);
+    if (p.relu) t = relu4(t);
+    t.x = __builtin_fmaf(xf, x.x, t.x);
+    t.y = __builtin_fmaf(xf, x.y, t.y);
+    t.z = __builtin_fmaf(xf, x.z, t.z);
+    t.w = __builtin_fmaf(xf, x.w, t.w);
+    epi_st4(rd, boff(eo, shd), td, t);
+    if (p.Y) epi_st4(ry, boff(eo, shy), ty, w);
   });
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
@@ -1173,70 +1123,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
             IntC<MF>{});
     };
 
-    if constexpr (CF::A_KMAJOR && CF::LOADER == 1) {
-      // ---- K-major A, register-staged loads, two LDS stages --------------
-      // Tile kt+2 is loaded to registers during tile kt and written to LDS
-      // (stage kt+2 % 2, free since the barrier of tile kt+1) during tile
-      // kt+1, before that tile's barrier makes it visible.
-      KMajorRegStager<CF, BM> ra_;
-      KMajorRegStager<CF, BN> rb_;
-      ra_.setup(Ab + (int64_t)m0 * kbytes, kbytes, (int)min((int64_t)BM, p.M - m0), wave, lane);
-      rb_.setup(Bb + (int64_t)n0 * kbytes, kbytes, (int)min((int64_t)BN, p.N - n0), wave, lane);
-      constexpr int QA = KMajorRegStager<CF, BM>::NQ, QB = KMajorRegStager<CF, BN>::NQ;
-      auto load_tile = [&](auto buf_c, int k_tile) {
-        constexpr int BUF = decltype(buf_c)::value;
-        const int64_t kv = kbytes - (int64_t)k_tile * CF::ROWB;
-        static_for<0, QA>([&](auto q) { ra_.template load<BUF, decltype(q)::value>(k_tile, kv); });
-        static_for<0, QB>([&](auto q) { rb_.template load<BUF, decltype(q)::value>(k_tile, kv); });
-      };
-      auto store_tile = [&](auto buf_c, int st) {
-        constexpr int BUF = decltype(buf_c)::value;
-        const int off = st * CF::STAGE_BYTES;
-        static_for<0, QA>([&](auto q) { ra_.template store<BUF, decltype(q)::value>(lds, off); });
-        static_for<0, QB>([&](auto q) { rb_.template store<BUF, decltype(q)::value>(lds, off + BM * CF::ROWB); });
-      };
-      // ops of a tile's first step: write tile kt+1 (register stage WBUF) to
-      // LDS stage WST, then load tile kt+2 into register stage LBUF
-      auto first_step_ops = [&](auto wbuf_c, int wst, auto lbuf_c, int ltile, bool lload) {
-        const int woff = wst * CF::STAGE_BYTES;
-        const int64_t kv = kbytes - (int64_t)ltile * CF::ROWB;
-        return [&ra_, &rb_, woff, kv, lload, ltile, wbuf_c, lbuf_c](auto k_c) {
-          constexpr int WB = decltype(wbuf_c)::value, LB = decltype(lbuf_c)::value;
-          constexpr int K2 = decltype(k_c)::value;
-          if constexpr (K2 < QA) ra_.template store<WB, K2>(lds, woff);
-          else if constexpr (K2 < QA + QB) rb_.template store<WB, K2 - QA>(lds, woff + BM * CF::ROWB);
-          else if constexpr (K2 < 2 * QA + QB) { if (lload) ra_.template load<LB, K2 - QA - QB>(ltile, kv); }
-          else { if (lload) rb_.template load<LB, K2 - 2 * QA - QB>(ltile, kv); }
-        };
-      };
-      constexpr int NOPS1 = 2 * (QA + QB);
-      // prologue: tile 0 -> regs 0 -> LDS stage 0; tile 1 -> regs 1
-      load_tile(IntC<0>{}, 0);
-      store_tile(IntC<0>{}, 0);
-      if (1 < KT) load_tile(IntC<1>{}, 1);
-      barrier_lds();
-      load_step(fa[0], fb[0], 0, 0);
-      auto tile_iter = [&](auto par_c, int kt) {
-        constexpr int P = decltype(par_c)::value;  // kt % 2
-        const int st = P, nst = P ^ 1;
-        // step 0: write tile kt+1 (regs P^1) to stage kt+1; load tile kt+2 to regs P
-        kstep_ops(IntC<0>{}, st, 1, IntC<NOPS1>{},
-                  first_step_ops(IntC<P ^ 1>{}, nst, IntC<P>{}, kt + 2, kt + 2 < KT), IntC<MF>{});
-        static_for<1, CF::KSTEPS - 1>([&](auto s_c) {
-          constexpr int SS = decltype(s_c)::value;
-          kstep_ops(IntC<SS & 1>{}, st, SS + 1, IntC<0>{}, [](auto) {}, IntC<MF>{});
-        });
-        barrier_lds();  // tile kt+1 written and visible; stage kt no longer read
-        kstep_ops(IntC<(CF::KSTEPS - 1) & 1>{}, nst, 0, IntC<0>{}, [](auto) {}, IntC<MF>{});
-      };
-      static_assert(CF::KSTEPS >= 2, "register loader needs two k steps per tile");
-      int kt = 0;
-      for (; kt + 1 < KT; kt += 2) {
-        tile_iter(IntC<0>{}, kt);
-        tile_iter(IntC<1>{}, kt + 1);
-      }
-      if (kt < KT) tile_iter(IntC<0>{}, kt);
-    } else if constexpr (CF::A_KMAJOR) {
+    if constexpr (CF::A_KMAJOR) {
       static_assert(CF::KSTEPS % 2 == 0, "k steps alternate fragment buffers across K tiles");
       // Prologue: two stages: K tiles 0 and 1 whole, tile 0 complete.  Deep
       // ring: K tiles 0 .. S-2 whole, tile 0 complete, then part 0 of tile
@@ -1323,13 +1210,12 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     // ---- fused epilogue ---------------------------------------------------
     const int emw = m0 + wm * CF::WM, enw = n0 + wn * CF::WN;
     if constexpr (CF::AB == T_I8) {
-      if (p.epi_kind == T_I32) epilogue_typed<CF, T_I32>(p, acc, lds, wave, lane, l, emw, enw);
-      else epilogue<CF>(p, acc, lds, wave, lane, l, emw, enw);
+      epilogue_typed<CF, T_I32>(p, acc, lds, wave, lane, l, emw, enw);
     } else {
       if (p.epi_kind == T_F16) epilogue_typed<CF, T_F16>(p, acc, lds, wave, lane, l, emw, enw);
       else if (p.epi_kind == T_BF16) epilogue_typed<CF, T_BF16>(p, acc, lds, wave, lane, l, emw, enw);
       else if (p.epi_kind == T_F32) epilogue_typed<CF, T_F32>(p, acc, lds, wave, lane, l, emw, enw);
-      else epilogue<CF>(p, acc, lds, wave, lane, l, emw, enw);
+      else epilogue_mixed<CF>(p, acc, lds, wave, lane, l, emw, enw);
     }
     barrier_lds();  // LDS is reused by the next tile's prologue
   }

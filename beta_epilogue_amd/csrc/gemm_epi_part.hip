@@ -52,8 +52,8 @@ void launch(const Params& p, int grid, hipStream_t s) {
 #error "GEMM_EPI_PART out of range"
 #endif
 #define GEMM_EPI_CAT(a, b) a##b
-#define X(PART, AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, LD, DS, BL, NAME) \
-  GEMM_EPI_CAT(GEMM_EPI_PICK_, PART)(AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, LD, DS, BL)
+#define X(PART, AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, DS, BL, NAME) \
+  GEMM_EPI_CAT(GEMM_EPI_PICK_, PART)(AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, DS, BL)
 #include "gemm_epi_variants.inc"
 #undef X
 

@@ -61,7 +61,8 @@ enum {
   GEMM_EPI_ERR_UNSUPPORTED = 2, /* valid request this library does not run */
   GEMM_EPI_ERR_ALIGNMENT = 3,   /* 16-byte rule broken (extent or pointer) */
   GEMM_EPI_ERR_DEVICE = 4,      /* no usable gfx950 device / HIP query failed */
-  GEMM_EPI_ERR_LAUNCH = 5       /* the kernel launch itself failed */
+  GEMM_EPI_ERR_LAUNCH = 5,      /* the kernel launch itself failed */
+  GEMM_EPI_ERR_HOST_ALLOC = 6   /* the host-side handle could not be allocated */
 };
 
 /* Element types.  GEMM_EPI_NONE marks an absent C, X or Y. */
@@ -114,19 +115,31 @@ typedef struct gemm_epi_plan {
 
 /*
  * Validate a problem and build an immutable plan for it.
+ * Defining passages: the problem is the CuTe DSL example's module docstring
+ * ("Tensor dimensions": A M x K x L with 'k' or 'm' major, B N x K x L with
+ * 'n' or 'k' major, C/D/X/Y M x N x L with 'n' or 'm' major) checked against
+ * its "Constraints" (supported input types, one type for A and B, one
+ * majorness for C/D/X/Y, 16-byte aligned contiguous dimension); building and
+ * validating the plan once, before any launch, with an error code on failure
+ * is the Blackwell pipeline API card's "Host side" convention.
  * desc : problem description (read only, not retained).
  * out  : receives the new handle, or NULL on any error.
  * Static checks come first and need no device: sizes >= 1 and the packed
  * element counts within int64; dtype combinations; contiguous extents a
- * multiple of 16 bytes; one majorness for C/D/X/Y (by construction).  Then
+ * multiple of 16 bytes; one majorness for C/D/X/Y (by construction); a
+ * tile's rows of A and B, and its lines of C/X/D/Y, addressable with 31-bit
+ * byte offsets (GEMM_EPI_ERR_UNSUPPORTED beyond: K or the leading extent of
+ * C/X/D/Y in the millions).  Then
  * the current HIP device is queried once (compute units, architecture);
  * anything but gfx950 is GEMM_EPI_ERR_DEVICE.  Allocates only the host
- * object.  Returns GEMM_EPI_OK or an error code.
+ * object (GEMM_EPI_ERR_HOST_ALLOC if that fails).  fp8 A/B with an fp32 D or
+ * Y select kernels that widen fp8 to fp16 in registers (exact) before an
+ * f16 MFMA.  Returns GEMM_EPI_OK or an error code.
  */
 int gemm_epi_create(const gemm_epi_desc* desc, gemm_epi_handle** out);
 
 /*
- * As gemm_epi_create, but forces kernel variant `variant` (0 <=
+ * As gemm_epi_create (same passages), but forces kernel variant `variant` (0 <=
  * variant < gemm_epi_variant_count()); -1 picks the default variant.  A
  * variant that cannot run the problem is GEMM_EPI_ERR_UNSUPPORTED.
  */
@@ -136,6 +149,11 @@ int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
 /*
  * Enqueue one fused GEMM on `stream` (a hipStream_t; NULL is the null
  * stream) and return without waiting.
+ * Defining passages: the CuTe DSL example's epilogue function (every load of
+ * C and X before any store; Y is the accumulator; D = alpha * accumulator +
+ * beta * C + x_factor * X, or its clamped form) and its run() (the call goes
+ * on the caller's current stream); the Blackwell pipeline API card's "Device
+ * side" (one persistent grid walks every output tile with the same handle).
  * A, B, D  : required device pointers.
  * C, X     : read only; may be NULL only if their dtype is NONE or their
  *            scalar (beta, x_factor) is 0, in which case they are not read.
@@ -155,17 +173,21 @@ int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void* B,
                  const void* C, const void* X, void* D, void* Y, float alpha,
                  float beta, float x_factor, void* stream);
 
-/* Free a handle (NULL is fine).  No run on it may still be being enqueued. */
+/* Free a handle (NULL is fine).  No run on it may still be being enqueued.
+ * (The handle owns no device memory: the API card's "Host side" puts buffer
+ * ownership with the caller.) */
 int gemm_epi_destroy(gemm_epi_handle* h);
 
-/* Fill *out with what the handle launches. */
+/* Fill *out with what the handle launches (tile, grid and LDS sizes: the
+ * quantities the API card's "Host side" computes for its launch). */
 int gemm_epi_get_plan(const gemm_epi_handle* h, gemm_epi_plan* out);
 
 /* Number of compiled kernel variants and the name of one. */
 int gemm_epi_variant_count(void);
 const char* gemm_epi_variant_name(int variant);
 
-/* Static text for a status code ("unknown status" for anything else). */
+/* Static text for a status code ("unknown status" for anything else): the
+ * error-string function of the API card's "Host side". */
 const char* gemm_epi_status_string(int code);
 
 /* Detail of the calling thread's last error ("" if none). */

@@ -9,9 +9,9 @@ Bars (per the operation's error analysis; the pages fix no tolerance):
   * float outputs: per element
         |D - D_ref| / (|alpha| S + |beta C| + |x_factor X|) <= tol,
         |Y - Y_ref| / S <= tol,
-    S = sum_k |a||b|, tol = 1e-5 for fp32 and 1e-3 for fp16/bf16 outputs
-    (bf16 outputs: 2^-8, since bf16's own rounding step is 2^-9 relative);
-    a zero denominator demands equality.
+    S = sum_k |a||b|, tol = 1e-5 for fp32 and 1e-3 for fp16 outputs
+    (bf16 outputs: 2^-8, since bf16's own rounding step is 2^-9 relative),
+    set by the output type alone; a zero denominator demands equality.
 """
 from __future__ import annotations
 
@@ -27,13 +27,10 @@ SENTINEL = {"f16": -12345.0, "bf16": -12345.0, "f32": -12345.0,
             "i32": 0x5A5A5A5A}
 
 
-def tolerance(dtype: str, ab: str = "f16") -> float:
-    """Normalised-error bar for an output type.  fp8 inputs are held to the
-    16-bit bar even for fp32 outputs: the fp8 MFMA sums each group of
-    products with about 14 fraction bits (measured: 1 + 2^-15 -> 1,
-    448^2 + 1 -> 200704), up to ~2.2e-4 of sum|a||b| at K = 64."""
-    if ab in ("e4m3", "e5m2") and dtype == "f32":
-        return 1e-3
+def tolerance(dtype: str) -> float:
+    """Normalised-error bar for an output type, whatever the input types:
+    1e-5 for fp32, 1e-3 for fp16 and 2^-8 for bf16 outputs (bf16's own
+    rounding step, 2^-9 relative, exceeds 1e-3)."""
     return {"f32": 1e-5, "f16": 1e-3, "bf16": 2.0 ** -8}[dtype]
 
 
@@ -115,7 +112,7 @@ def check(p: synth.Problem, D_gpu, Y_gpu, Dref, Yref, S, cvals, xvals,
         assert np.all(diff[zero] == 0), "D differs where the bound is 0"
         err = np.where(zero, 0.0, diff / np.where(zero, 1.0, den))
         errd = float(err.max()) if err.size else 0.0
-        tol = tolerance(p.d, p.ab)
+        tol = tolerance(p.d)
         assert errd <= tol, "D normalised error %.3g > %.3g at %s" % (
             errd, tol, np.argmax(err))
     erry = 0.0
@@ -129,7 +126,7 @@ def check(p: synth.Problem, D_gpu, Y_gpu, Dref, Yref, S, cvals, xvals,
             assert np.all(diff[zero] == 0)
             err = np.where(zero, 0.0, diff / np.where(zero, 1.0, S))
             erry = float(err.max()) if err.size else 0.0
-            assert erry <= tolerance(p.y, p.ab), "Y normalised error %.3g" % erry
+            assert erry <= tolerance(p.y), "Y normalised error %.3g" % erry
     return errd, erry
 
 
@@ -150,8 +147,11 @@ def parity_full(p: synth.Problem, variant=-1, exact=False, ins=None):
     return errs, plan
 
 
-def sample_points(p: synth.Problem, n_random=2048, seed=7):
-    """Whole rows and columns at the edges and middle, plus random points."""
+def sample_points(p: synth.Problem, n_random=2048, seed=7, tile=256, sub=128):
+    """Whole rows and columns at the edges and middle, one random point in
+    every sub x sub quadrant of every tile x tile output tile of every batch
+    (so a tile the persistent schedule dropped, duplicated or misplaced, or a
+    wave that wrote another wave's quadrant, fails), plus random points."""
     rng = np.random.default_rng(seed)
     pts = []
     for l in sorted({0, p.L - 1}):
@@ -159,9 +159,16 @@ def sample_points(p: synth.Problem, n_random=2048, seed=7):
             pts += [(l, m, n) for n in range(p.N)]
         for n in sorted({0, p.N - 1, (p.N // 3 + 5) % p.N}):
             pts += [(l, m, n) for m in range(p.M)]
+    m0 = np.arange(0, p.M, sub)
+    n0 = np.arange(0, p.N, sub)
+    ll, mm, nn = np.meshgrid(np.arange(p.L), m0, n0, indexing="ij")
+    ll, mm, nn = ll.reshape(-1), mm.reshape(-1), nn.reshape(-1)
+    mq = mm + (rng.random(mm.size) * np.minimum(sub, p.M - mm)).astype(np.int64)
+    nq = nn + (rng.random(nn.size) * np.minimum(sub, p.N - nn)).astype(np.int64)
+    quad = np.stack([ll, mq, nq], axis=1)
     r = np.stack([rng.integers(0, p.L, n_random), rng.integers(0, p.M, n_random),
                   rng.integers(0, p.N, n_random)], axis=1)
-    pts = np.concatenate([np.asarray(pts, np.int64).reshape(-1, 3), r])
+    pts = np.concatenate([np.asarray(pts, np.int64).reshape(-1, 3), quad, r])
     return np.unique(pts, axis=0)
 
 
@@ -174,7 +181,8 @@ def flat_index(p: synth.Problem, pts):
 
 def parity_sampled(p: synth.Problem, variant=-1, n_random=2048, ins=None):
     """Full-size run, compared at sampled outputs the oracle computes one by
-    one (edge and middle rows/columns plus random points)."""
+    one (edge and middle rows/columns, a point in every quadrant of every
+    output tile, random points)."""
     ins = ins if ins is not None else synth.make_inputs(p)
     D, Y, plan = run_gpu(p, ins, variant)
     pts = sample_points(p, n_random)

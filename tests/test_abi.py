@@ -41,7 +41,7 @@ def test_measurement_library_exports_its_declared_symbol():
 
 def test_status_strings():
     assert ge.status_string(0) == "success"
-    for c in range(1, 6):
+    for c in range(1, 7):
         assert ge.status_string(c) not in ("success", "unknown status")
     assert ge.status_string(99) == "unknown status"
 
@@ -79,6 +79,7 @@ BAD = [
     (dict(N=100), ge.GEMM_EPI_ERR_ALIGNMENT),                     # f16 C/D rows
     (dict(ab="e4m3", K=8), ge.GEMM_EPI_ERR_ALIGNMENT),            # 8 B rows
     (dict(a_major="M", M=100), ge.GEMM_EPI_ERR_ALIGNMENT),
+    (dict(M=16, N=2**21, K=64), ge.GEMM_EPI_ERR_UNSUPPORTED),    # 31-bit epilogue offsets
 ]
 
 
@@ -112,22 +113,41 @@ def test_create_bad_enums():
     assert ge.lib().gemm_epi_create(ctypes.byref(desc), None) == ge.GEMM_EPI_ERR_INVALID_ARG
 
 
-def test_mixed_epilogue_types_refuse_16x16_variants():
-    """Mixed C/X/D/Y types need the general epilogue, which only the 32x32
-    variants run: forcing a 16x16 variant is an error (checked before any
-    device query), never a silent wrong path."""
+def test_mixed_epilogue_types_run_on_every_block_shape():
+    """Mixed C/X/D/Y types (the general epilogue) are accepted by 16x16- and
+    32x32-block variants alike: validation passes and, with no GPU here,
+    creation stops at the device query."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
     names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
-    v16 = names.index("bf16_kk_n_256x256_r128_w4_s2_b16")
     desc = ge.make_desc(300, 264, 128, 1, ab="bf16", c="f32", x="bf16", d="f32")
+    for v in ("bf16_kk_n_256x256_r128_w4_s2_b16", "bf16_kk_n_256x256_r128_w4_s2_q2"):
+        h = ctypes.c_void_p()
+        assert ge.lib().gemm_epi_create_variant(ctypes.byref(desc), names.index(v),
+                                                ctypes.byref(h)) == ge.GEMM_EPI_ERR_DEVICE
+        assert h.value is None
+
+
+def test_fp8_with_fp32_outputs_only_on_widening_variants():
+    """fp8 A/B with an fp32 D or Y run the kernels that widen fp8 to fp16: an
+    fp8-MFMA variant refuses such a problem, a widening one accepts it, and a
+    widening one refuses fp8 problems without fp32 outputs."""
+    names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
+    f8 = names.index("e4m3_kk_n_256x256_r128_w4_s2")
+    w = names.index("e4m3w_kk_n_256x256_r128_w4_s2_b16")
     h = ctypes.c_void_p()
-    assert ge.lib().gemm_epi_create_variant(ctypes.byref(desc), v16, ctypes.byref(h)) == \
-        ge.GEMM_EPI_ERR_UNSUPPORTED
-    assert "mixed-type" in ge.last_error()
-    desc = ge.make_desc(300, 264, 128, 1, ab="bf16", c="f32", x="f32", d="f32")
-    assert ge.lib().gemm_epi_create_variant(ctypes.byref(desc), v16, ctypes.byref(h)) in \
-        (ge.GEMM_EPI_OK, ge.GEMM_EPI_ERR_DEVICE)
-    if h.value:
-        ge.lib().gemm_epi_destroy(h)
+    for d, y, v, ok in (("f32", None, f8, False), ("f16", "f32", f8, False),
+                        ("f32", None, w, True), ("f16", "f32", w, True),
+                        ("f16", None, w, False), ("f16", None, f8, True)):
+        desc = ge.make_desc(256, 256, 256, 1, ab="e4m3", c="f16", d=d, y=y)
+        rc = ge.lib().gemm_epi_create_variant(ctypes.byref(desc), v, ctypes.byref(h))
+        if ok:
+            assert rc in (ge.GEMM_EPI_OK, ge.GEMM_EPI_ERR_DEVICE), (d, y, names[v])
+            if h.value:
+                ge.lib().gemm_epi_destroy(h)
+        else:
+            assert rc == ge.GEMM_EPI_ERR_UNSUPPORTED, (d, y, names[v], rc)
 
 
 def test_unsupported_layout_is_an_error_not_a_fallback():

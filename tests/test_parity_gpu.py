@@ -87,24 +87,28 @@ EDGE = [
 ]
 
 
-def test_general_epilogue_routing_and_ragged_n():
-    """Mixed C/X/D/Y types run the general epilogue, on 32x32-block variants
-    only: the default picks one and a forced 16x16 variant is refused.  Linear
-    and ReLU forms, a ragged N tile, with and without Y, batched."""
+def test_general_epilogue_both_block_shapes_ragged_n():
+    """Mixed C/X/D/Y types run the general epilogue on the 16x16-block default
+    and on a 32x32-block variant alike: linear and ReLU forms, a ragged N
+    tile, with and without Y, batched.  (M = 191, N = 344 with f32 C and bf16
+    D/Y once gave wrong values with 16x16 blocks; the packing of 2-byte
+    results went through a pointer of another type.)"""
     import beta_epilogue_amd as ge
     names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
-    for epi in ("linear", "relu"):
-        for y in (None, "bf16"):
-            p = CFG[1].replace(name="general_%s_%s" % (epi, y), M=191, N=344, K=200, L=2,
-                               c="f32", x="bf16", y=y, x_factor=0.5,
-                               beta=-1.0 if epi == "relu" else 1.0, epilogue=epi, seed=7070)
-            _say("case", p.name)
-            _, plan = parity_full(p)
-            assert plan["name"] == "bf16_kk_n_256x256_r128_w4_s2_q2", plan["name"]
-    with pytest.raises(ge.GemmEpiError) as e:
-        ge.FusedGemm(300, 264, 128, ab="bf16", c="f32", x="bf16", d="f32",
-                     variant=names.index("bf16_kk_n_256x256_r128_w4_s2_b16"))
-    assert e.value.code == ge.GEMM_EPI_ERR_UNSUPPORTED
+    for v in ("bf16_kk_n_256x256_r128_w4_s2_b16", "bf16_kk_n_256x256_r128_w4_s2_q2"):
+        for epi in ("linear", "relu"):
+            for y in (None, "bf16"):
+                p = CFG[1].replace(name="general_%s_%s_%s" % (v, epi, y), M=191, N=344, K=200,
+                                   L=2, c="f32", x="bf16", y=y, d="bf16" if y else "f32",
+                                   x_factor=0.5, beta=-1.0 if epi == "relu" else 1.0,
+                                   epilogue=epi, seed=7070)
+                _say("case", p.name)
+                _, plan = parity_full(p, variant=names.index(v))
+                assert plan["name"] == v
+    p = CFG[1].replace(name="general_default", M=191, N=344, K=200, c="f32", x="bf16",
+                       y="bf16", d="bf16", x_factor=0.5, seed=7071)
+    _, plan = parity_full(p)
+    assert plan["name"] == "bf16_kk_n_256x256_r128_w4_s2_b16", plan["name"]
 
 
 @pytest.mark.parametrize("p", EDGE, ids=[e.name for e in EDGE])
@@ -112,6 +116,190 @@ def test_parity_edge_cases(p):
     _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
     (ed, ey), plan = parity_full(p)
     _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+# The ReLU form D = max(0, alpha*A.B^T + beta*C) + x_factor*X: mixed-sign
+# sums so both sides of the clamp occur; typed epilogues (f16, f32, int32)
+# and the mixed-type one, both majornesses.
+RELU = [
+    small(CFG[2], 600, 520, 392).replace(name="relu_f16_cxdy", epilogue="relu", seed=7200),
+    small(CFG[2], 264, 392, 136).replace(name="relu_f16_mmajor", cd_major="M",
+                                         epilogue="relu", seed=7300),
+    small(CFG[1], 592, 528, 392).replace(name="relu_bf16_f32", alpha=1.0, beta=-1.0,
+                                         epilogue="relu", seed=7400),
+    small(CFG[3], 592, 528, 400, L=2).replace(name="relu_i8_mmajorA", beta=-1.0,
+                                              epilogue="relu", seed=7500),
+    CFG[3].replace(name="relu_i8_kmajor_xy", M=260, N=264, K=160, L=1, a_major="K",
+                   x="i32", y="i32", alpha=-3.0, beta=2.0, x_factor=5.0, dist_x="i1000",
+                   epilogue="relu", seed=7600),
+    CFG[4].replace(name="relu_e4m3_mixed", M=260, N=264, K=256, x="bf16", y="f32",
+                   x_factor=-1.5, beta=-1.0, epilogue="relu", seed=7700),
+]
+
+
+@pytest.mark.parametrize("p", RELU, ids=[e.name for e in RELU])
+def test_parity_relu(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
+    (ed, ey), plan = parity_full(p)
+    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_parity_relu_full_size_sampled():
+    """The 8192^3 fp16 workload in the ReLU form, at the bench's launch."""
+    p = CFG[2].replace(name="f16_8192_fused_cxdy_relu", epilogue="relu")
+    _say("case", p.name)
+    (ed, ey), plan, npts = parity_sampled(p)
+    _say("  plan", plan["name"], "points", npts, "err D %.3g Y %.3g" % (ed, ey))
+
+
+# D == C in place: bit-identical to the out-of-place run, and within the bar
+# of the oracle, for typed (f16, int32) and mixed-type epilogues.  Every C
+# element is loaded by the lane that later stores its D (the example's
+# epilogue: all loads before any store).
+INPLACE = [
+    small(CFG[2], 600, 520, 392).replace(name="inplace_f16", seed=7800),
+    small(CFG[2], 264, 392, 136).replace(name="inplace_f16_relu_mmajor", cd_major="M",
+                                         epilogue="relu", seed=7850),
+    small(CFG[3], 592, 528, 400, L=2).replace(name="inplace_i32", seed=7900),
+    CFG[1].replace(name="inplace_mixed", M=300, N=264, K=128, d="f32", c="f32", x="bf16",
+                   x_factor=0.5, seed=7950),
+]
+
+
+@pytest.mark.parametrize("p", INPLACE, ids=[e.name for e in INPLACE])
+def test_inplace_d_is_c(p):
+    import beta_epilogue_amd as ge
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
+    ins = synth.make_inputs(p)
+    D_out, Y_out, _ = run_gpu(p, ins)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in ins.items()}
+    g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, a_major=p.a_major, b_major=p.b_major,
+                     cd_major=p.cd_major, c=p.c, x=p.x, d=p.d, y=p.y, epilogue=p.epilogue)
+    CD = dev["C"].clone()
+    Y = torch.empty_like(Y_out, device="cuda") if p.y else None
+    g(dev["A"], dev["B"], CD, dev["X"], D=CD, Y=Y, alpha=p.alpha, beta=p.beta,
+      x_factor=p.x_factor)
+    torch.cuda.synchronize()
+    g.close()
+    assert torch.equal(CD.cpu().view(torch.uint8), D_out.view(torch.uint8)), "in place != out of place"
+    if p.y:
+        assert torch.equal(Y.cpu().view(torch.uint8), Y_out.view(torch.uint8))
+    (ed, ey), _ = parity_full(p, ins=ins)
+    _say("  err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_aliasing_rules():
+    """Every overlap other than D == C (with C read, same type) is refused
+    before launch: D or Y on X, Y on C, Y on D, D on an unread C."""
+    import beta_epilogue_amd as ge
+    p = small(CFG[2], 256, 256, 64)
+    ins = synth.make_inputs(p)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in ins.items()}
+    g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, c=p.c, x=p.x, d=p.d, y=p.y)
+    D = torch.empty_like(dev["C"])
+    for kw in (dict(D=dev["X"], Y=D), dict(D=D, Y=dev["X"]), dict(D=D, Y=dev["C"]),
+               dict(D=D, Y=D)):
+        with pytest.raises(ge.GemmEpiError) as e:
+            g(dev["A"], dev["B"], dev["C"], dev["X"], alpha=p.alpha, beta=p.beta,
+              x_factor=p.x_factor, **kw)
+        assert e.value.code == ge.GEMM_EPI_ERR_INVALID_ARG
+    # D == C with beta == 0 (C not read) is not an in-place update
+    with pytest.raises(ge.GemmEpiError) as e:
+        g(dev["A"], dev["B"], dev["C"], dev["X"], D=dev["C"], Y=D, alpha=1.0, beta=0.0,
+          x_factor=p.x_factor)
+    assert e.value.code == ge.GEMM_EPI_ERR_INVALID_ARG
+    g.close()
+    # D == C with a C of another element type is refused too
+    g = ge.FusedGemm(256, 256, 64, ab="f16", c="f32", d="f16")
+    c32 = torch.zeros(256 * 256 * 2, dtype=torch.float16, device="cuda")
+    with pytest.raises(ge.GemmEpiError) as e:
+        g(dev["A"], dev["B"], c32, D=c32, alpha=1.0, beta=1.0)
+    assert e.value.code == ge.GEMM_EPI_ERR_INVALID_ARG
+    g.close()
+
+
+# fp8 e5m2 A/B (format selectors 1/1 of the f8f6f4 MFMA): the e4m3 workload's
+# shapes and outputs with e5m2 values of |v| <= 4; the f32-output case runs
+# the widening kernels.
+E5M2 = [
+    small(CFG[4], 600, 528, 400).replace(name="e5m2_f16out", ab="e5m2", dist_ab="e5m2tab",
+                                         seed=8100),
+    CFG[4].replace(name="e5m2_mmajor_cd", M=264, N=296, K=160, cd_major="M", ab="e5m2",
+                   dist_ab="e5m2tab", seed=8200),
+    CFG[4].replace(name="e5m2_f32_xy", M=260, N=264, K=256, d="f32", c="f32", x="bf16",
+                   y="f32", x_factor=-1.5, ab="e5m2", dist_ab="e5m2tab", seed=8300),
+    CFG[4].replace(name="e5m2_relu", M=260, N=264, K=256, ab="e5m2", dist_ab="e5m2tab",
+                   beta=-1.0, epilogue="relu", seed=8400),
+]
+
+
+@pytest.mark.parametrize("p", E5M2, ids=[e.name for e in E5M2])
+def test_parity_e5m2(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
+    (ed, ey), plan = parity_full(p)
+    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+# fp8 pairs: A e4m3 with B e5m2 and the reverse (per-operand format
+# selectors, or per-operand widening with fp32 outputs).
+F8PAIRS = [
+    small(CFG[4], 600, 528, 400).replace(name="e4m3_x_e5m2", b_ab="e5m2", dist_b="e5m2tab",
+                                         seed=8600),
+    small(CFG[4], 600, 528, 400).replace(name="e5m2_x_e4m3", ab="e5m2", dist_ab="e5m2tab",
+                                         b_ab="e4m3", dist_b="e4m3tab", seed=8700),
+    CFG[4].replace(name="e4m3_x_e5m2_f32_xy", M=260, N=264, K=256, d="f32", c="f32", x="bf16",
+                   y="f32", x_factor=-1.5, b_ab="e5m2", dist_b="e5m2tab", seed=8800),
+    CFG[4].replace(name="e4m3_x_e5m2_mmajor", M=264, N=296, K=160, cd_major="M", b_ab="e5m2",
+                   dist_b="e5m2tab", seed=8900),
+    CFG[4].replace(name="e5m2_x_e4m3_mmajor_relu", M=264, N=296, K=160, cd_major="M",
+                   ab="e5m2", dist_ab="e5m2tab", b_ab="e4m3", dist_b="e4m3tab", beta=-1.0,
+                   epilogue="relu", seed=8950),
+]
+
+
+@pytest.mark.parametrize("p", F8PAIRS, ids=[e.name for e in F8PAIRS])
+def test_parity_fp8_pairs(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.ab, p.b_ab)
+    (ed, ey), plan = parity_full(p)
+    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_parity_e5m2_full_size_sampled():
+    p = CFG[4].replace(name="e5m2_8192_f16out", ab="e5m2", dist_ab="e5m2tab", seed=8500)
+    _say("case", p.name)
+    (ed, ey), plan, npts = parity_sampled(p)
+    _say("  plan", plan["name"], "points", npts, "err D %.3g Y %.3g" % (ed, ey))
+
+
+# fp8 inputs with fp32 outputs run the kernels that widen fp8 to fp16 (exact)
+# before an f16 MFMA: held to the fp32 bar, 1e-5, like every fp32 output.
+FP8_F32 = [
+    CFG[4].replace(name="e4m3_f32_out", M=600, N=528, K=400, d="f32", c="f32", seed=8910),
+    CFG[4].replace(name="e4m3_f32_y_only", M=264, N=296, K=1024, d="f16", y="f32", seed=8920),
+    CFG[4].replace(name="e4m3_f32_mmajor", M=264, N=296, K=160, cd_major="M", d="f32",
+                   c="f32", x="f32", x_factor=0.75, y="f32", seed=8930),
+    CFG[4].replace(name="e5m2_f32_out_k_tail", M=300, N=264, K=144, ab="e5m2",
+                   dist_ab="e5m2tab", d="f32", c="f16", seed=8940),
+]
+
+
+@pytest.mark.parametrize("p", FP8_F32, ids=[e.name for e in FP8_F32])
+def test_parity_fp8_fp32_outputs(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.ab, p.d, p.y)
+    (ed, ey), plan = parity_full(p)
+    assert "w_" in plan["name"], plan["name"]
+    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_parity_more_tiles_than_compute_units():
+    """Whole-output parity on a launch with more tiles (320) than workgroups:
+    every workgroup walks several tiles of several batches."""
+    p = CFG[2].replace(name="f16_2048x5_k64", M=2048, N=2048, K=64, L=5, seed=8990)
+    _say("case", p.name)
+    (ed, ey), plan = parity_full(p)
+    assert plan["tiles"] > plan["grid"], plan
+    _say("  plan", plan["name"], "grid", plan["grid"], "tiles", plan["tiles"],
+         "err D %.3g Y %.3g" % (ed, ey))
 
 
 def test_beta_zero_does_not_read_c():
@@ -139,6 +327,13 @@ def test_every_variant_runs():
         "e5e4": CFG[4].replace(M=264, N=272, K=144, L=2, ab="e5m2", dist_ab="e5m2tab",
                                b_ab="e4m3", dist_b="e4m3tab"),
         "i8": CFG[3].replace(M=272, N=264, K=144, L=2),
+        "e4m3w": CFG[4].replace(M=264, N=272, K=144, L=2, d="f32", c="f32"),
+        "e5m2w": CFG[4].replace(M=264, N=272, K=144, L=2, ab="e5m2", dist_ab="e5m2tab",
+                                d="f16", y="f32"),
+        "e4e5w": CFG[4].replace(M=264, N=272, K=144, L=2, b_ab="e5m2", dist_b="e5m2tab",
+                                d="f32"),
+        "e5e4w": CFG[4].replace(M=264, N=272, K=144, L=2, ab="e5m2", dist_ab="e5m2tab",
+                                b_ab="e4m3", dist_b="e4m3tab", d="f32", x="f32", x_factor=0.5),
     }
     for i, name in enumerate(names):
         ab, layout = name.split("_")[0], name.split("_")[1:3]
