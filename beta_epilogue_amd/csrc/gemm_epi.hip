@@ -169,28 +169,33 @@ static int validate_desc(const gemm_epi_desc* d) {
   return GEMM_EPI_OK;
 }
 
-// The kernel's A/B code: the common type, or an fp8 pair.  fp8 inputs with an
-// fp32 D or Y run the kernels that widen fp8 to fp16 before an f16 MFMA (exact
-// conversion, fp32 sums), so the fp32 outputs keep fp32's precision.
-static int kernel_ab(const gemm_epi_desc* d) {
-  const int a = d->ab_dtype;
-  const int b = d->b_dtype == GEMM_EPI_NONE ? a : d->b_dtype;
-  const bool f8 = (a == GEMM_EPI_E4M3 || a == GEMM_EPI_E5M2) && (b == GEMM_EPI_E4M3 || b == GEMM_EPI_E5M2);
-  if (f8 && (d->d_dtype == GEMM_EPI_F32 || d->y_dtype == GEMM_EPI_F32)) {
-    if (a == b) return a == GEMM_EPI_E4M3 ? gemm_epi::T_W_E4M3 : gemm_epi::T_W_E5M2;
-    return a == GEMM_EPI_E4M3 ? gemm_epi::T_W_E4M3_E5M2 : gemm_epi::T_W_E5M2_E4M3;
-  }
+// A/B types of a problem: A's, and B's (A's unless an fp8 pair).
+static int b_type(const gemm_epi_desc* d) { return d->b_dtype == GEMM_EPI_NONE ? d->ab_dtype : d->b_dtype; }
+static bool is_fp8(int t) { return t == GEMM_EPI_E4M3 || t == GEMM_EPI_E5M2; }
+
+// The fp8-MFMA kernel code of a problem: the common type or an fp8 pair.
+static int exact_ab(const gemm_epi_desc* d) {
+  const int a = d->ab_dtype, b = b_type(d);
   if (a == b) return a;
   if (a == GEMM_EPI_E4M3 && b == GEMM_EPI_E5M2) return gemm_epi::T_E4M3_E5M2;
   if (a == GEMM_EPI_E5M2 && b == GEMM_EPI_E4M3) return gemm_epi::T_E5M2_E4M3;
   return -1;
 }
 
+// Whether variant v runs the problem.  fp8 A/B with an fp32 D or Y run only
+// the kernels that widen fp8 to fp16 before an f16 MFMA (exact conversion,
+// fp32 sums), so the fp32 outputs keep fp32's precision; other fp8 problems
+// run an fp8-MFMA kernel of their pairing and layout, or, for the pairings
+// and layouts that have none, a widening kernel.
 static bool variant_fits(const Variant& v, const gemm_epi_desc* d) {
-  return v.ab == kernel_ab(d) && v.a_major == d->a_major && v.b_major == d->b_major &&
-         v.cd_major == d->cd_major;
+  if (v.a_major != d->a_major || v.b_major != d->b_major || v.cd_major != d->cd_major) return false;
+  if (is_fp8(d->ab_dtype) && is_fp8(b_type(d))) {
+    const bool f32_out = d->d_dtype == GEMM_EPI_F32 || d->y_dtype == GEMM_EPI_F32;
+    if (v.ab == gemm_epi::T_W_F8) return true;
+    return !f32_out && v.ab == exact_ab(d);
+  }
+  return v.ab == exact_ab(d);
 }
-
 
 extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
                                        gemm_epi_handle** out) {
@@ -221,6 +226,11 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   if ((int64_t)v.bm * desc->K * es >= (int64_t(1) << 31) ||
       (int64_t)v.bn * desc->K * es >= (int64_t(1) << 31))
     return fail(GEMM_EPI_ERR_UNSUPPORTED, "K too large for 32-bit tile offsets");
+  // An M-major A or N-major B is addressed with 32-bit offsets over all of K.
+  const int64_t kpad = desc->K + 2 * (int64_t)v.bk;
+  if ((desc->a_major == GEMM_EPI_MAJOR_M && kpad * desc->M * es >= (int64_t(1) << 31)) ||
+      (desc->b_major == GEMM_EPI_MAJOR_N && kpad * desc->N * es >= (int64_t(1) << 31)))
+    return fail(GEMM_EPI_ERR_UNSUPPORTED, "M-major A / N-major B larger than 2 GiB per batch");
   // The epilogue addresses a wave's output lines (at most a tile's BM or BN
   // lines of the leading extent) with 31-bit byte offsets.
   const int64_t ld = desc->cd_major == GEMM_EPI_MAJOR_N ? desc->N : desc->M;
@@ -319,6 +329,8 @@ extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void*
   p.ix = int_path ? (int32_t)x_factor : 0;
   p.xcd_remap = (h->grid % 8 == 0) ? 1 : 0;
   p.relu = d.epilogue == GEMM_EPI_RELU ? 1 : 0;
+  p.f8a = d.ab_dtype == GEMM_EPI_E5M2 ? 1 : 0;
+  p.f8b = b_type(&d) == GEMM_EPI_E5M2 ? 1 : 0;
   // Element type shared by every C/X/D/Y in use (one-type epilogue), else 0
   // (mixed-type epilogue).
   int kind = d.d_dtype;

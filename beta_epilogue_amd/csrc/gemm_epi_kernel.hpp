@@ -34,15 +34,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gemm_epi {
 
 // Element type codes; the same numbers as the public header.
 enum : int { T_NONE = 0, T_F16 = 1, T_BF16 = 2, T_E4M3 = 3, T_I8 = 4, T_F32 = 5, T_I32 = 6, T_E5M2 = 7 };
 // Kernel A/B codes of the fp8 pairs (A's format x B's).
 enum : int { T_E4M3_E5M2 = 8, T_E5M2_E4M3 = 9 };
-// Kernel A/B codes of fp8 operands widened to fp16 before the f16 MFMA (A's
-// format x B's), used when an fp32 output is asked for.
-enum : int { T_W_E4M3 = 10, T_W_E5M2 = 11, T_W_E4M3_E5M2 = 12, T_W_E5M2_E4M3 = 13 };
+// Kernel A/B code of fp8 operands (any pairing, formats chosen at run time)
+// widened to fp16 before the f16 MFMA: used when an fp32 output is asked for,
+// and for the fp8 pairings and layouts no fp8-MFMA kernel is built for.
+enum : int { T_W_F8 = 10 };
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -77,6 +80,7 @@ struct Params {
   int32_t xcd_remap;          // grid is a multiple of 8: remap ids per XCD
   int32_t epi_kind;           // element type shared by every C/X/D/Y in use (0: mixed)
   int32_t relu;               // D = max(0, alpha*acc + beta*C) + x_factor*X
+  int32_t f8a, f8b;           // widening kernels: fp8 format of A, B (0 e4m3, 1 e5m2)
 };
 
 // ---------------------------------------------------------------------------
@@ -216,24 +220,27 @@ __device__ __forceinline__ v8h widen8(v2i x) {
   return v8h{h[0].x, h[0].y, h[1].x, h[1].y, h[2].x, h[2].y, h[3].x, h[3].y};
 }
 
-// fp8 operands (formats FA x FB) in LDS, widened to fp16 in registers for the
-// 16x16x32 f16 MFMA: the products and their fp32 sums are those of fp16
-// inputs, so fp32 outputs keep fp32's precision (the fp8 MFMA sums a group of
-// products with fewer fraction bits).  A k step is 32 bytes of an LDS row;
-// lane group q = l / 16 takes bytes [8q, 8q + 8).
-template <int FA, int FB>
+// fp8 operands in LDS, widened to fp16 in registers for the 16x16x32 f16
+// MFMA: the products and their fp32 sums are those of fp16 inputs, so fp32
+// outputs keep fp32's precision (the fp8 MFMA sums a group of products with
+// fewer fraction bits).  The formats of A and B (Params::f8a, f8b) are
+// uniform run-time values: each conversion computes both decodings and keeps
+// one, so one kernel serves every pairing.  A k step is 32 bytes of an LDS
+// row; lane group q = l / 16 takes bytes [8q, 8q + 8).
+__device__ __forceinline__ v8h widen8(v2i x, bool e5m2) {
+  const v8h a = widen8<0>(x), b = widen8<1>(x);
+  return e5m2 ? b : a;
+}
 struct MmaWiden : MmaLayout16 {
   typedef v4f acc_t;
-  typedef v2i frag_t;
+  typedef v4i frag_t;  // eight fp16 values, after widening
   static constexpr int ESIZE = 1, KSB = 32;
   static __device__ __forceinline__ acc_t mma(frag_t a, frag_t b, acc_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8<FA>(a), widen8<FB>(b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c,
+                                                  0, 0, 0);
   }
 };
-template <> struct Mma<T_W_E4M3, 16> : MmaWiden<0, 0> {};
-template <> struct Mma<T_W_E5M2, 16> : MmaWiden<1, 1> {};
-template <> struct Mma<T_W_E4M3_E5M2, 16> : MmaWiden<0, 1> {};
-template <> struct Mma<T_W_E5M2_E4M3, 16> : MmaWiden<1, 0> {};
+template <> struct Mma<T_W_F8, 16> : MmaWiden {};
 
 // Compile-time kernel configuration.
 //   BM x BN     workgroup tile (multiples of 32 per wave)
@@ -250,6 +257,10 @@ struct Cfg {
   static constexpr int BLK = BLK_;
   using MM = Mma<AB_, BLK_>;
   static constexpr int DQ = DQ_;
+  // fp8 widened to fp16: an LDS fragment (8 bytes per lane) becomes a register
+  // fragment of eight fp16 values
+  static constexpr bool WIDEN = AB_ == T_W_F8;
+  using RAW = typename std::conditional<WIDEN, v2i, typename MM::frag_t>::type;
   static_assert(DQ >= 0 && DQ <= 4 && (STAGES_ == 2 || DQ == 0), "DQ: quarters, two-stage rings only");
   static constexpr int AB = AB_;
   static constexpr bool A_KMAJOR = A_KMAJOR_, B_KMAJOR = B_KMAJOR_, CD_NMAJOR = CD_NMAJOR_;
@@ -271,13 +282,14 @@ struct Cfg {
   static constexpr int STAGES = STAGES_;
   static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
   static constexpr int PIPE_BYTES = STAGES * STAGE_BYTES;
-  // epilogue: per wave, 32 lines of the block being re-laid out
-  static constexpr int EPI_LINE = CD_NMAJOR ? WN : WM;
+  // epilogue: per wave, 32 lines of the block being re-laid out; lines are
+  // rows (N-major C/D: WN floats each) or columns (M-major: WM floats)
+  static constexpr int epi_line(bool nmaj) { return nmaj ? WN : WM; }
   // words; N-major: the lane groups of one accumulator write (rows 4 apart)
   // land on disjoint banks
-  static constexpr int EPI_PITCH = EPI_LINE + (CD_NMAJOR && BLK == 32 ? 8 : 4);
-  static constexpr int EPI_WAVE_BYTES = 32 * EPI_PITCH * 4;
-  static constexpr int EPI_BYTES = NW * EPI_WAVE_BYTES;
+  static constexpr int epi_pitch(bool nmaj) { return epi_line(nmaj) + (nmaj && BLK == 32 ? 8 : 4); }
+  static constexpr int epi_wave_bytes(bool nmaj) { return 32 * epi_pitch(nmaj) * 4; }
+  static constexpr int EPI_BYTES = NW * epi_wave_bytes(CD_NMAJOR);
   static constexpr int LDS_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
   static constexpr int KSTEPS = ROWB / MM::KSB;
   static_assert(KSTEPS >= 1, "a stage must hold at least one MFMA k step");
@@ -325,17 +337,16 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 // ---------------------------------------------------------------------------
-// Staging of a K-major operand tile (R rows x ROWB bytes) straight into LDS.
-// One wave instruction moves 64 chunks = 1 KiB of LDS, written linearly:
-// lane j fills physical chunk j % CH of row j / CH, so it fetches the logical
-// chunk (j % CH) ^ swz(row) from global memory.
+// Operand tiles in LDS.  Each operand (A: BM rows, B: BN rows) owns a region
+// of STAGES stages; a stage holds one K tile of BK elements.  The DMA that
+// fills a stage is issued through inline asm on purpose: the compiler tracks
+// LDS DMA it emits itself and then waits for every outstanding VMEM
+// operation before any later LDS read, which would drain the whole ring
+// each K tile.  Completion is tracked with counted vmcnt waits followed by a
+// workgroup barrier.  One wave instruction moves 64 chunks of 16 bytes = 1
+// KiB, written to LDS linearly; the swizzle of a layout is applied on the
+// global side (lane j fetches whichever chunk belongs in LDS chunk j).
 // ---------------------------------------------------------------------------
-//
-// The DMA is issued through inline asm on purpose: the compiler tracks LDS
-// DMA it emits itself and then waits for every outstanding VMEM operation
-// before any later LDS read, which would drain the whole ring each K tile.
-// Completion is instead tracked here with counted vmcnt waits followed by a
-// workgroup barrier.
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds_addr, uint32_t voff) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
@@ -372,8 +383,17 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t nbytes) {
   return r;
 }
 
-template <class CF, int R>
-struct KMajorStager {
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// K-major operand (A 'K' or B 'K'): R rows x ROWB bytes of K per stage; the
+// 16-byte chunk c of row r is stored at c ^ swz(r).  Rows past the matrix
+// read as zero through the buffer's range check (its extent ends with the
+// tile's last row), chunks past K through an out-of-range offset.
+// ---------------------------------------------------------------------------
+template <class CF, int R, int WR>
+struct KMajorOperand {
   static constexpr int NQ = R / (CF::ROWS_PER_DMA * CF::NW);
   static_assert(NQ * CF::ROWS_PER_DMA * CF::NW == R, "rows must split evenly over the waves");
   // Consecutive instructions of one wave are NW*ROWS_PER_DMA rows apart, a
@@ -382,153 +402,191 @@ struct KMajorStager {
   static_assert((CF::NW * CF::ROWS_PER_DMA) % (CF::CH << CF::SWZ_SHIFT) == 0,
                 "one chunk offset per lane for all instructions");
   v4i rsrc;
-  uint32_t voff[NQ];
-  uint32_t cb;  // byte offset of this lane's logical chunk within its row
+  uint32_t voff;   // global byte offset of this lane's chunk in instruction 0
+  uint32_t qstep;  // bytes between consecutive instructions (NW * ROWS_PER_DMA rows)
+  uint32_t cb;     // byte offset of this lane's logical chunk within its row
+  int row0, q;     // reader: LDS row of this lane in block 0, its k share
 
-  __device__ __forceinline__ void setup(const char* tile_base, int64_t ld_bytes, int valid_rows,
-                                        int wave, int lane) {
+  // batch: the operand's batch l; extent: M (A) or N (B); r0: the tile's
+  // first row.
+  __device__ __forceinline__ void setup(const char* batch, int64_t extent, int64_t K, int r0, int wave,
+                                        int lane) {
+    const int64_t ld_bytes = K * CF::MM::ESIZE;
     const int rsub = lane / CF::CH;
     const int pc = lane % CF::CH;
-    rsrc = make_rsrc(tile_base, (uint32_t)((int64_t)valid_rows * ld_bytes));
+    const int valid_rows = (int)min((int64_t)R, extent - r0);
+    rsrc = make_rsrc(batch + (int64_t)r0 * ld_bytes, (uint32_t)((int64_t)valid_rows * ld_bytes));
     cb = (uint32_t)((pc ^ swz<CF>(wave * CF::ROWS_PER_DMA + rsub)) * 16);
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int row = (q * CF::NW + wave) * CF::ROWS_PER_DMA + rsub;
-      voff[q] = (uint32_t)(row * ld_bytes) + cb;
-    }
+    voff = (uint32_t)((wave * CF::ROWS_PER_DMA + rsub) * ld_bytes) + cb;
+    qstep = (uint32_t)(CF::NW * CF::ROWS_PER_DMA * ld_bytes);
+  }
+  // rbase: first row of this wave's blocks within the tile.
+  __device__ __forceinline__ void setup_reader(int rbase, int lane) {
+    row0 = rbase + lane % CF::BLK;
+    q = lane / CF::BLK;
   }
 
-  // Issue instructions [Q0, Q1) of the loads of K tile kt into LDS at byte
-  // address lds_addr (LDS address space).  kvalid = bytes of K left from
-  // this K tile on; chunks at or past it get an out-of-range offset and read
-  // as zero.
-  // Instruction Q of a K tile: LDS byte address sbase + REGION + Q*NW KiB
-  // (sbase = the stage's address plus this wave's KiB), global offset kofs
-  // into each row.  GUARD: kvalid = bytes of K left from kofs (> 0); chunks
-  // at or past it read as zero.  Without GUARD the K tile is whole.
-  template <int Q, uint32_t REGION, bool GUARD>
-  __device__ __forceinline__ void issue_one(uint32_t sbase, uint32_t kofs, int kvalid) {
-    uint32_t vo = voff[Q];
+  // Instruction Q of K tile k_tile into the stage at LDS byte address sbase
+  // (plus this wave's KiB).  GUARD: kvalid = bytes of K left from the tile's
+  // start (> 0); chunks at or past it read as zero.  Without GUARD the K
+  // tile is whole.
+  template <int Q, bool GUARD>
+  __device__ __forceinline__ void issue_one(uint32_t sbase, int k_tile, int kvalid) {
+    uint32_t vo = voff;
     if constexpr (GUARD) vo = (int)cb < kvalid ? vo : 0x80000000u;
-    dma16s<REGION + (uint32_t)Q * CF::NW * 1024u>(rsrc, sbase, vo, kofs);
+    dma16s<(uint32_t)Q * CF::NW * 1024u>(rsrc, sbase, vo, (uint32_t)k_tile * (uint32_t)CF::ROWB + Q * qstep);
   }
 
-  template <int Q0 = 0, int Q1 = NQ>
-  __device__ __forceinline__ void issue(uint32_t lds_addr, int wave, int kt, int64_t kvalid) {
-    const uint32_t kofs = (uint32_t)kt * (uint32_t)CF::ROWB;
-    if (kvalid >= CF::ROWB) {
-#pragma unroll
-      for (int q = Q0; q < Q1; ++q)
-        dma16(rsrc, lds_addr + (uint32_t)((q * CF::NW + wave) * 1024), voff[q] + kofs);
+  // Fragment of MFMA block blk, k step s, from the stage at byte offset off
+  // of the LDS array: lane group q's share (BPL bytes) of the step in row
+  // row0 + blk*BLK.  Rows BLK apart share their chunk swizzle (a block spans
+  // whole swizzle periods), so block blk is an immediate offset from block
+  // 0's address.
+  __device__ __forceinline__ typename CF::RAW read(const char* lds, int off, int blk, int s) const {
+    static_assert(CF::BLK % (CF::CH << CF::SWZ_SHIFT) == 0, "block rows span whole swizzle periods");
+    const char* rp = lds + off + row0 * CF::ROWB + blk * (CF::BLK * CF::ROWB);
+    const int sw = swz<CF>(row0);
+    if constexpr (CF::BPL == 8) {
+      const int c = s * (CF::MM::KSB / 16) + (q >> 1);
+      return *(const v2i*)(rp + ((c ^ sw) << 4) + (q & 1) * 8);
+    } else if constexpr (CF::CPL == 1) {
+      const int c = s * (CF::MM::KSB / 16) + q;
+      return *(const v4i*)(rp + ((c ^ sw) << 4));
     } else {
-#pragma unroll
-      for (int q = Q0; q < Q1; ++q) {
-        const uint32_t vo = (int64_t)cb < kvalid ? voff[q] + kofs : 0x80000000u;
-        dma16(rsrc, lds_addr + (uint32_t)((q * CF::NW + wave) * 1024), vo);
-      }
+      static_assert(CF::CPL == 2, "one or two chunks per lane");
+      const int c = s * (CF::MM::KSB / 16) + q * CF::CPL;
+      const v4i lo = *(const v4i*)(rp + ((c ^ sw) << 4));
+      const v4i hi = *(const v4i*)(rp + (((c + 1) ^ sw) << 4));
+      return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
 };
 
-// 4x4 byte transpose: x_r holds bytes (r,0..3); c_j receives bytes (0..3, j).
-__device__ __forceinline__ void tr4x4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
-                                      uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3) {
-  const uint32_t u0 = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0b0 x1b0 x0b1 x1b1
-  const uint32_t u1 = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0b2 x1b2 x0b3 x1b3
-  const uint32_t v0 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
-  const uint32_t v1 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
-  c0 = __builtin_amdgcn_perm(v0, u0, 0x05040100u);
-  c1 = __builtin_amdgcn_perm(v0, u0, 0x07060302u);
-  c2 = __builtin_amdgcn_perm(v1, u1, 0x05040100u);
-  c3 = __builtin_amdgcn_perm(v1, u1, 0x07060302u);
-}
-
 // ---------------------------------------------------------------------------
-// Staging of an M-major one-byte A tile: global A[l][k][m], ROWB k rows by
-// BM m bytes per stage.  Each thread owns blocks of 8 k x 8 m bytes: eight
-// 8-byte global loads (a wave covers whole k rows of the tile), an 8x8 byte
-// transpose in registers, then eight 8-byte LDS writes into the same
-// K-contiguous swizzled layout the K-major path produces.
+// MN-major operand (A 'M' or B 'N'): a stage is BK k-rows of R elements (RB
+// bytes); the 16-byte chunk c of k-row k is stored at c ^ mn_swz(k).  The
+// MFMA wants each lane's k values of one row (m or n) side by side: the
+// gfx950 transposing LDS loads give exactly that.  Within each group of 16
+// lanes, ds_read_b64_tr_b16 reads 4 k-rows of 16 elements (4 lanes per k-row,
+// 4 consecutive elements each) and hands lane i element i of every k-row;
+// ds_read_b64_tr_b8 does the same with 8 k-rows (2 lanes per k-row, 8 bytes
+// each).  So a lane receives E = 8 / ES consecutive k of one row per read.
+// Out-of-range rows read as zero: the buffer's extent ends at the end of K,
+// and a chunk past M (N) gets an out-of-range offset.
 // ---------------------------------------------------------------------------
 template <class CF>
-struct MMajorStager8 {
-  static constexpr int MB = CF::BM / 8;                       // m blocks per tile
-  static constexpr int NB = (CF::ROWB / 8) * MB / CF::THREADS;  // blocks per thread
-  static_assert(NB >= 1 && NB * CF::THREADS == (CF::ROWB / 8) * MB, "blocks must split evenly");
-  v2u buf[NB][8];
-  const char* base;  // A + l*M*K (bytes)
-  int64_t M, K;
-  int m0;
-
-  __device__ __forceinline__ void setup(const char* a_batch, int64_t M_, int64_t K_, int m0_) {
-    base = a_batch;
-    M = M_;
-    K = K_;
-    m0 = m0_;
+struct MNSwizzle {
+  // XOR applied to the chunk index of k-row k, chosen so that the chunks
+  // read by one half-wave (32 lanes, one LDS cycle of 8-byte reads) hit 16
+  // distinct 16-byte bank groups of the 64-bank LDS:
+  //   2-byte, 16x16 blocks: k-rows {0..3, 8..11} (+4), 2 chunks each;
+  //   2-byte, 32x32 blocks: k-rows {0..3} (+4), 4 chunks each;
+  //   1-byte, 16x16 blocks, 16 B per lane: k-rows {0..7, 16..23} (+8), 1 chunk;
+  //   1-byte, 16x16 blocks, 8 B per lane (widened fp8): k-rows {0..15}, 1 chunk;
+  //   1-byte, 32x32 blocks: k-rows {0..7} (+8), 2 chunks each.
+  static constexpr __host__ __device__ int of(int k) {
+    if constexpr (CF::MM::ESIZE == 2)
+      return CF::BLK == 16 ? 2 * ((k & 3) | ((k >> 1) & 4)) : 4 * (k & 3);
+    else if constexpr (CF::BLK == 32)
+      return 2 * (k & 7);
+    else if constexpr (CF::BPL == 8)
+      return k & 15;
+    else
+      return (k & 7) | ((k >> 1) & 8);
   }
-
-  __device__ __forceinline__ void load(int kt, int tid) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int id = b * CF::THREADS + tid;
-      const int bm = id % MB, bk = id / MB;
-      const int64_t m = (int64_t)m0 + bm * 8;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int64_t k = (int64_t)kt * CF::ROWB + bk * 8 + r;
-        if (k < K && m < M)
-          buf[b][r] = *(const v2u*)(base + k * M + m);
-        else
-          buf[b][r] = v2u{0u, 0u};
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(char* lds, int lds_off, int tid) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int id = b * CF::THREADS + tid;
-      const int bm = id % MB, bk = id / MB;
-      uint32_t lo[8], hi[8];
-      tr4x4(buf[b][0].x, buf[b][1].x, buf[b][2].x, buf[b][3].x, lo[0], lo[1], lo[2], lo[3]);
-      tr4x4(buf[b][4].x, buf[b][5].x, buf[b][6].x, buf[b][7].x, hi[0], hi[1], hi[2], hi[3]);
-      tr4x4(buf[b][0].y, buf[b][1].y, buf[b][2].y, buf[b][3].y, lo[4], lo[5], lo[6], lo[7]);
-      tr4x4(buf[b][4].y, buf[b][5].y, buf[b][6].y, buf[b][7].y, hi[4], hi[5], hi[6], hi[7]);
-      const int chunk = bk >> 1, sub = (bk & 1) * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = bm * 8 + i;
-        const int off = lds_off + row * CF::ROWB + ((chunk ^ swz<CF>(row)) << 4) + sub;
-        *(v2u*)(lds + off) = v2u{lo[i], hi[i]};
-      }
-    }
+  static constexpr int MAX = 15;
+  // of(k) == of(k + step) for every k
+  static constexpr bool periodic(int step) {
+    for (int k = 0; k < 256; ++k)
+      if (of(k) != of(k + step)) return false;
+    return true;
   }
 };
 
-// Fragment read: lane group q's share (BPL bytes) of k step s of LDS row
-// row0 + blk*BLK.  Rows BLK apart share their chunk swizzle (a block spans
-// whole swizzle periods), so the swizzle is taken from row0 and block blk is
-// an immediate offset from block 0's address.
-template <class CF>
-__device__ __forceinline__ typename CF::MM::frag_t read_frag(const char* lds, int tile_off, int row0, int blk,
-                                                             int s, int q) {
-  static_assert(CF::BLK % (CF::CH << CF::SWZ_SHIFT) == 0, "block rows span whole swizzle periods");
-  const char* rp = lds + tile_off + row0 * CF::ROWB + blk * (CF::BLK * CF::ROWB);
-  const int sw = swz<CF>(row0);
-  if constexpr (CF::BPL == 8) {
-    const int c = s * (CF::MM::KSB / 16) + (q >> 1);
-    return *(const v2i*)(rp + ((c ^ sw) << 4) + (q & 1) * 8);
-  } else if constexpr (CF::CPL == 1) {
-    const int c = s * (CF::MM::KSB / 16) + q;
-    return *(const v4i*)(rp + ((c ^ sw) << 4));
-  } else {
-    const int c = s * (CF::MM::KSB / 16) + q * CF::CPL;
-    static_assert(CF::CPL == 2, "one or two chunks per lane");
-    const v4i lo = *(const v4i*)(rp + ((c ^ sw) << 4));
-    const v4i hi = *(const v4i*)(rp + (((c + 1) ^ sw) << 4));
-    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+template <class CF, int R, int WR>
+struct MNMajorOperand {
+  static constexpr int ES = CF::MM::ESIZE;
+  static constexpr int BK = CF::BK;       // k per stage
+  static constexpr int RB = R * ES;       // bytes of one k-row
+  static constexpr int CPR = RB / 16;     // chunks per k-row
+  static constexpr int RPI = 1024 / RB;   // k-rows per wave instruction
+  static constexpr int NQ = BK / (RPI * CF::NW);
+  static_assert(RPI * RB == 1024 && NQ * RPI * CF::NW == BK, "k-rows must split evenly over the waves");
+  static_assert(CPR > MNSwizzle<CF>::MAX, "the swizzle stays inside a k-row");
+  static constexpr int E = 8 / ES;              // k per lane and transposing read
+  static constexpr int KPL = CF::BPL / ES;      // k per lane and step
+  static constexpr int NR = KPL / E;            // transposing reads per fragment
+  static constexpr int KK = CF::MM::KSB / ES;   // k per step
+  static constexpr int NBLK = WR / CF::BLK;  // blocks of the reading wave along R
+  // The swizzle of the k-rows of instruction i depends on i only through
+  // i & 1 (instructions are NW*RPI k-rows apart, a multiple of 8), so two
+  // per-lane offsets serve them all; the rest of the step is a scalar.
+  static constexpr int NV = NQ < 2 ? NQ : 2;
+  static_assert(MNSwizzle<CF>::periodic(2 * CF::NW * RPI), "two offset patterns cover every instruction");
+  v4i rsrc;
+  uint32_t voff[NV];
+  uint32_t kstride;  // bytes of one K tile in global memory
+  uint32_t qstep;    // bytes between instructions i and i + 2
+  int raddr;         // reader: LDS byte offset of block 0 (k step 0, read 0)
+
+  __device__ __forceinline__ void setup(const char* batch, int64_t extent, int64_t K, int r0, int wave,
+                                        int lane) {
+    const int64_t ldb = extent * ES;  // bytes of one global k-row
+    rsrc = make_rsrc(batch + (int64_t)r0 * ES, (uint32_t)(K * ldb - (int64_t)r0 * ES));
+    kstride = (uint32_t)(BK * ldb);
+    qstep = (uint32_t)(2 * CF::NW * RPI * ldb);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int krow = (i * CF::NW + wave) * RPI + lane / CPR;
+      const int lc = (lane % CPR) ^ MNSwizzle<CF>::of(krow);
+      voff[i] = (int64_t)r0 + lc * (16 / ES) < extent ? (uint32_t)(krow * ldb + lc * 16) : 0x80000000u;
+    }
   }
-}
+  // Block blk's chunks are block 0's with the bits of blk * BLK * ES flipped:
+  // the row offset of the wave (a multiple of its WR rows), the block and the
+  // lane's place inside a block occupy disjoint bits, and the swizzle is an
+  // XOR, so the byte address of block blk is raddr ^ (blk * BLK * ES).
+  __device__ __forceinline__ void setup_reader(int rbase, int lane) {
+    static_assert((WR & (WR - 1)) == 0 && (CF::BLK * NBLK) == WR, "wave rows a power of two");
+    constexpr int LPR = 16 / E;  // lanes per k-row in one read
+    const int i16 = lane & 15, b = lane >> 4;
+    const int q = CF::BLK == 16 ? b : b >> 1;           // k group of this lane
+    const int roff = CF::BLK == 16 ? 0 : (b & 1) * 16;  // rows of the block's half
+    const int krow = q * KPL + i16 / LPR;               // + s*KK + h*E at read time
+    const int rbyte = (rbase + roff + (i16 % LPR) * E) * ES;
+    raddr = krow * RB + (((rbyte >> 4) ^ MNSwizzle<CF>::of(krow)) << 4) + (rbyte & 15);
+  }
+  template <int Q, bool GUARD>
+  __device__ __forceinline__ void issue_one(uint32_t sbase, int k_tile, int) {
+    dma16s<(uint32_t)Q * CF::NW * 1024u>(rsrc, sbase, voff[Q & 1], (uint32_t)k_tile * kstride + (Q >> 1) * qstep);
+  }
+
+  // Fragment of block blk, k step s: NR transposing reads of E k each (the
+  // swizzle of a lane's k-rows does not change with s or the read index).
+  __device__ __forceinline__ typename CF::RAW read(const char* lds, int off, int blk, int s) const {
+    lds_char_t* base = (lds_char_t*)lds + off + (raddr ^ (blk * CF::BLK * ES)) + s * KK * RB;
+    int r[2 * NR];
+#pragma unroll
+    for (int h = 0; h < NR; ++h) {
+      v2i v;
+      if constexpr (ES == 2)
+        v = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                        (__attribute__((address_space(3))) v4s*)(base + h * E * RB)));
+      else
+        v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(base + h * E * RB));
+      r[2 * h] = v.x;
+      r[2 * h + 1] = v.y;
+    }
+    if constexpr (NR == 1) return v2i{r[0], r[1]};
+    else if constexpr (NR == 2) return v4i{r[0], r[1], r[2], r[3]};
+    else return v8i{r[0], r[1], r[2], r[3], r[4], r[5], r[6], r[7]};
+  }
+};
+
+// R: rows of the operand tile (BM or BN); WR: rows of one wave's share.
+template <class CF, int R, int WR, bool KMAJ>
+using Operand = typename std::conditional<KMAJ, KMajorOperand<CF, R, WR>, MNMajorOperand<CF, R, WR>>::type;
+
 
 // Accumulator element as the 32-bit pattern stored in LDS.  (The element is
 // read into a scalar first: bit-casting a vector-element lvalue directly
@@ -540,13 +598,13 @@ __device__ __forceinline__ float acc_bits(int v) { return __int_as_float(v); }
 // region (fp32 or int32 bit patterns): for N-major outputs rows blk*32 ..
 // blk*32+31 of the wave tile (line = row, WN columns), for M-major columns
 // (line = column, WM rows).
-template <class CF, class ACC>
+template <class CF, bool NMAJ, class ACC>
 __device__ __forceinline__ void epi_stage_block(const ACC (&acc)[CF::FM][CF::FN], float* region, int lane,
                                                 int blk) {
   using MM = typename CF::MM;
-  constexpr int BLK = CF::BLK, PITCH = CF::EPI_PITCH, SUB = 32 / BLK;
+  constexpr int BLK = CF::BLK, PITCH = CF::epi_pitch(NMAJ), SUB = 32 / BLK;
   const int lc = lane % BLK;
-  if constexpr (CF::CD_NMAJOR) {
+  if constexpr (NMAJ) {
 #pragma unroll
     for (int b = 0; b < SUB; ++b)
 #pragma unroll
@@ -644,17 +702,16 @@ __device__ __forceinline__ void epi_st(__amdgpu_buffer_rsrc_t r, uint32_t off, v
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, EPI_NT);
 }
 
-template <class CF, int T, class ACC>
+template <class CF, bool NMAJ, int T, class ACC>
 __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)[CF::FM][CF::FN], char* lds,
                                                int wave, int lane, int l, int mw, int nw) {
-  constexpr bool NMAJ = CF::CD_NMAJOR;
-  constexpr int LINE = CF::EPI_LINE, PITCH = CF::EPI_PITCH;
+  constexpr int LINE = CF::epi_line(NMAJ), PITCH = CF::epi_pitch(NMAJ);
   constexpr int ES = EpiElem<T>::SIZE;
   constexpr int VEC = 16 / ES;         // elements per lane: one 16-byte access per array
   constexpr int LPL = LINE / VEC;      // lanes per line
   constexpr int LINES_PER_PASS = 64 / LPL;
   static_assert(LPL >= 1 && LPL <= 64 && 32 % LINES_PER_PASS == 0, "line split over the lanes");
-  float* region = (float*)(lds + wave * CF::EPI_WAVE_BYTES);
+  float* region = (float*)(lds + wave * CF::epi_wave_bytes(NMAJ));
   constexpr int NBLK = (NMAJ ? CF::WM : CF::WN) / 32;
   constexpr int PASSES = 32 / LINES_PER_PASS;
   constexpr int NP = NBLK * PASSES;
@@ -690,7 +747,7 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
     return lane_off + (uint32_t)(line * ld * ES);
   };
 
-  auto write_block = [&](auto blk_c) { epi_stage_block<CF>(acc, region, lane, decltype(blk_c)::value); };
+  auto write_block = [&](auto blk_c) { epi_stage_block<CF, NMAJ>(acc, region, lane, decltype(blk_c)::value); };
 
   v4u cr[DIST + 1], xr[DIST + 1];
   static_for<0, DIST>([&](auto i_c) {
@@ -784,16 +841,15 @@ __device__ __forceinline__ void epi_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, 
 
 __device__ __forceinline__ int epi_shift(int dt) { return dt == T_F32 || dt == T_I32 ? 2 : 1; }
 
-template <class CF, class ACC>
+template <class CF, bool NMAJ, class ACC>
 __device__ __forceinline__ void epilogue_mixed(const Params& p, const ACC (&acc)[CF::FM][CF::FN], char* lds,
                                                int wave, int lane, int l, int mw, int nw) {
-  constexpr bool NMAJ = CF::CD_NMAJOR;
-  constexpr int LINE = CF::EPI_LINE, PITCH = CF::EPI_PITCH;
+  constexpr int LINE = CF::epi_line(NMAJ), PITCH = CF::epi_pitch(NMAJ);
   constexpr int VEC = 4;
   constexpr int LPL = LINE / VEC;
   constexpr int LINES_PER_PASS = 64 / LPL;
   static_assert(LPL >= 1 && LPL <= 64 && 32 % LINES_PER_PASS == 0, "line split over the lanes");
-  float* region = (float*)(lds + wave * CF::EPI_WAVE_BYTES);
+  float* region = (float*)(lds + wave * CF::epi_wave_bytes(NMAJ));
   constexpr int NBLK = (NMAJ ? CF::WM : CF::WN) / 32;
   constexpr int PASSES = 32 / LINES_PER_PASS;
   constexpr int NP = NBLK * PASSES;
@@ -829,7 +885,7 @@ __device__ __forceinline__ void epilogue_mixed(const Params& p, const ACC (&acc)
   };
   auto boff = [&](uint32_t eo, int sh) { return lane_ok ? eo << sh : 0x80000000u; };
 
-  auto write_block = [&](auto blk_c) { epi_stage_block<CF>(acc, region, lane, decltype(blk_c)::value); };
+  auto write_block = [&](auto blk_c) { epi_stage_block<CF, NMAJ>(acc, region, lane, decltype(blk_c)::value); };
 
   v4u cr[DIST + 1], xr[DIST + 1];
   static_for<0, DIST>([&](auto i_c) {
@@ -866,20 +922,6 @@ __device__ __forceinline__ void epilogue_mixed(const Params& p, const ACC (&acc)
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-// Scheduling pattern for one k step: READS LDS reads spread evenly over
-// MFMAS matrix instructions ([1 read, MFMAS/READS MFMAs] repeated).
-template <int R, int READS, int MFMAS>
-struct InterleaveHint {
-  static __device__ __forceinline__ void run() {
-    if constexpr (R < READS) {
-      constexpr int n = MFMAS / READS + (R < MFMAS % READS ? 1 : 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
-      if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x008, n, 0);  // MFMAs
-      InterleaveHint<R + 1, READS, MFMAS>::run();
-    }
-  }
-};
-
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
@@ -897,8 +939,6 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % CF::WAVES_M, wn = wave / CF::WAVES_M;
-  const int lq = lane / CF::BLK, lr = lane % CF::BLK;  // k share and row of this lane in a block
-
 
   const int G = gridDim.x;
   const int bid = blockIdx.x;
@@ -908,9 +948,25 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
   const int KT = (int)((kbytes + CF::ROWB - 1) / CF::ROWB);
   const int64_t tiles_mn = (int64_t)p.tiles_m * p.tiles_n;
 
+  using OpA = Operand<CF, BM, CF::WM, CF::A_KMAJOR>;
+  using OpB = Operand<CF, BN, CF::WN, CF::B_KMAJOR>;
   // DMA instructions per wave per stage (for the counted waits)
-  constexpr int NQ_A = CF::A_KMAJOR ? KMajorStager<CF, BM>::NQ : 0;
-  constexpr int NQ_STAGE = NQ_A + KMajorStager<CF, BN>::NQ;
+  constexpr int NQ_A = OpA::NQ;
+  constexpr int NQ_STAGE = NQ_A + OpB::NQ;
+  // LDS: A's stages, then B's stages.
+  constexpr int A_STAGE = BM * CF::ROWB, B_STAGE = BN * CF::ROWB;
+  constexpr int B_REGION = S * A_STAGE;
+
+  OpA opa;
+  OpB opb;
+  opa.setup_reader(wm * CF::WM, lane);
+  opb.setup_reader(wn * CF::WN, lane);
+  // LDS fragment -> MFMA operand (fp8 widened to fp16 in the widening kernels)
+  const bool a_e5m2 = p.f8a != 0, b_e5m2 = p.f8b != 0;
+  auto frag = [](typename CF::RAW raw, bool e5m2) -> frag_t {
+    if constexpr (CF::WIDEN) return __builtin_bit_cast(v4i, widen8(raw, e5m2));
+    else return raw;
+  };
 
   for (int64_t t = g; t < p.tiles_total; t += G) {
     // ---- tile coordinates: grouped raster inside each batch -------------
@@ -926,32 +982,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     const int m0 = tm * BM, n0 = tn * BN;
 
     // ---- staging set-up --------------------------------------------------
-    const char* Ab = (const char*)p.A + (int64_t)l * p.M * kbytes;
-    const char* Bb = (const char*)p.B + (int64_t)l * p.N * kbytes;
-    KMajorStager<CF, BN> sb;
-    sb.setup(Bb + (int64_t)n0 * kbytes, kbytes, (int)min((int64_t)BN, p.N - n0), wave, lane);
-    KMajorStager<CF, BM> sa_k;
-    if constexpr (CF::A_KMAJOR)
-      sa_k.setup(Ab + (int64_t)m0 * kbytes, kbytes, (int)min((int64_t)BM, p.M - m0), wave, lane);
-
-    auto issue_dma = [&](int k_tile) {
-      const int st = (k_tile % S) * CF::STAGE_BYTES;
-      const int64_t kv = kbytes - (int64_t)k_tile * CF::ROWB;
-      if constexpr (CF::A_KMAJOR) sa_k.issue(lds_u32 + st, wave, k_tile, kv);
-      sb.issue(lds_u32 + st + BM * CF::ROWB, wave, k_tile, kv);
-    };
-    // Part PART of NPARTS of the loads of K tile k_tile (A and B split alike).
-    using SA = KMajorStager<CF, BM>;
-    using SB = KMajorStager<CF, BN>;
-    auto issue_dma_part = [&](auto part_c, auto nparts_c, int k_tile) {
-      constexpr int PART = decltype(part_c)::value, NP = decltype(nparts_c)::value;
-      const int st = (k_tile % S) * CF::STAGE_BYTES;
-      const int64_t kv = kbytes - (int64_t)k_tile * CF::ROWB;
-      if constexpr (CF::A_KMAJOR)
-        sa_k.template issue<PART * SA::NQ / NP, (PART + 1) * SA::NQ / NP>(lds_u32 + st, wave, k_tile, kv);
-      sb.template issue<PART * SB::NQ / NP, (PART + 1) * SB::NQ / NP>(lds_u32 + st + BM * CF::ROWB, wave,
-                                                                      k_tile, kv);
-    };
+    opa.setup((const char*)p.A + (int64_t)l * p.M * kbytes, p.M, p.K, m0, wave, lane);
+    opb.setup((const char*)p.B + (int64_t)l * p.N * kbytes, p.N, p.K, n0, wave, lane);
 
     acc_t acc[CF::FM][CF::FN];
 #pragma unroll
@@ -962,49 +994,14 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     // Fragments of one k step: A blocks then B blocks of this wave.
     frag_t fa[2][CF::FM], fb[2][CF::FN];
     auto load_step = [&](frag_t (&ra)[CF::FM], frag_t (&rb)[CF::FN], int st, int s) {
-      const int a_off = st * CF::STAGE_BYTES, b_off = a_off + BM * CF::ROWB;
 #pragma unroll
-      for (int i = 0; i < CF::FM; ++i) ra[i] = read_frag<CF>(lds, a_off, wm * CF::WM + lr, i, s, lq);
+      for (int i = 0; i < CF::FM; ++i) ra[i] = frag(opa.read(lds, st * A_STAGE, i, s), a_e5m2);
 #pragma unroll
-      for (int j = 0; j < CF::FN; ++j) rb[j] = read_frag<CF>(lds, b_off, wn * CF::WN + lr, j, s, lq);
+      for (int j = 0; j < CF::FN; ++j) rb[j] = frag(opb.read(lds, B_REGION + st * B_STAGE, j, s), b_e5m2);
     };
-    auto mma_step = [&](const frag_t (&ra)[CF::FM], const frag_t (&rb)[CF::FN]) {
-#pragma unroll
-      for (int i = 0; i < CF::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < CF::FN; ++j) acc[i][j] = MM::mma(ra[i], rb[j], acc[i][j]);
-    };
-    // Interleave the next step's LDS reads with this step's MFMAs so each
-    // read's latency hides under MFMAs already queued.
-    auto pipeline_hint = [&]() {
-      constexpr int READS = (CF::FM + CF::FN) * CF::CPL;
-      constexpr int MFMAS = CF::FM * CF::FN;
-      InterleaveHint<0, READS, MFMAS>::run();
-    };
-    // One K tile from stage st; the last step prefetches step 0 of stage nst.
-    // The DMA of K tile dma_tile (if < KT) is issued in NP parts after the
-    // first NP k steps, so the memory pipeline is fed while MFMAs run rather
-    // than in one burst that stalls the wave's issue.
-    auto compute = [&](int st, int nst, int dma_tile, auto np_c) {
-      constexpr int NP = decltype(np_c)::value;
-      static_for<0, CF::KSTEPS>([&](auto s_c) {
-        constexpr int s = decltype(s_c)::value;
-        constexpr int cur = s & 1;
-        if constexpr (s + 1 < CF::KSTEPS)
-          load_step(fa[cur ^ 1], fb[cur ^ 1], st, s + 1);
-        else
-          load_step(fa[cur ^ 1], fb[cur ^ 1], nst, 0);
-        mma_step(fa[cur], fb[cur]);
-        pipeline_hint();
-        if constexpr (s < NP) {
-          if (dma_tile < KT) issue_dma_part(IntC<s>{}, IntC<NP>{}, dma_tile);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      });
-    };
-    static_assert(CF::KSTEPS % 2 == 0, "fragment double buffer needs an even step count");
+    static_assert(CF::KSTEPS % 2 == 0, "k steps alternate fragment buffers across K tiles");
 
-    // ---- K-major A: explicitly ordered k steps ---------------------------
+    // ---- explicitly ordered k steps ----------------------------------------
     // Each k step issues its MFMAs in a fixed order (sched_barrier pins it);
     // after each MFMA come the fragment reads of the next step scheduled
     // there (ordered by first use: A0, B0.., A1..) and a share of the DMA
@@ -1014,13 +1011,12 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     auto read_r = [&](auto buf_c, auto r_c, auto st_x, auto ks_x) {
       constexpr int BUF = decltype(buf_c)::value, R = decltype(r_c)::value;
       const int st = (int)st_x, ks = (int)ks_x;
-      const int a_off = st * CF::STAGE_BYTES, b_off = a_off + BM * CF::ROWB;
       if constexpr (R == 0)
-        fa[BUF][0] = read_frag<CF>(lds, a_off, wm * CF::WM + lr, 0, ks, lq);
+        fa[BUF][0] = frag(opa.read(lds, st * A_STAGE, 0, ks), a_e5m2);
       else if constexpr (R <= CF::FN)
-        fb[BUF][R - 1] = read_frag<CF>(lds, b_off, wn * CF::WN + lr, R - 1, ks, lq);
+        fb[BUF][R - 1] = frag(opb.read(lds, B_REGION + st * B_STAGE, R - 1, ks), b_e5m2);
       else
-        fa[BUF][R - CF::FN] = read_frag<CF>(lds, a_off, wm * CF::WM + lr, R - CF::FN, ks, lq);
+        fa[BUF][R - CF::FN] = frag(opa.read(lds, st * A_STAGE, R - CF::FN, ks), a_e5m2);
     };
     // DMA instruction D of K tile k_tile into stage stg.  GUARD: the tile
     // may not exist (k_tile >= KT) or may be cut by the end of K; without
@@ -1030,13 +1026,11 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       constexpr int D = decltype(d_c)::value;
       constexpr bool GUARD = decltype(guard_c)::value;
       if (GUARD && k_tile >= KT) return;
-      const uint32_t sbase = lds_wave + (uint32_t)stg * (uint32_t)CF::STAGE_BYTES;
-      const uint32_t kofs = (uint32_t)k_tile * (uint32_t)CF::ROWB;
-      const int kv = GUARD ? (int)min(kbytes - (int64_t)kofs, (int64_t)CF::ROWB) : CF::ROWB;
+      const int kv = GUARD ? (int)min(kbytes - (int64_t)k_tile * CF::ROWB, (int64_t)CF::ROWB) : CF::ROWB;
       if constexpr (D < NQ_A)
-        sa_k.template issue_one<D, 0u, GUARD>(sbase, kofs, kv);
+        opa.template issue_one<D, GUARD>(lds_wave + (uint32_t)stg * (uint32_t)A_STAGE, k_tile, kv);
       else
-        sb.template issue_one<D - NQ_A, (uint32_t)(BM * CF::ROWB), GUARD>(sbase, kofs, kv);
+        opb.template issue_one<D - NQ_A, GUARD>(lds_wave + (uint32_t)(B_REGION + stg * B_STAGE), k_tile, kv);
     };
     // One k step on buffer CUR: reads of (stage rst, step rs) into CUR^1 and
     // NOPS memory operations op(IntC<k>) spread evenly over the MFMAs.
@@ -1123,99 +1117,83 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
             IntC<MF>{});
     };
 
-    if constexpr (CF::A_KMAJOR) {
-      static_assert(CF::KSTEPS % 2 == 0, "k steps alternate fragment buffers across K tiles");
-      // Prologue: two stages: K tiles 0 and 1 whole, tile 0 complete.  Deep
-      // ring: K tiles 0 .. S-2 whole, tile 0 complete, then part 0 of tile
-      // S-1 (stage S-1 is untouched so far).
-      if constexpr (S == 2) {
-        issue_dma(0);
-        if (1 < KT) {
-          issue_dma(1);
-          wait_vmcnt<NQ_STAGE>();
-        } else {
-          wait_vmcnt<0>();
-        }
+    // Prologue: two stages: K tiles 0 and 1 whole, tile 0 complete.  Deep
+    // ring: K tiles 0 .. S-2 whole, tile 0 complete, then part 0 of tile
+    // S-1 (stage S-1 is untouched so far).
+    // (tile numbers known at compile time are hidden from constant folding:
+    // the DMA's scalar offset operand takes no literal)
+    auto issue_tile = [&](int k_tile) {
+      asm("" : "+s"(k_tile));
+      static_for<0, NQ_STAGE>([&](auto d_c) { dma_one(d_c, IntC<1>{}, k_tile, k_tile % S); });
+    };
+    if constexpr (S == 2) {
+      issue_tile(0);
+      if (1 < KT) {
+        issue_tile(1);
+        wait_vmcnt<NQ_STAGE>();
       } else {
-#pragma unroll
-        for (int k = 0; k < S - 1; ++k)
-          if (k < KT) issue_dma(k);
-        wait_pending(min(S - 1, KT) - 1);
-        // (tile numbers known at compile time are hidden from constant
-        // folding: the DMA's scalar offset operand takes no literal)
-        int t_pro = S - 1;
-        asm("" : "+s"(t_pro));
-        static_for<0, P0>([&](auto d_c) { dma_one(d_c, IntC<1>{}, t_pro, S - 1); });
-      }
-      barrier_lds();
-      load_step(fa[0], fb[0], 0, 0);
-      // Guarded K tiles: the first one of the two-stage ring (its tile 1 was
-      // issued whole) and every K tile whose loads reach past the last whole
-      // K tile; the rest run without checks.
-      const int kt_whole = (int)(kbytes / CF::ROWB);
-      int kt = 0, st = 0;
-      auto next = [](int x) { return x + 1 == S ? 0 : x + 1; };
-      auto prev = [](int x) { return x == 0 ? S - 1 : x - 1; };
-      if constexpr (S == 2) {
-        k_tile(IntC<1>{}, 0, 0, 1, 1, KT);
-        kt = 1;
-        st = 1;
-      }
-      if constexpr (S == 2) {
-        // Two stages: K tiles in pairs with the stage a compile-time
-        // constant, so every fragment address is a loop-invariant register
-        // plus an immediate (no address arithmetic between the MFMAs).
-        if (kt + S < kt_whole && st == 1) {
-          k_tile(IntC<0>{}, kt, IntC<1>{}, IntC<0>{}, IntC<0>{}, kt + S - 1);
-          ++kt;
-          st = 0;
-        }
-        for (; kt + 1 + S < kt_whole; kt += 2) {
-          k_tile(IntC<0>{}, kt, IntC<0>{}, IntC<1>{}, IntC<1>{}, kt + S - 1);
-          k_tile(IntC<0>{}, kt + 1, IntC<1>{}, IntC<0>{}, IntC<0>{}, kt + S);
-        }
-      }
-      for (; kt + S < kt_whole; ++kt) {
-        k_tile(IntC<0>{}, kt, st, next(st), prev(st), kt + S - 1);
-        st = next(st);
-      }
-      for (; kt < KT; ++kt) {
-        k_tile(IntC<1>{}, kt, st, next(st), prev(st), kt + S - 1);
-        st = next(st);
-      }
-      wait_vmcnt<0>();
-    } else {
-      // ---- M-major one-byte A: registers + transpose, B by DMA -----------
-      MMajorStager8<CF> sa_m;
-      sa_m.setup(Ab, p.M, p.K, m0);
-      sa_m.load(0, tid);
-      sa_m.store(lds, 0, tid);
-      sb.issue(lds_u32 + BM * CF::ROWB, wave, 0, kbytes);
-      for (int kt = 0; kt < KT; ++kt) {
         wait_vmcnt<0>();
-        barrier_lds();  // stage kt complete; stage kt+1 free
-        const bool more = kt + 1 < KT;
-        const int nxt = ((kt + 1) % S) * CF::STAGE_BYTES;
-        if (more) {
-          sa_m.load(kt + 1, tid);
-          sb.issue(lds_u32 + nxt + BM * CF::ROWB, wave, kt + 1, kbytes - (int64_t)(kt + 1) * CF::ROWB);
-        }
-        load_step(fa[0], fb[0], kt % S, 0);
-        compute(kt % S, kt % S, KT, IntC<0>{});
-        if (more) sa_m.store(lds, nxt, tid);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < S - 1; ++k)
+        if (k < KT) issue_tile(k);
+      wait_pending(min(S - 1, KT) - 1);
+      int t_pro = S - 1;
+      asm("" : "+s"(t_pro));
+      static_for<0, P0>([&](auto d_c) { dma_one(d_c, IntC<1>{}, t_pro, S - 1); });
+    }
+    barrier_lds();
+    load_step(fa[0], fb[0], 0, 0);
+    // Guarded K tiles: the first one of the two-stage ring (its tile 1 was
+    // issued whole) and every K tile whose loads reach past the last whole
+    // K tile; the rest run without checks.
+    const int kt_whole = (int)(kbytes / CF::ROWB);
+    int kt = 0, st = 0;
+    auto next = [](int x) { return x + 1 == S ? 0 : x + 1; };
+    auto prev = [](int x) { return x == 0 ? S - 1 : x - 1; };
+    if constexpr (S == 2) {
+      k_tile(IntC<1>{}, 0, 0, 1, 1, KT);
+      kt = 1;
+      st = 1;
+    }
+    if constexpr (S == 2) {
+      // Two stages: K tiles in pairs with the stage a compile-time
+      // constant, so every fragment address is a loop-invariant register
+      // plus an immediate (no address arithmetic between the MFMAs).
+      if (kt + S < kt_whole && st == 1) {
+        k_tile(IntC<0>{}, kt, IntC<1>{}, IntC<0>{}, IntC<0>{}, kt + S - 1);
+        ++kt;
+        st = 0;
+      }
+      for (; kt + 1 + S < kt_whole; kt += 2) {
+        k_tile(IntC<0>{}, kt, IntC<0>{}, IntC<1>{}, IntC<1>{}, kt + S - 1);
+        k_tile(IntC<0>{}, kt + 1, IntC<1>{}, IntC<0>{}, IntC<0>{}, kt + S);
       }
     }
+    for (; kt + S < kt_whole; ++kt) {
+      k_tile(IntC<0>{}, kt, st, next(st), prev(st), kt + S - 1);
+      st = next(st);
+    }
+    for (; kt < KT; ++kt) {
+      k_tile(IntC<1>{}, kt, st, next(st), prev(st), kt + S - 1);
+      st = next(st);
+    }
+    wait_vmcnt<0>();
     barrier_lds();  // every wave is done reading the ring
 
     // ---- fused epilogue ---------------------------------------------------
+    // One element type for every C/X/D/Y in use and that type fp16 (8
+    // elements per lane) or int32: the one-type epilogue; otherwise the
+    // mixed-type one (4 elements per lane: 16 bytes of fp32 as in a one-type
+    // fp32 epilogue, 8 of fp16/bf16).
+    constexpr bool NM = CF::CD_NMAJOR;
     const int emw = m0 + wm * CF::WM, enw = n0 + wn * CF::WN;
     if constexpr (CF::AB == T_I8) {
-      epilogue_typed<CF, T_I32>(p, acc, lds, wave, lane, l, emw, enw);
+      epilogue_typed<CF, NM, T_I32>(p, acc, lds, wave, lane, l, emw, enw);
     } else {
-      if (p.epi_kind == T_F16) epilogue_typed<CF, T_F16>(p, acc, lds, wave, lane, l, emw, enw);
-      else if (p.epi_kind == T_BF16) epilogue_typed<CF, T_BF16>(p, acc, lds, wave, lane, l, emw, enw);
-      else if (p.epi_kind == T_F32) epilogue_typed<CF, T_F32>(p, acc, lds, wave, lane, l, emw, enw);
-      else epilogue_mixed<CF>(p, acc, lds, wave, lane, l, emw, enw);
+      if (p.epi_kind == T_F16) epilogue_typed<CF, NM, T_F16>(p, acc, lds, wave, lane, l, emw, enw);
+      else epilogue_mixed<CF, NM>(p, acc, lds, wave, lane, l, emw, enw);
     }
     barrier_lds();  // LDS is reused by the next tile's prologue
   }

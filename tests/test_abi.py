@@ -121,8 +121,8 @@ def test_mixed_epilogue_types_run_on_every_block_shape():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
-    desc = ge.make_desc(300, 264, 128, 1, ab="bf16", c="f32", x="bf16", d="f32")
-    for v in ("bf16_kk_n_256x256_r128_w4_s2_b16", "bf16_kk_n_256x256_r128_w4_s2_q2"):
+    for v, cd in (("bf16_kk_n_256x256_r128_w4_s2_b16", "N"), ("bf16_kk_m_256x256_r128_w4_s2_q2", "M")):
+        desc = ge.make_desc(304, 264, 128, 1, ab="bf16", c="f32", x="bf16", d="f32", cd_major=cd)
         h = ctypes.c_void_p()
         assert ge.lib().gemm_epi_create_variant(ctypes.byref(desc), names.index(v),
                                                 ctypes.byref(h)) == ge.GEMM_EPI_ERR_DEVICE
@@ -131,16 +131,17 @@ def test_mixed_epilogue_types_run_on_every_block_shape():
 
 def test_fp8_with_fp32_outputs_only_on_widening_variants():
     """fp8 A/B with an fp32 D or Y run the kernels that widen fp8 to fp16: an
-    fp8-MFMA variant refuses such a problem, a widening one accepts it, and a
-    widening one refuses fp8 problems without fp32 outputs."""
+    fp8-MFMA variant refuses such a problem, a widening one accepts it (and
+    also accepts fp8 problems without fp32 outputs, any pairing)."""
     names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
     f8 = names.index("e4m3_kk_n_256x256_r128_w4_s2")
-    w = names.index("e4m3w_kk_n_256x256_r128_w4_s2_b16")
+    w = names.index("f8w_kk_n_256x256_r128_w4_s2_b16")
     h = ctypes.c_void_p()
-    for d, y, v, ok in (("f32", None, f8, False), ("f16", "f32", f8, False),
-                        ("f32", None, w, True), ("f16", "f32", w, True),
-                        ("f16", None, w, False), ("f16", None, f8, True)):
-        desc = ge.make_desc(256, 256, 256, 1, ab="e4m3", c="f16", d=d, y=y)
+    for d, y, v, ok, b in (("f32", None, f8, False, None), ("f16", "f32", f8, False, None),
+                           ("f32", None, w, True, None), ("f16", "f32", w, True, None),
+                           ("f16", None, w, True, None), ("f16", None, f8, True, None),
+                           ("f16", None, w, True, "e5m2"), ("f16", None, f8, False, "e5m2")):
+        desc = ge.make_desc(256, 256, 256, 1, ab="e4m3", c="f16", d=d, y=y, b=b)
         rc = ge.lib().gemm_epi_create_variant(ctypes.byref(desc), v, ctypes.byref(h))
         if ok:
             assert rc in (ge.GEMM_EPI_OK, ge.GEMM_EPI_ERR_DEVICE), (d, y, names[v])
@@ -150,11 +151,31 @@ def test_fp8_with_fp32_outputs_only_on_widening_variants():
             assert rc == ge.GEMM_EPI_ERR_UNSUPPORTED, (d, y, names[v], rc)
 
 
-def test_unsupported_layout_is_an_error_not_a_fallback():
-    rc, _ = _create(b_major="N")  # no N-major B kernel yet
-    assert rc in (ge.GEMM_EPI_ERR_UNSUPPORTED, ge.GEMM_EPI_ERR_DEVICE)
-    if rc == ge.GEMM_EPI_ERR_UNSUPPORTED:
-        assert "no kernel" in ge.last_error()
+def test_every_majorness_has_a_kernel():
+    """Every A/B type with every A ('K', 'M'), B ('K', 'N') and C/D ('N', 'M')
+    majorness is accepted by static validation (with no GPU here, creation
+    stops at the device query, never at "no kernel")."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    for ab, b, outs in (("f16", None, "f16"), ("bf16", None, "f32"), ("e4m3", None, "f16"),
+                        ("e5m2", None, "f16"), ("e4m3", "e5m2", "f16"), ("e5m2", "e4m3", "f32"),
+                        ("i8", None, "i32")):
+        for a_major in "KM":
+            for b_major in "KN":
+                for cd in "NM":
+                    rc, h = _create(ab=ab, b=b, a_major=a_major, b_major=b_major, cd_major=cd,
+                                    c=outs, x=None, d=outs, y=None)
+                    assert rc == ge.GEMM_EPI_ERR_DEVICE, (ab, b, a_major, b_major, cd, rc,
+                                                          ge.last_error())
+
+
+def test_too_large_mn_major_operand_is_an_error_not_a_fallback():
+    """An M-major A beyond 2 GiB per batch cannot be addressed with the
+    kernels' 32-bit offsets: refused at create, before any device query."""
+    rc, _ = _create(a_major="M", M=65536, K=32768, N=16)
+    assert rc == ge.GEMM_EPI_ERR_UNSUPPORTED, ge.last_error()
+    assert "2 GiB" in ge.last_error()
 
 
 def test_run_and_plan_reject_null_handle():

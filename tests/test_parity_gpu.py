@@ -84,31 +84,46 @@ EDGE = [
     # mixed C/X/D/Y types (general epilogue), ragged N
     CFG[1].replace(name="mixed_types_ragged", M=300, N=264, K=128, c="f32", x="bf16",
                    y="bf16", x_factor=0.5, seed=7060),
+    # M-major A and N-major B (transposing LDS reads): ragged M, N and K tails,
+    # K shorter than one K tile, tiny extents, every type
+    CFG[2].replace(name="mn_f16_ktail", M=264, N=136, K=72, a_major="M", b_major="N", seed=7100),
+    CFG[2].replace(name="mn_f16_tiny", M=8, N=16, K=8, L=3, a_major="M", b_major="N", seed=7110),
+    CFG[1].replace(name="kn_bf16_cdm", M=300, N=264, K=200, b_major="N", cd_major="M", seed=7120),
+    CFG[1].replace(name="mk_bf16_ragged", M=200, N=300, K=264, a_major="M", seed=7125),
+    CFG[4].replace(name="mk_e4m3", M=272, N=296, K=176, a_major="M", seed=7130),
+    CFG[4].replace(name="kn_e4m3_cdm", M=296, N=272, K=144, b_major="N", cd_major="M", seed=7135),
+    CFG[4].replace(name="mn_e4e5_pair_widened", M=272, N=288, K=160, a_major="M", b_major="N",
+                   b_ab="e5m2", dist_b="e5m2tab", seed=7140),
+    CFG[3].replace(name="mn_i8_short_k", M=272, N=272, K=48, L=2, b_major="N", seed=7150),
+    CFG[3].replace(name="kn_i8_xy", M=260, N=272, K=272, L=1, a_major="K", b_major="N",
+                   x="i32", y="i32", alpha=-3.0, beta=2.0, x_factor=5.0, dist_x="i1000",
+                   seed=7160),
 ]
 
 
 def test_general_epilogue_both_block_shapes_ragged_n():
-    """Mixed C/X/D/Y types run the general epilogue on the 16x16-block default
-    and on a 32x32-block variant alike: linear and ReLU forms, a ragged N
-    tile, with and without Y, batched.  (M = 191, N = 344 with f32 C and bf16
-    D/Y once gave wrong values with 16x16 blocks; the packing of 2-byte
-    results went through a pointer of another type.)"""
+    """Mixed C/X/D/Y types run the mixed-type epilogue on the 16x16-block
+    default and on a 32x32-block variant alike (N-major: 16x16; M-major
+    C/D: 32x32; forced 32x32 for f16 N-major): linear and ReLU forms, a
+    ragged N tile, with and without Y, batched.  (M = 191, N = 344 with f32
+    C and bf16 D/Y once gave wrong values with 16x16 blocks.)"""
     import beta_epilogue_amd as ge
     names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
-    for v in ("bf16_kk_n_256x256_r128_w4_s2_b16", "bf16_kk_n_256x256_r128_w4_s2_q2"):
+    for cd, v in (("N", "bf16_kk_n_256x256_r128_w4_s2_b16"), ("M", "bf16_kk_m_256x256_r128_w4_s2_q2")):
         for epi in ("linear", "relu"):
             for y in (None, "bf16"):
-                p = CFG[1].replace(name="general_%s_%s_%s" % (v, epi, y), M=191, N=344, K=200,
-                                   L=2, c="f32", x="bf16", y=y, d="bf16" if y else "f32",
-                                   x_factor=0.5, beta=-1.0 if epi == "relu" else 1.0,
-                                   epilogue=epi, seed=7070)
+                p = CFG[1].replace(name="general_%s_%s_%s" % (v, epi, y), M=192 if cd == "M" else 191,
+                                   N=344, K=200, L=2, c="f32", x="bf16", y=y,
+                                   d="bf16" if y else "f32", x_factor=0.5, cd_major=cd,
+                                   beta=-1.0 if epi == "relu" else 1.0, epilogue=epi, seed=7070)
                 _say("case", p.name)
-                _, plan = parity_full(p, variant=names.index(v))
-                assert plan["name"] == v
-    p = CFG[1].replace(name="general_default", M=191, N=344, K=200, c="f32", x="bf16",
-                       y="bf16", d="bf16", x_factor=0.5, seed=7071)
-    _, plan = parity_full(p)
-    assert plan["name"] == "bf16_kk_n_256x256_r128_w4_s2_b16", plan["name"]
+                _, plan = parity_full(p)
+                assert plan["name"] == v, plan["name"]
+    v = "f16_kk_n_256x256_r128_w4_s2_q2"
+    p = CFG[2].replace(name="general_" + v, M=191, N=344, K=200, L=2, c="f32", x="bf16",
+                       y="f16", d="bf16", x_factor=0.5, seed=7071)
+    _, plan = parity_full(p, variant=names.index(v))
+    assert plan["name"] == v
 
 
 @pytest.mark.parametrize("p", EDGE, ids=[e.name for e in EDGE])
@@ -315,32 +330,29 @@ def test_beta_zero_does_not_read_c():
 
 
 def test_every_variant_runs():
-    """Each compiled kernel variant passes parity on a problem it accepts."""
+    """Each compiled kernel variant passes parity on a problem it accepts (its
+    A/B type, A, B and C/D majorness; ragged M, N, K; two batches)."""
     import beta_epilogue_amd as ge
     names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
     base = {
         "f16": CFG[2].replace(M=264, N=272, K=136, L=2),
         "bf16": CFG[1].replace(M=264, N=272, K=136, L=2),
-        "e4m3": CFG[4].replace(M=264, N=272, K=144, L=2),
-        "e5m2": CFG[4].replace(M=264, N=272, K=144, L=2, ab="e5m2", dist_ab="e5m2tab"),
-        "e4e5": CFG[4].replace(M=264, N=272, K=144, L=2, b_ab="e5m2", dist_b="e5m2tab"),
-        "e5e4": CFG[4].replace(M=264, N=272, K=144, L=2, ab="e5m2", dist_ab="e5m2tab",
+        "e4m3": CFG[4].replace(M=272, N=288, K=144, L=2),
+        "e5m2": CFG[4].replace(M=272, N=288, K=144, L=2, ab="e5m2", dist_ab="e5m2tab"),
+        "e4e5": CFG[4].replace(M=272, N=288, K=144, L=2, b_ab="e5m2", dist_b="e5m2tab"),
+        "e5e4": CFG[4].replace(M=272, N=288, K=144, L=2, ab="e5m2", dist_ab="e5m2tab",
                                b_ab="e4m3", dist_b="e4m3tab"),
-        "i8": CFG[3].replace(M=272, N=264, K=144, L=2),
-        "e4m3w": CFG[4].replace(M=264, N=272, K=144, L=2, d="f32", c="f32"),
-        "e5m2w": CFG[4].replace(M=264, N=272, K=144, L=2, ab="e5m2", dist_ab="e5m2tab",
-                                d="f16", y="f32"),
-        "e4e5w": CFG[4].replace(M=264, N=272, K=144, L=2, b_ab="e5m2", dist_b="e5m2tab",
-                                d="f32"),
-        "e5e4w": CFG[4].replace(M=264, N=272, K=144, L=2, ab="e5m2", dist_ab="e5m2tab",
-                                b_ab="e4m3", dist_b="e4m3tab", d="f32", x="f32", x_factor=0.5),
+        "i8": CFG[3].replace(M=272, N=288, K=144, L=2),
+        # widening kernels: an fp32 output, an e5m2 x e4m3 pairing
+        "f8w": CFG[4].replace(M=272, N=288, K=144, L=2, ab="e5m2", dist_ab="e5m2tab",
+                              b_ab="e4m3", dist_b="e4m3tab", d="f32", x="f32", x_factor=0.5),
     }
     for i, name in enumerate(names):
-        ab, layout = name.split("_")[0], name.split("_")[1:3]
+        ab, layout, cd = name.split("_")[0:3]
         p = base[ab].replace(name="variant_" + name,
-                             a_major="K" if layout[0][0] == "k" else "M",
-                             b_major="K" if layout[0][1] == "k" else "N",
-                             cd_major=layout[1].upper())
+                             a_major="K" if layout[0] == "k" else "M",
+                             b_major="K" if layout[1] == "k" else "N",
+                             cd_major=cd.upper())
         _say("variant", i, name)
         (ed, ey), plan = parity_full(p, variant=i)
         assert plan["name"] == name
@@ -403,7 +415,8 @@ def _random_problem(i):
     dist = {"f16": "normal", "bf16": "normal", "e4m3": "e4m3tab", "e5m2": "e5m2tab",
             "i8": "i8full"}
     cd = "NM"[int(rng.integers(2))]
-    a_major = "M" if ab == "i8" and rng.integers(2) else "K"
+    a_major = "KM"[int(rng.integers(2))]
+    b_major = "KN"[int(rng.integers(2))]
     kq = 8 if ab in ("f16", "bf16") else 16
     K = int(kq * rng.integers(1, 40))
     L = int(rng.integers(1, 4))
@@ -423,15 +436,17 @@ def _random_problem(i):
         N = max(cdq, N // cdq * cdq)
     else:
         M = max(cdq, M // cdq * cdq)
-    if a_major == "M":
+    if a_major == "M":  # the 16-byte rule on M-major A / N-major B
         M = max(16, M // 16 * 16)
+    if b_major == "N":
+        N = max(16, N // 16 * 16)
     if ab == "i8":
         alpha, beta, xf = (float(rng.integers(-3, 4)) for _ in range(3))
     else:
         alpha, beta, xf = (float(np.round(rng.uniform(-2, 2), 3)) for _ in range(3))
     return synth.Problem(
-        "random_%d_%s_%s%s_%s" % (i, kind, a_major.lower(), cd.lower(), d), M, N, K, L, ab,
-        a_major=a_major, cd_major=cd, c=c, x=x, d=d, y=y, alpha=alpha,
+        "random_%d_%s_%s%s%s_%s" % (i, kind, a_major.lower(), b_major.lower(), cd.lower(), d),
+        M, N, K, L, ab, a_major=a_major, b_major=b_major, cd_major=cd, c=c, x=x, d=d, y=y, alpha=alpha,
         beta=beta if c else 0.0, x_factor=xf if x else 0.0, dist_ab=dist[ab],
         dist_c="i1000" if ab == "i8" else "normal", dist_x="i1000" if ab == "i8" else "normal",
         seed=9100 + 10 * i, epilogue="relu" if rng.integers(2) else "linear", b_ab=b_ab,
