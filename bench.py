@@ -136,7 +136,8 @@ def main():
                     help="workload index 0..4 (2 = 8192^3 fp16 with C, X, D, Y); 5 = the same at K=256 (HBM-bound)")
     ap.add_argument("--epilogue", choices=("linear", "relu"), default="linear",
                     help="relu: D = max(0, alpha*A.B^T + beta*C) + x_factor*X")
-    ap.add_argument("--variant", type=int, default=-1)
+    ap.add_argument("--variant", default="-1",
+                    help="kernel variant: table index or name (-1: the default for the workload)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true",
@@ -186,9 +187,13 @@ def main():
     shape = p.storage_shape("D")
     D = torch.empty(shape, dtype=synth.TORCH_DTYPE[p.d], device="cuda")
     Y = torch.empty(shape, dtype=synth.TORCH_DTYPE[p.y], device="cuda") if p.y else None
+    variant = args.variant
+    if not variant.lstrip("-").isdigit():
+        names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
+        variant = names.index(variant)
     g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, a_major=p.a_major,
                      b_major=p.b_major, cd_major=p.cd_major, c=p.c, x=p.x,
-                     d=p.d, y=p.y, variant=args.variant, epilogue=p.epilogue)
+                     d=p.d, y=p.y, variant=int(variant), epilogue=p.epilogue)
     plan = g.plan
     stream = torch.cuda.current_stream()
 

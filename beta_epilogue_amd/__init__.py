@@ -38,7 +38,8 @@ class gemm_epi_desc(ctypes.Structure):
                 ("cd_major", ctypes.c_int32), ("ab_dtype", ctypes.c_int32),
                 ("c_dtype", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
                 ("d_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32),
-                ("epilogue", ctypes.c_int32), ("b_dtype", ctypes.c_int32)]
+                ("epilogue", ctypes.c_int32), ("b_dtype", ctypes.c_int32),
+                ("splits", ctypes.c_int32)]
 
 
 class gemm_epi_plan(ctypes.Structure):
@@ -46,7 +47,8 @@ class gemm_epi_plan(ctypes.Structure):
                 ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("tiles", ctypes.c_int64), ("lds_bytes", ctypes.c_int32),
-                ("cus", ctypes.c_int32), ("name", ctypes.c_char * 64)]
+                ("cus", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64), ("name", ctypes.c_char * 64)]
 
 
 class GemmEpiError(RuntimeError):
@@ -110,12 +112,13 @@ EPILOGUES = {"linear": 0, "relu": 1}
 
 def make_desc(M, N, K, L=1, *, ab="f16", a_major="K", b_major="K",
               cd_major="N", c=None, x=None, d="f32", y=None,
-              epilogue="linear", b=None) -> gemm_epi_desc:
-    """b: B's own type when it differs from A's (the fp8 pairs)."""
+              epilogue="linear", b=None, splits=0) -> gemm_epi_desc:
+    """b: B's own type when it differs from A's (the fp8 pairs); splits: 0
+    (the library's choice), 1 (no split-K) or the number of K slices."""
     return gemm_epi_desc(M, N, K, L, MAJOR[a_major], MAJOR[b_major],
                          MAJOR[cd_major], DTYPES[ab], DTYPES[c], DTYPES[x],
                          DTYPES[d], DTYPES[y], EPILOGUES[epilogue],
-                         DTYPES[b] if b and b != ab else 0)
+                         DTYPES[b] if b and b != ab else 0, splits)
 
 
 def gemm_epi_create(desc: gemm_epi_desc) -> int:
@@ -150,6 +153,7 @@ def gemm_epi_get_plan(h: int) -> dict:
     return {"variant": p.variant, "tile_m": p.tile_m, "tile_n": p.tile_n,
             "tile_k": p.tile_k, "threads": p.threads, "grid": p.grid,
             "tiles": p.tiles, "lds_bytes": p.lds_bytes, "cus": p.cus,
+            "splits": p.splits, "workspace_bytes": p.workspace_bytes,
             "name": p.name.decode()}
 
 
@@ -172,10 +176,10 @@ class FusedGemm:
 
     def __init__(self, M, N, K, L=1, *, ab="f16", a_major="K", b_major="K",
                  cd_major="N", c=None, x=None, d="f32", y=None, variant=-1,
-                 epilogue="linear", b=None):
+                 epilogue="linear", b=None, splits=0):
         self.desc = make_desc(M, N, K, L, ab=ab, a_major=a_major,
                               b_major=b_major, cd_major=cd_major, c=c, x=x,
-                              d=d, y=y, epilogue=epilogue, b=b)
+                              d=d, y=y, epilogue=epilogue, b=b, splits=splits)
         self.shape = (M, N, K, L)
         self.handle = (gemm_epi_create(self.desc) if variant == -1
                        else gemm_epi_create_variant(self.desc, variant))

@@ -18,10 +18,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgemm_epi.so")
 MAIN_SOURCE = os.path.join(CSRC, "gemm_epi.hip")
+SPLITK_SOURCE = os.path.join(CSRC, "gemm_epi_splitk.hip")
 PART_SOURCE = os.path.join(CSRC, "gemm_epi_part.hip")
-GEMM_EPI_PARTS = 8
-SOURCES = [MAIN_SOURCE, PART_SOURCE]
+GEMM_EPI_PARTS = 16
+SOURCES = [MAIN_SOURCE, PART_SOURCE, SPLITK_SOURCE]
 HEADERS = [os.path.join(CSRC, "gemm_epi_kernel.hpp"), os.path.join(CSRC, "gemm_epi_launch.hpp"),
+           os.path.join(CSRC, "gemm_epi_splitk.hpp"),
            os.path.join(CSRC, "gemm_epi_variants.inc"), os.path.join(ROOT, "include", "gemm_epi.h")]
 # measurement tool used by bench.py --mfma-ceiling (not part of the GEMM path)
 CEILING_LIB = os.path.join(HERE, "libmfma_ceiling.so")
@@ -56,23 +58,54 @@ def _jobs() -> int:
     return max(1, min(n, 16))
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def _variant_subset(tmp: str, names) -> list:
+    """A copy of the variant table holding only the named variants, in an
+    include directory searched before csrc/ (a partial build for
+    development; the library then has only those kernels)."""
+    src = os.path.join(CSRC, "gemm_epi_variants.inc")
+    keep, found = [], set()
+    for line in open(src):
+        if line.startswith("X("):
+            name = line.rsplit('"', 2)[1]
+            if name not in names:
+                continue
+            found.add(name)
+        keep.append(line)
+    missing = set(names) - found
+    if missing:
+        raise ValueError("unknown variants: %s" % ", ".join(sorted(missing)))
+    d = os.path.join(tmp, "subset")
+    os.makedirs(d)
+    with open(os.path.join(d, "gemm_epi_variants.inc"), "w") as f:
+        f.writelines(keep)
+    return ["-I", d]
+
+
+def build(verbose: bool = False, extra=(), only=None) -> str:
     """Compile libgemm_epi.so and libmfma_ceiling.so next to this file
-    (always recompiles)."""
+    (always recompiles).  only: variant names to compile (default: every
+    variant; the GEMM_EPI_ONLY environment variable, comma-separated, sets it
+    too)."""
     extra = list(extra)
+    if only is None and os.environ.get("GEMM_EPI_ONLY"):
+        only = [n for n in os.environ["GEMM_EPI_ONLY"].split(",") if n]
     with tempfile.TemporaryDirectory(prefix="gemm_epi_build_") as tmp:
+        if only:
+            extra = extra + _variant_subset(tmp, set(only))
         jobs = [(["hipcc"] + HIPCC_FLAGS + extra + INCLUDES +
                  ["-c", "-DGEMM_EPI_PART=%d" % k, "-o", os.path.join(tmp, "part%d.o" % k), PART_SOURCE])
                 for k in range(GEMM_EPI_PARTS)]
         jobs.append(["hipcc"] + HIPCC_FLAGS + extra + INCLUDES +
                     ["-c", "-o", os.path.join(tmp, "main.o"), MAIN_SOURCE])
+        jobs.append(["hipcc"] + HIPCC_FLAGS + extra + INCLUDES +
+                    ["-c", "-o", os.path.join(tmp, "splitk.o"), SPLITK_SOURCE])
         ceil_tmp = CEILING_LIB + ".tmp%d" % os.getpid()
         jobs.append(["hipcc"] + HIPCC_FLAGS + INCLUDES + ["-shared", "-o", ceil_tmp, CEILING_SOURCE])
         with ThreadPoolExecutor(max_workers=_jobs()) as ex:
             for f in [ex.submit(_run, c, verbose) for c in jobs]:
                 f.result()
         lib_tmp = LIB + ".tmp%d" % os.getpid()
-        objs = [os.path.join(tmp, "main.o")] + [os.path.join(tmp, "part%d.o" % k)
+        objs = [os.path.join(tmp, "main.o"), os.path.join(tmp, "splitk.o")] + [os.path.join(tmp, "part%d.o" % k)
                                                 for k in range(GEMM_EPI_PARTS)]
         _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib_tmp] + objs, verbose)
         os.replace(ceil_tmp, CEILING_LIB)

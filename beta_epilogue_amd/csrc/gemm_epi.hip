@@ -10,15 +10,19 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "gemm_epi.h"
 #include "gemm_epi_kernel.hpp"
 #include "gemm_epi_launch.hpp"
+#include "gemm_epi_splitk.hpp"
 
 namespace {
 
@@ -70,7 +74,7 @@ using namespace gemm_epi;
 #define X(PART, AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, DS, BL, NAME) \
   make_variant<Cfg<AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, DS, BL>>(NAME),
 const Variant kVariants[] = {
-#include "gemm_epi_variants.inc"
+#include <gemm_epi_variants.inc>  // (angle brackets: a partial build can put its own table first)
 };
 #undef X
 #undef V
@@ -108,9 +112,16 @@ struct gemm_epi_handle {
   int grid;
   int cus;
   int device;
-  int64_t tiles_m, tiles_n, tiles;
+  int64_t tiles_m, tiles_n, tiles;  // output tiles (one K slice)
   int group_m;
+  int splits;                       // K slices (1: no split)
+  int64_t kslice;                   // K elements per slice
+  int64_t ws_bytes;                 // split-K workspace: splits * L*M*N * 4 bytes
+  std::atomic<void*> ws{nullptr};   // allocated by the first gemm_epi_run, freed by destroy
+  std::mutex ws_mutex;
 };
+
+
 
 // Static validation: everything that needs no device.
 static int validate_desc(const gemm_epi_desc* d) {
@@ -133,6 +144,7 @@ static int validate_desc(const gemm_epi_desc* d) {
       !((d->ab_dtype == GEMM_EPI_E4M3 || d->ab_dtype == GEMM_EPI_E5M2) &&
         (d->b_dtype == GEMM_EPI_E4M3 || d->b_dtype == GEMM_EPI_E5M2)))
     return fail(GEMM_EPI_ERR_INVALID_ARG, "b_dtype may differ from ab_dtype only as the other fp8 format");
+  if (d->splits < 0) return fail(GEMM_EPI_ERR_INVALID_ARG, "splits must be >= 0 (got %d)", d->splits);
   if (d->epilogue != GEMM_EPI_LINEAR && d->epilogue != GEMM_EPI_RELU)
     return fail(GEMM_EPI_ERR_INVALID_ARG, "epilogue must be LINEAR or RELU (got %d)", d->epilogue);
   const int ab = d->ab_dtype;
@@ -258,8 +270,21 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   h->tiles_n = (desc->N + v.bn - 1) / v.bn;
   h->tiles = h->tiles_m * h->tiles_n * desc->L;
   h->group_m = 4;
-  const int64_t occupancy = 1;  // one 256x256 workgroup per compute unit
-  h->grid = (int)std::min<int64_t>(h->tiles, (int64_t)h->cus * occupancy);
+  // Split K when the output tiles cannot fill half of the compute units and
+  // K is long: each slice gets at least four K tiles, at most 16 slices.
+  const int64_t ktiles = (desc->K + v.bk - 1) / v.bk;
+  int64_t splits = 1;
+  if (desc->splits >= 1) {
+    splits = std::min<int64_t>(desc->splits, ktiles);
+  } else if (h->tiles * 2 <= h->cus && ktiles >= 8) {
+    splits = std::min<int64_t>(std::min<int64_t>(h->cus / h->tiles, ktiles / 4), 16);
+  }
+  if (splits < 1) splits = 1;
+  h->kslice = ((ktiles + splits - 1) / splits) * v.bk;
+  h->splits = (int)((desc->K + h->kslice - 1) / h->kslice);
+  if (h->splits == 1) h->kslice = desc->K;
+  h->ws_bytes = h->splits > 1 ? (int64_t)h->splits * desc->L * desc->M * desc->N * 4 : 0;
+  h->grid = (int)std::min<int64_t>(h->tiles * h->splits, (int64_t)h->cus);  // one workgroup per CU
   *out = h;
   return GEMM_EPI_OK;
 }
@@ -272,11 +297,13 @@ static bool integral_24(float v) {
   return std::isfinite(v) && std::nearbyint(v) == v && std::fabs(v) <= 16777216.0f;
 }
 
-extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void* B, const void* C,
-                            const void* X, void* D, void* Y, float alpha, float beta,
-                            float x_factor, void* stream) {
+// One fused GEMM; split-K plans use the handle's workspace (allocated here on
+// first use).
+static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, const void* C, const void* X,
+                    void* D, void* Y, float alpha, float beta, float x_factor, void* stream) {
   g_last_error[0] = 0;
-  if (!h) return fail(GEMM_EPI_ERR_INVALID_ARG, "handle is NULL");
+  if (!hc) return fail(GEMM_EPI_ERR_INVALID_ARG, "handle is NULL");
+  gemm_epi_handle* h = const_cast<gemm_epi_handle*>(hc);  // only the lazily allocated workspace changes
   const gemm_epi_desc& d = h->desc;
   if (!A || !B || !D) return fail(GEMM_EPI_ERR_INVALID_ARG, "A, B and D are required");
   const bool use_c = d.c_dtype != GEMM_EPI_NONE && beta != 0.0f;
@@ -312,7 +339,7 @@ extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void*
   p.M = d.M;
   p.N = d.N;
   p.K = d.K;
-  p.tiles_total = h->tiles;
+  p.tiles_total = h->tiles * h->splits;
   p.L = (int32_t)d.L;
   p.tiles_m = (int32_t)h->tiles_m;
   p.tiles_n = (int32_t)h->tiles_n;
@@ -337,15 +364,65 @@ extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void*
   for (int t : {use_c ? d.c_dtype : 0, use_x ? d.x_dtype : 0, d.y_dtype})
     if (t != GEMM_EPI_NONE && t != kind) kind = 0;
   p.epi_kind = kind;
+  p.splits = h->splits;
+  p.kslice = h->kslice;
+  p.ws = nullptr;
+  if (h->splits > 1) {
+    p.ws = h->ws.load();
+    if (!p.ws) {
+      std::lock_guard<std::mutex> lock(h->ws_mutex);
+      p.ws = h->ws.load();
+      if (!p.ws) {
+        if (hipMalloc(&p.ws, (size_t)h->ws_bytes) != hipSuccess || !p.ws)
+          return fail(GEMM_EPI_ERR_DEVICE, "hipMalloc of a %lld-byte split-K workspace failed",
+                      (long long)h->ws_bytes);
+        h->ws.store(p.ws);
+      }
+    }
+  }
 
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   kVariants[h->variant].launch(p, h->grid, (hipStream_t)stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GEMM_EPI_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  if (h->splits > 1) {
+    // the slices' sums and the epilogue, on the same stream
+    gemm_epi::SplitkParams q;
+    q.ws = p.ws;
+    q.C = p.C;
+    q.X = p.X;
+    q.D = D;
+    q.Y = Y;
+    q.groups = d.L * d.M * d.N / 4;
+    q.splits = h->splits;
+    q.c_dtype = p.c_dtype;
+    q.x_dtype = p.x_dtype;
+    q.d_dtype = p.d_dtype;
+    q.y_dtype = p.y_dtype;
+    q.int_path = int_path ? 1 : 0;
+    q.alpha = alpha;
+    q.beta = beta;
+    q.xf = x_factor;
+    q.ialpha = p.ialpha;
+    q.ibeta = p.ibeta;
+    q.ix = p.ix;
+    q.relu = p.relu;
+    const int64_t blocks = (q.groups + 255) / 256;
+    gemm_epi::launch_splitk_epilogue(q, (int)std::min<int64_t>(blocks, (int64_t)h->cus * 8), (hipStream_t)stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(GEMM_EPI_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  }
   return GEMM_EPI_OK;
 }
 
+extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void* B, const void* C,
+                            const void* X, void* D, void* Y, float alpha, float beta,
+                            float x_factor, void* stream) {
+  return run_impl(h, A, B, C, X, D, Y, alpha, beta, x_factor, stream);
+}
+
 extern "C" int gemm_epi_destroy(gemm_epi_handle* h) {
+  if (h && h->ws.load()) (void)hipFree(h->ws.load());
   delete h;
   return GEMM_EPI_OK;
 }
@@ -363,6 +440,8 @@ extern "C" int gemm_epi_get_plan(const gemm_epi_handle* h, gemm_epi_plan* out) {
   out->tiles = h->tiles;
   out->lds_bytes = v.lds;
   out->cus = h->cus;
+  out->splits = h->splits;
+  out->workspace_bytes = h->ws_bytes;
   std::snprintf(out->name, sizeof out->name, "%s", v.name);
   return GEMM_EPI_OK;
 }

@@ -81,6 +81,14 @@ struct Params {
   int32_t epi_kind;           // element type shared by every C/X/D/Y in use (0: mixed)
   int32_t relu;               // D = max(0, alpha*acc + beta*C) + x_factor*X
   int32_t f8a, f8b;           // widening kernels: fp8 format of A, B (0 e4m3, 1 e5m2)
+  // Split K: the K range is cut into `splits` slices of kslice elements (a
+  // multiple of the K tile; the last one may be shorter).  With splits > 1 a
+  // tile of slice s writes its fp32 (int32) partial sums to ws + s * L*M*N
+  // (D's layout) instead of running the epilogue; a second kernel adds the
+  // slices and applies the epilogue.  splits == 1: kslice == K, ws unused.
+  int32_t splits;
+  int64_t kslice;
+  void* ws;
 };
 
 // ---------------------------------------------------------------------------
@@ -407,15 +415,17 @@ struct KMajorOperand {
   uint32_t cb;     // byte offset of this lane's logical chunk within its row
   int row0, q;     // reader: LDS row of this lane in block 0, its k share
 
-  // batch: the operand's batch l; extent: M (A) or N (B); r0: the tile's
-  // first row.
-  __device__ __forceinline__ void setup(const char* batch, int64_t extent, int64_t K, int r0, int wave,
-                                        int lane) {
+  // batch: the operand's batch l; extent: M (A) or N (B); K: the full K
+  // (the row length); kbeg: the first k of the K range staged (a K slice);
+  // r0: the tile's first row.
+  __device__ __forceinline__ void setup(const char* batch, int64_t extent, int64_t K, int64_t kbeg, int r0,
+                                        int wave, int lane) {
     const int64_t ld_bytes = K * CF::MM::ESIZE;
+    const int64_t kb = kbeg * CF::MM::ESIZE;
     const int rsub = lane / CF::CH;
     const int pc = lane % CF::CH;
     const int valid_rows = (int)min((int64_t)R, extent - r0);
-    rsrc = make_rsrc(batch + (int64_t)r0 * ld_bytes, (uint32_t)((int64_t)valid_rows * ld_bytes));
+    rsrc = make_rsrc(batch + (int64_t)r0 * ld_bytes + kb, (uint32_t)((int64_t)valid_rows * ld_bytes - kb));
     cb = (uint32_t)((pc ^ swz<CF>(wave * CF::ROWS_PER_DMA + rsub)) * 16);
     voff = (uint32_t)((wave * CF::ROWS_PER_DMA + rsub) * ld_bytes) + cb;
     qstep = (uint32_t)(CF::NW * CF::ROWS_PER_DMA * ld_bytes);
@@ -529,10 +539,12 @@ struct MNMajorOperand {
   uint32_t qstep;    // bytes between instructions i and i + 2
   int raddr;         // reader: LDS byte offset of block 0 (k step 0, read 0)
 
-  __device__ __forceinline__ void setup(const char* batch, int64_t extent, int64_t K, int r0, int wave,
-                                        int lane) {
+  // A K slice other than the last is a whole number of K tiles, so every
+  // k-row staged from it lies inside it; k-rows past K read as zero.
+  __device__ __forceinline__ void setup(const char* batch, int64_t extent, int64_t K, int64_t kbeg, int r0,
+                                        int wave, int lane) {
     const int64_t ldb = extent * ES;  // bytes of one global k-row
-    rsrc = make_rsrc(batch + (int64_t)r0 * ES, (uint32_t)(K * ldb - (int64_t)r0 * ES));
+    rsrc = make_rsrc(batch + (int64_t)r0 * ES + kbeg * ldb, (uint32_t)((K - kbeg) * ldb - (int64_t)r0 * ES));
     kstride = (uint32_t)(BK * ldb);
     qstep = (uint32_t)(2 * CF::NW * RPI * ldb);
 #pragma unroll
@@ -944,9 +956,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
   const int bid = blockIdx.x;
   const int g = p.xcd_remap ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
 
-  const int64_t kbytes = p.K * ES;
-  const int KT = (int)((kbytes + CF::ROWB - 1) / CF::ROWB);
   const int64_t tiles_mn = (int64_t)p.tiles_m * p.tiles_n;
+  const int64_t tiles_split = (int64_t)p.L * tiles_mn;  // tiles of one K slice
 
   using OpA = Operand<CF, BM, CF::WM, CF::A_KMAJOR>;
   using OpB = Operand<CF, BN, CF::WN, CF::B_KMAJOR>;
@@ -969,9 +980,14 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
   };
 
   for (int64_t t = g; t < p.tiles_total; t += G) {
-    // ---- tile coordinates: grouped raster inside each batch -------------
-    const int l = (int)(t / tiles_mn);
-    const int64_t r = t - (int64_t)l * tiles_mn;
+    // ---- tile coordinates: K slice, batch, grouped raster inside a batch ---
+    const int split = (int)(t / tiles_split);
+    const int64_t ts = t - (int64_t)split * tiles_split;
+    const int l = (int)(ts / tiles_mn);
+    const int64_t r = ts - (int64_t)l * tiles_mn;
+    const int64_t kbeg = (int64_t)split * p.kslice;
+    const int64_t kbytes = min(p.K - kbeg, p.kslice) * ES;  // this slice's K, in bytes
+    const int KT = (int)((kbytes + CF::ROWB - 1) / CF::ROWB);
     const int64_t gsize = (int64_t)p.group_m * p.tiles_n;
     const int gid = (int)(r / gsize);
     const int first_m = gid * p.group_m;
@@ -982,8 +998,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     const int m0 = tm * BM, n0 = tn * BN;
 
     // ---- staging set-up --------------------------------------------------
-    opa.setup((const char*)p.A + (int64_t)l * p.M * kbytes, p.M, p.K, m0, wave, lane);
-    opb.setup((const char*)p.B + (int64_t)l * p.N * kbytes, p.N, p.K, n0, wave, lane);
+    opa.setup((const char*)p.A + (int64_t)l * p.M * p.K * ES, p.M, p.K, kbeg, m0, wave, lane);
+    opb.setup((const char*)p.B + (int64_t)l * p.N * p.K * ES, p.N, p.K, kbeg, n0, wave, lane);
 
     acc_t acc[CF::FM][CF::FN];
 #pragma unroll
@@ -1184,15 +1200,28 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
 
     // ---- fused epilogue ---------------------------------------------------
     // One element type for every C/X/D/Y in use and that type fp16 (8
-    // elements per lane) or int32: the one-type epilogue; otherwise the
-    // mixed-type one (4 elements per lane: 16 bytes of fp32 as in a one-type
-    // fp32 epilogue, 8 of fp16/bf16).
+    // elements per lane), fp32 or int32 (4): the one-type epilogue;
+    // otherwise (bf16 included) the mixed-type one (4 elements per lane).
     constexpr bool NM = CF::CD_NMAJOR;
     const int emw = m0 + wm * CF::WM, enw = n0 + wn * CF::WN;
-    if constexpr (CF::AB == T_I8) {
+    if (p.splits > 1) {
+      // a K slice: its partial sums, unscaled, into the slice's workspace
+      Params q = p;
+      q.D = (char*)p.ws + (int64_t)split * p.L * p.M * p.N * 4;
+      q.C = q.X = nullptr;
+      q.Y = nullptr;
+      q.alpha = 1.0f;
+      q.beta = q.xf = 0.0f;
+      q.ialpha = 1;
+      q.ibeta = q.ix = 0;
+      q.relu = 0;
+      if constexpr (CF::AB == T_I8) epilogue_typed<CF, NM, T_I32>(q, acc, lds, wave, lane, l, emw, enw);
+      else epilogue_typed<CF, NM, T_F32>(q, acc, lds, wave, lane, l, emw, enw);
+    } else if constexpr (CF::AB == T_I8) {
       epilogue_typed<CF, NM, T_I32>(p, acc, lds, wave, lane, l, emw, enw);
     } else {
       if (p.epi_kind == T_F16) epilogue_typed<CF, NM, T_F16>(p, acc, lds, wave, lane, l, emw, enw);
+      else if (p.epi_kind == T_F32) epilogue_typed<CF, NM, T_F32>(p, acc, lds, wave, lane, l, emw, enw);
       else epilogue_mixed<CF, NM>(p, acc, lds, wave, lane, l, emw, enw);
     }
     barrier_lds();  // LDS is reused by the next tile's prologue

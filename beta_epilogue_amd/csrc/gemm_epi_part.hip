@@ -4,7 +4,7 @@
 #include "gemm_epi_launch.hpp"
 
 #ifndef GEMM_EPI_PART
-#error "GEMM_EPI_PART must be defined (0 .. 7)"
+#error "GEMM_EPI_PART must be defined (0 .. 15)"
 #endif
 
 namespace gemm_epi {
@@ -24,6 +24,14 @@ void launch(const Params& p, int grid, hipStream_t s) {
 #define GEMM_EPI_PICK_5 GEMM_EPI_SKIP
 #define GEMM_EPI_PICK_6 GEMM_EPI_SKIP
 #define GEMM_EPI_PICK_7 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_8 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_9 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_10 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_11 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_12 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_13 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_14 GEMM_EPI_SKIP
+#define GEMM_EPI_PICK_15 GEMM_EPI_SKIP
 #if GEMM_EPI_PART == 0
 #undef GEMM_EPI_PICK_0
 #define GEMM_EPI_PICK_0 GEMM_EPI_INSTANTIATE
@@ -48,13 +56,37 @@ void launch(const Params& p, int grid, hipStream_t s) {
 #elif GEMM_EPI_PART == 7
 #undef GEMM_EPI_PICK_7
 #define GEMM_EPI_PICK_7 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 8
+#undef GEMM_EPI_PICK_8
+#define GEMM_EPI_PICK_8 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 9
+#undef GEMM_EPI_PICK_9
+#define GEMM_EPI_PICK_9 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 10
+#undef GEMM_EPI_PICK_10
+#define GEMM_EPI_PICK_10 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 11
+#undef GEMM_EPI_PICK_11
+#define GEMM_EPI_PICK_11 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 12
+#undef GEMM_EPI_PICK_12
+#define GEMM_EPI_PICK_12 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 13
+#undef GEMM_EPI_PICK_13
+#define GEMM_EPI_PICK_13 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 14
+#undef GEMM_EPI_PICK_14
+#define GEMM_EPI_PICK_14 GEMM_EPI_INSTANTIATE
+#elif GEMM_EPI_PART == 15
+#undef GEMM_EPI_PICK_15
+#define GEMM_EPI_PICK_15 GEMM_EPI_INSTANTIATE
 #else
 #error "GEMM_EPI_PART out of range"
 #endif
 #define GEMM_EPI_CAT(a, b) a##b
 #define X(PART, AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, DS, BL, NAME) \
   GEMM_EPI_CAT(GEMM_EPI_PICK_, PART)(AB, AK, BK, CDN, BM, BN, RB, WM, WN, S, DS, BL)
-#include "gemm_epi_variants.inc"
+#include <gemm_epi_variants.inc>  // (angle brackets: a partial build can put its own table first)
 #undef X
 
 }  // namespace gemm_epi

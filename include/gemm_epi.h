@@ -42,8 +42,9 @@
  *
  * Memory ownership: all tensor pointers are device pointers owned by the
  * caller, which keeps them alive until the work queued on the stream has
- * finished.  The library allocates no device memory; a handle is a small
- * host object.
+ * finished.  A handle is a small host object; the only device memory the
+ * library allocates is a split-K plan's workspace (see gemm_epi_run), owned
+ * by the handle.
  */
 #ifndef GEMM_EPI_H
 #define GEMM_EPI_H
@@ -97,6 +98,10 @@ typedef struct gemm_epi_desc {
   int32_t b_dtype;     /* NONE (0): B has ab_dtype.  Else the other fp8 format
                           for an fp8 ab_dtype: E4M3 x E5M2 or E5M2 x E4M3
                           (A's format x B's) */
+  int32_t splits;      /* K split: 0 = chosen by the library (split when the
+                          output tiles fill less than half of the GPU and K
+                          is long), 1 = never, n >= 2 = n slices (fewer if K
+                          has fewer K tiles) */
 } gemm_epi_desc;
 
 typedef struct gemm_epi_handle gemm_epi_handle;
@@ -110,6 +115,8 @@ typedef struct gemm_epi_plan {
   int64_t tiles;        /* L * ceil(M/tile_m) * ceil(N/tile_n) */
   int32_t lds_bytes;    /* LDS per workgroup */
   int32_t cus;          /* compute units of the device */
+  int32_t splits;       /* K slices (1: no split-K) */
+  int64_t workspace_bytes; /* split-K partial sums: splits * L*M*N * 4 (0 if none) */
   char name[64];        /* kernel variant name */
 } gemm_epi_plan;
 
@@ -161,6 +168,13 @@ int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
  * alpha, beta, x_factor : fp32 scalars.  With int32 outputs they must be
  *            integers of magnitude <= 2^24 (the epilogue is then exact int32
  *            arithmetic), else GEMM_EPI_ERR_UNSUPPORTED.
+ * Split-K plans (gemm_epi_plan.splits > 1) run two kernels on `stream`: the
+ * K slices write fp32 (int32) partial sums to a workspace of
+ * plan.workspace_bytes, then a second kernel adds them (in slice order) and
+ * applies the epilogue.  The first such run allocates the workspace
+ * (hipMalloc; it belongs to the handle and gemm_epi_destroy frees it), so
+ * runs of one split-K handle that overlap in time on different streams race
+ * on it.
  * Every pointer must be 16-byte aligned.  D may be C itself (the same
  * pointer, with d_dtype == c_dtype): an in-place update, since each output
  * element's C is read before its D is written by the same lane.  No other
@@ -173,9 +187,9 @@ int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void* B,
                  const void* C, const void* X, void* D, void* Y, float alpha,
                  float beta, float x_factor, void* stream);
 
-/* Free a handle (NULL is fine).  No run on it may still be being enqueued.
- * (The handle owns no device memory: the API card's "Host side" puts buffer
- * ownership with the caller.) */
+/* Free a handle and its split-K workspace, if any (NULL is fine).  No run on
+ * it may still be being enqueued or executing.  (Tensors are the caller's:
+ * the API card's "Host side" puts buffer ownership with the caller.) */
 int gemm_epi_destroy(gemm_epi_handle* h);
 
 /* Fill *out with what the handle launches (tile, grid and LDS sizes: the

@@ -59,13 +59,15 @@ class GuardedOut:
         return bool(torch.all(lo == s).item()) and bool(torch.all(hi == s).item())
 
 
-def run_gpu(p: synth.Problem, ins, variant=-1, check_inputs=True):
-    """Run problem p on the GPU through the C ABI.  Returns host D, Y."""
+def run_gpu(p: synth.Problem, ins, variant=-1, check_inputs=True, splits=0):
+    """Run problem p on the GPU through the C ABI.  Returns host D, Y.
+    splits: the K split asked for (0: the library's choice)."""
     dev = {k: (v.cuda() if v is not None else None) for k, v in ins.items()}
     keep = {k: v.clone() for k, v in dev.items() if v is not None and k in "CX"}
     g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, a_major=p.a_major,
                      b_major=p.b_major, cd_major=p.cd_major, c=p.c, x=p.x,
-                     d=p.d, y=p.y, variant=variant, epilogue=p.epilogue, b=p.b_ab)
+                     d=p.d, y=p.y, variant=variant, epilogue=p.epilogue, b=p.b_ab,
+                     splits=splits)
     shape = p.storage_shape("D")
     D = GuardedOut(p.d, shape)
     Y = GuardedOut(p.y, shape) if p.y else None
@@ -130,10 +132,10 @@ def check(p: synth.Problem, D_gpu, Y_gpu, Dref, Yref, S, cvals, xvals,
     return errd, erry
 
 
-def parity_full(p: synth.Problem, variant=-1, exact=False, ins=None):
+def parity_full(p: synth.Problem, variant=-1, exact=False, ins=None, splits=0):
     """Whole-output parity against the full oracle result."""
     ins = ins if ins is not None else synth.make_inputs(p)
-    D, Y, plan = run_gpu(p, ins, variant)
+    D, Y, plan = run_gpu(p, ins, variant, splits=splits)
     Dref, Yref, S = oracle.gemm_epi(p.M, p.N, p.K, p.L, ins["A"], ins["B"],
                                     ins["C"], ins["X"], ab=p.ab, b=p.b_ab, c=p.c, x=p.x,
                                     a_major=p.a_major, b_major=p.b_major,

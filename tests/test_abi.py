@@ -80,6 +80,7 @@ BAD = [
     (dict(ab="e4m3", K=8), ge.GEMM_EPI_ERR_ALIGNMENT),            # 8 B rows
     (dict(a_major="M", M=100), ge.GEMM_EPI_ERR_ALIGNMENT),
     (dict(M=16, N=2**21, K=64), ge.GEMM_EPI_ERR_UNSUPPORTED),    # 31-bit epilogue offsets
+    (dict(splits=-1), ge.GEMM_EPI_ERR_INVALID_ARG),
 ]
 
 

@@ -317,6 +317,49 @@ def test_parity_more_tiles_than_compute_units():
          "err D %.3g Y %.3g" % (ed, ey))
 
 
+# Split K: the K range in slices whose fp32 (int32) partial sums a second
+# kernel adds before the epilogue.  Forced slice counts on small problems
+# (every output type path, both C/D majornesses, M/N-major operands, int8
+# exact), and the library's own choice on a few-tile, long-K shape.
+SPLITK = [
+    (CFG[2].replace(name="splitk3_f16_cxdy", M=300, N=264, K=1000, seed=7300), 3),
+    (CFG[2].replace(name="splitk2_f16_relu_cdm", M=264, N=392, K=520, cd_major="M",
+                    epilogue="relu", seed=7310), 2),
+    (CFG[1].replace(name="splitk5_bf16_mixed_l2", M=200, N=264, K=1288, L=2, c="f32", x="bf16",
+                    y="bf16", x_factor=0.5, seed=7320), 5),
+    (CFG[3].replace(name="splitk4_i8_mmajorA", M=272, N=272, K=2048, L=2, seed=7330), 4),
+    (CFG[4].replace(name="splitk3_e4m3_kn", M=272, N=288, K=1152, b_major="N", seed=7340), 3),
+    (CFG[4].replace(name="splitk2_f8w_f32", M=272, N=288, K=768, d="f32", c="f32", y="f32",
+                    seed=7350), 2),
+]
+
+
+@pytest.mark.parametrize("p,splits", SPLITK, ids=[c[0].name for c in SPLITK])
+def test_parity_split_k(p, splits):
+    _say("case", p.name, p.M, p.N, p.K, p.L, "splits", splits)
+    (ed, ey), plan = parity_full(p, exact=p.ab == "i8", splits=splits)
+    assert plan["splits"] == splits, plan
+    assert plan["workspace_bytes"] == splits * p.L * p.M * p.N * 4
+    _say("  plan", plan["name"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_split_k_chosen_for_few_long_tiles():
+    """512 x 512 x 8192: four output tiles, so the library splits K (16
+    slices of eight K tiles) and fills the GPU; whole-output parity."""
+    p = CFG[2].replace(name="splitk_auto_512", M=512, N=512, K=8192, seed=7360)
+    _say("case", p.name)
+    (ed, ey), plan = parity_full(p)
+    assert plan["splits"] == 16 and plan["grid"] == 64, plan
+    _say("  plan", plan["name"], "splits", plan["splits"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_split_k_not_chosen_when_tiles_fill_the_gpu():
+    import beta_epilogue_amd as ge
+    g = ge.FusedGemm(8192, 8192, 8192, ab="f16", c="f16", x="f16", d="f16", y="f16")
+    assert g.plan["splits"] == 1 and g.plan["workspace_bytes"] == 0
+    g.close()
+
+
 def test_beta_zero_does_not_read_c():
     """beta = 0 skips C: NaN in C cannot reach D (C is given but unread)."""
     p = CFG[2].replace(name="beta0_nan_c", M=256, N=264, K=64, beta=0.0, x_factor=0.0)
