@@ -25,6 +25,7 @@ GEMM_EPI_ERR_ALIGNMENT = 3
 GEMM_EPI_ERR_DEVICE = 4
 GEMM_EPI_ERR_LAUNCH = 5
 GEMM_EPI_ERR_HOST_ALLOC = 6
+GEMM_EPI_STATIC_SCRATCH_BYTES = 64 << 20  # include/gemm_epi.h
 
 DTYPES = {None: 0, "none": 0, "f16": 1, "bf16": 2, "e4m3": 3, "i8": 4,
           "f32": 5, "i32": 6, "e5m2": 7}
@@ -78,6 +79,8 @@ def lib():
         L.gemm_epi_run.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
                                    ctypes.c_float, P]
         L.gemm_epi_run.restype = ctypes.c_int
+        L.gemm_epi_run_static.argtypes = L.gemm_epi_run.argtypes
+        L.gemm_epi_run_static.restype = ctypes.c_int
         L.gemm_epi_destroy.argtypes = [P]
         L.gemm_epi_destroy.restype = ctypes.c_int
         L.gemm_epi_get_plan.argtypes = [P, ctypes.POINTER(gemm_epi_plan)]
@@ -143,6 +146,13 @@ def gemm_epi_run(h: int, A: int, B: int, C: Optional[int], X: Optional[int],
                               stream), "gemm_epi_run")
 
 
+def gemm_epi_run_static(h: int, A: int, B: int, C: Optional[int], X: Optional[int],
+                        D: int, Y: Optional[int], alpha: float, beta: float,
+                        x_factor: float, stream: Optional[int]) -> None:
+    _check(lib().gemm_epi_run_static(h, A, B, C, X, D, Y, alpha, beta, x_factor,
+                                     stream), "gemm_epi_run_static")
+
+
 def gemm_epi_destroy(h: Optional[int]) -> None:
     _check(lib().gemm_epi_destroy(h), "gemm_epi_destroy")
 
@@ -199,14 +209,16 @@ class FusedGemm:
         return t.data_ptr()
 
     def __call__(self, A, B, C=None, X=None, *, D, Y=None, alpha=1.0,
-                 beta=0.0, x_factor=0.0, stream=None):
+                 beta=0.0, x_factor=0.0, stream=None, static_scratch=False):
+        """static_scratch: run through gemm_epi_run_static (no allocation)."""
         import torch
         if stream is None:
             stream = torch.cuda.current_stream()
         sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
-        gemm_epi_run(self.handle, self._ptr(A), self._ptr(B), self._ptr(C),
-                     self._ptr(X), self._ptr(D), self._ptr(Y), float(alpha),
-                     float(beta), float(x_factor), sptr)
+        run = gemm_epi_run_static if static_scratch else gemm_epi_run
+        run(self.handle, self._ptr(A), self._ptr(B), self._ptr(C),
+            self._ptr(X), self._ptr(D), self._ptr(Y), float(alpha),
+            float(beta), float(x_factor), sptr)
         return D
 
     def close(self):

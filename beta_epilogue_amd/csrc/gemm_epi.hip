@@ -119,9 +119,38 @@ struct gemm_epi_handle {
   int64_t ws_bytes;                 // split-K workspace: splits * L*M*N * 4 bytes
   std::atomic<void*> ws{nullptr};   // allocated by the first gemm_epi_run, freed by destroy
   std::mutex ws_mutex;
+  void* ws_static = nullptr;        // device address of the static scratch array
 };
 
+// ---------------------------------------------------------------------------
+// Allocation-free runs (gemm_epi_run_static): the split-K workspace is a
+// file-scope device array, one copy per GPU, instead of memory of the handle.
+// Host code uses the array's device address from hipGetSymbolAddress (taken
+// once per device, with that device current), never the array's name.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchBytes = GEMM_EPI_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
 
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (NULL: not taken yet)
+
+// The device address of `scratch` on the current device `dev`.
+int scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(GEMM_EPI_ERR_DEVICE, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(GEMM_EPI_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GEMM_EPI_OK;
+}
+}  // namespace
 
 // Static validation: everything that needs no device.
 static int validate_desc(const gemm_epi_desc* d) {
@@ -285,6 +314,10 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   if (h->splits == 1) h->kslice = desc->K;
   h->ws_bytes = h->splits > 1 ? (int64_t)h->splits * desc->L * desc->M * desc->N * 4 : 0;
   h->grid = (int)std::min<int64_t>(h->tiles * h->splits, (int64_t)h->cus);  // one workgroup per CU
+  if (scratch_address(dev, &h->ws_static) != GEMM_EPI_OK) {
+    delete h;
+    return GEMM_EPI_ERR_DEVICE;
+  }
   *out = h;
   return GEMM_EPI_OK;
 }
@@ -298,9 +331,9 @@ static bool integral_24(float v) {
 }
 
 // One fused GEMM; split-K plans use the handle's workspace (allocated here on
-// first use).
+// first use) or, with use_static, the static scratch array.
 static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, const void* C, const void* X,
-                    void* D, void* Y, float alpha, float beta, float x_factor, void* stream) {
+                    void* D, void* Y, float alpha, float beta, float x_factor, void* stream, bool use_static) {
   g_last_error[0] = 0;
   if (!hc) return fail(GEMM_EPI_ERR_INVALID_ARG, "handle is NULL");
   gemm_epi_handle* h = const_cast<gemm_epi_handle*>(hc);  // only the lazily allocated workspace changes
@@ -368,15 +401,23 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
   p.kslice = h->kslice;
   p.ws = nullptr;
   if (h->splits > 1) {
-    p.ws = h->ws.load();
-    if (!p.ws) {
-      std::lock_guard<std::mutex> lock(h->ws_mutex);
+    if (use_static) {
+      if (h->ws_bytes > kScratchBytes)
+        return fail(GEMM_EPI_ERR_UNSUPPORTED,
+                    "split-K workspace of %lld bytes exceeds the static scratch of %lld bytes",
+                    (long long)h->ws_bytes, (long long)kScratchBytes);
+      p.ws = h->ws_static;
+    } else {
       p.ws = h->ws.load();
       if (!p.ws) {
-        if (hipMalloc(&p.ws, (size_t)h->ws_bytes) != hipSuccess || !p.ws)
-          return fail(GEMM_EPI_ERR_DEVICE, "hipMalloc of a %lld-byte split-K workspace failed",
-                      (long long)h->ws_bytes);
-        h->ws.store(p.ws);
+        std::lock_guard<std::mutex> lock(h->ws_mutex);
+        p.ws = h->ws.load();
+        if (!p.ws) {
+          if (hipMalloc(&p.ws, (size_t)h->ws_bytes) != hipSuccess || !p.ws)
+            return fail(GEMM_EPI_ERR_DEVICE, "hipMalloc of a %lld-byte split-K workspace failed",
+                        (long long)h->ws_bytes);
+          h->ws.store(p.ws);
+        }
       }
     }
   }
@@ -418,7 +459,13 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
 extern "C" int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void* B, const void* C,
                             const void* X, void* D, void* Y, float alpha, float beta,
                             float x_factor, void* stream) {
-  return run_impl(h, A, B, C, X, D, Y, alpha, beta, x_factor, stream);
+  return run_impl(h, A, B, C, X, D, Y, alpha, beta, x_factor, stream, false);
+}
+
+extern "C" int gemm_epi_run_static(const gemm_epi_handle* h, const void* A, const void* B, const void* C,
+                                   const void* X, void* D, void* Y, float alpha, float beta,
+                                   float x_factor, void* stream) {
+  return run_impl(h, A, B, C, X, D, Y, alpha, beta, x_factor, stream, true);
 }
 
 extern "C" int gemm_epi_destroy(gemm_epi_handle* h) {

@@ -120,6 +120,10 @@ typedef struct gemm_epi_plan {
   char name[64];        /* kernel variant name */
 } gemm_epi_plan;
 
+/* Largest split-K workspace gemm_epi_run_static can use (its static device
+ * array, one per GPU). */
+#define GEMM_EPI_STATIC_SCRATCH_BYTES (64LL << 20)
+
 /*
  * Validate a problem and build an immutable plan for it.
  * Defining passages: the problem is the CuTe DSL example's module docstring
@@ -186,6 +190,21 @@ int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
 int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void* B,
                  const void* C, const void* X, void* D, void* Y, float alpha,
                  float beta, float x_factor, void* stream);
+
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): gemm_epi_run with the
+ * same arguments, checks and results, which never allocates.  A split-K plan
+ * uses a file-scope device array of GEMM_EPI_STATIC_SCRATCH_BYTES (one per
+ * GPU, held until the process ends) as its workspace instead of the
+ * handle's; a plan whose workspace is larger is GEMM_EPI_ERR_UNSUPPORTED.
+ * Every call on one GPU shares that array (the partial sums of a call are
+ * fully written before they are read, so nothing needs clearing), so calls
+ * of split-K plans that overlap in time on one GPU race.
+ */
+int gemm_epi_run_static(const gemm_epi_handle* h, const void* A, const void* B,
+                        const void* C, const void* X, void* D, void* Y,
+                        float alpha, float beta, float x_factor, void* stream);
 
 /* Free a handle and its split-K workspace, if any (NULL is fine).  No run on
  * it may still be being enqueued or executing.  (Tensors are the caller's:

@@ -59,9 +59,10 @@ class GuardedOut:
         return bool(torch.all(lo == s).item()) and bool(torch.all(hi == s).item())
 
 
-def run_gpu(p: synth.Problem, ins, variant=-1, check_inputs=True, splits=0):
+def run_gpu(p: synth.Problem, ins, variant=-1, check_inputs=True, splits=0, static_scratch=False):
     """Run problem p on the GPU through the C ABI.  Returns host D, Y.
-    splits: the K split asked for (0: the library's choice)."""
+    splits: the K split asked for (0: the library's choice);
+    static_scratch: run through gemm_epi_run_static."""
     dev = {k: (v.cuda() if v is not None else None) for k, v in ins.items()}
     keep = {k: v.clone() for k, v in dev.items() if v is not None and k in "CX"}
     g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, a_major=p.a_major,
@@ -72,7 +73,7 @@ def run_gpu(p: synth.Problem, ins, variant=-1, check_inputs=True, splits=0):
     D = GuardedOut(p.d, shape)
     Y = GuardedOut(p.y, shape) if p.y else None
     g(dev["A"], dev["B"], dev["C"], dev["X"], D=D.t, Y=Y.t if Y else None,
-      alpha=p.alpha, beta=p.beta, x_factor=p.x_factor)
+      alpha=p.alpha, beta=p.beta, x_factor=p.x_factor, static_scratch=static_scratch)
     torch.cuda.synchronize()
     assert D.guards_intact(), "D guard band overwritten"
     if Y:
