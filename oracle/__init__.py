@@ -32,10 +32,10 @@ _lib = None
 
 # The oracle's own type numbering (see the enum in gemm_epi_oracle.c).
 TYPES = {"none": 0, "f16": 1, "bf16": 2, "e4m3": 3, "i8": 4, "f32": 5, "i32": 6,
-         "e5m2": 7}
+         "e5m2": 7, "u8": 8}
 # numpy container for the raw stored bits of each type
 STORAGE = {"f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8, "e5m2": np.uint8,
-           "i8": np.int8, "f32": np.float32, "i32": np.int32}
+           "i8": np.int8, "u8": np.uint8, "f32": np.float32, "i32": np.int32}
 
 
 class _Desc(ctypes.Structure):
@@ -131,7 +131,7 @@ def _bits(arr, type_name):
         if t.device.type != "cpu":
             raise ValueError("oracle inputs must be host tensors")
         view = {"f16": torch.int16, "bf16": torch.int16, "e4m3": torch.uint8, "e5m2": torch.uint8,
-                "i8": torch.int8, "f32": torch.float32, "i32": torch.int32}
+                "i8": torch.int8, "u8": torch.uint8, "f32": torch.float32, "i32": torch.int32}
         arr = t.view(view[type_name]).numpy()
     a = np.ascontiguousarray(arr).view(STORAGE[type_name])
     return a

@@ -20,7 +20,7 @@
  *
  *     D[l,m,n] = max(0, alpha * Y[l,m,n] + beta * C[l,m,n]) + x_factor * X[l,m,n]
  *
- * Inputs: fp16, bf16, OCP fp8 E4M3 and E5M2, int8; B may have its own type
+ * Inputs: fp16, bf16, OCP fp8 E4M3 and E5M2, int8, uint8; B may have its own type
  * (the fp8 pairs E4M3 x E5M2 and E5M2 x E4M3).  A is M x K x L, B is N x K x L (so the product is A times B-transposed in
  * row-major algebra), C/X/D/Y are M x N x L.  Every stored element is decoded
  * exactly to double, the contraction runs in double in ascending k, and the
@@ -57,7 +57,8 @@ enum {
   ORC_I8 = 4,
   ORC_F32 = 5,
   ORC_I32 = 6,
-  ORC_E5M2 = 7 /* OCP fp8 E5M2: bias 15, IEEE-like infinities and NaNs */
+  ORC_E5M2 = 7, /* OCP fp8 E5M2: bias 15, IEEE-like infinities and NaNs */
+  ORC_U8 = 8    /* unsigned 8-bit integer, 0..255 */
 };
 
 typedef struct {
@@ -132,6 +133,7 @@ static double load(const void* p, int type, int64_t i) {
     case ORC_E4M3: return dec_e4m3(((const uint8_t*)p)[i]);
     case ORC_E5M2: return dec_e5m2(((const uint8_t*)p)[i]);
     case ORC_I8: return (double)((const int8_t*)p)[i];
+    case ORC_U8: return (double)((const uint8_t*)p)[i];
     case ORC_F32: return dec_f32(((const uint32_t*)p)[i]);
     case ORC_I32: return (double)((const int32_t*)p)[i];
     default: return NAN;
@@ -140,7 +142,7 @@ static double load(const void* p, int type, int64_t i) {
 
 /* Decode n stored elements to double (exposed so tests can pin decoding). */
 int orc_decode(int type, const void* src, int64_t n, double* out) {
-  if (type < ORC_F16 || type > ORC_E5M2 || (n > 0 && (!src || !out))) return 1;
+  if (type < ORC_F16 || type > ORC_U8 || (n > 0 && (!src || !out))) return 1;
   for (int64_t i = 0; i < n; ++i) out[i] = load(src, type, i);
   return 0;
 }
@@ -254,8 +256,10 @@ static int run_threads(const orc_problem* p, int64_t items, int mode,
 static int check_desc(const orc_desc* d, const void* A, const void* B) {
   if (!d || !A || !B) return 1;
   if (d->M < 0 || d->N < 0 || d->K < 0 || d->L < 0) return 1;
-  if ((d->ab_type < ORC_F16 || d->ab_type > ORC_I8) && d->ab_type != ORC_E5M2) return 1;
-  if (d->b_type != ORC_NONE && (d->b_type < ORC_F16 || d->b_type > ORC_I8) && d->b_type != ORC_E5M2)
+  if ((d->ab_type < ORC_F16 || d->ab_type > ORC_I8) && d->ab_type != ORC_E5M2 && d->ab_type != ORC_U8)
+    return 1;
+  if (d->b_type != ORC_NONE && (d->b_type < ORC_F16 || d->b_type > ORC_I8) && d->b_type != ORC_E5M2 &&
+      d->b_type != ORC_U8)
     return 1;
   return 0;
 }

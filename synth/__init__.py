@@ -20,9 +20,9 @@ import torch
 TORCH_DTYPE = {
     "f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn,
     "e5m2": torch.float8_e5m2,
-    "i8": torch.int8, "f32": torch.float32, "i32": torch.int32,
+    "i8": torch.int8, "u8": torch.uint8, "f32": torch.float32, "i32": torch.int32,
 }
-ELEM_BYTES = {"f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1, "i8": 1, "f32": 4, "i32": 4}
+ELEM_BYTES = {"f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1, "i8": 1, "u8": 1, "f32": 4, "i32": 4}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -156,6 +156,9 @@ def draw(dist: str, dtype: str, numel: int, seed: int) -> torch.Tensor:
         return v.to(td)
     if dist == "i8full":  # integers in [-128, 127]
         v = torch.randint(-128, 128, (numel,), generator=g, dtype=torch.int32)
+        return v.to(td)
+    if dist == "u8full":  # integers in [0, 255]
+        v = torch.randint(0, 256, (numel,), generator=g, dtype=torch.int32)
         return v.to(td)
     if dist == "i1000":  # integers in [-1000, 1000]
         v = torch.randint(-1000, 1001, (numel,), generator=g,

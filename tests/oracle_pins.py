@@ -29,7 +29,8 @@ import synth
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "number_formats.txt")
 
 FLOAT_AB = ("f16", "bf16", "e4m3", "e5m2")
-ALL_AB = FLOAT_AB + ("i8",)
+INT_AB = ("i8", "u8")
+ALL_AB = FLOAT_AB + INT_AB
 LAYOUTS = [(a, b, cd) for a in "KM" for b in "KN" for cd in "NM"]
 
 
@@ -101,7 +102,7 @@ def _rand(dist, dtype, shape, seed):
 
 def _dist_for(ab):
     return {"f16": "normal", "bf16": "normal", "e4m3": "e4m3tab", "e5m2": "e5m2tab",
-            "i8": "i8full"}[ab]
+            "i8": "i8full", "u8": "u8full"}[ab]
 
 
 # --------------------------------------------------------------------------
@@ -147,6 +148,8 @@ def pin_decode_vs_library(orc):
         assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan])), typ
     i8 = np.arange(-128, 128, dtype=np.int8)
     assert np.array_equal(orc.decode("i8", i8), i8.astype(np.float64))
+    u8 = np.arange(256, dtype=np.uint8)  # every code is its unsigned value
+    assert np.array_equal(orc.decode("u8", u8), np.arange(256, dtype=np.float64))
     i32 = np.array([0, 1, -1, 2**31 - 1, -2**31, 123456789], dtype=np.int32)
     assert np.array_equal(orc.decode("i32", i32), i32.astype(np.float64))
     f32 = np.array([0.0, -1.5, 3.4028234663852886e38, 1e-45, 0.1], np.float32)
@@ -168,7 +171,7 @@ def pin_bruteforce_exact(orc):
             seed += 10
             Al = _rand(_dist_for(ab), ab, (L, M, K), seed + 1)
             Bl = _rand(_dist_for(ab), ab, (L, N, K), seed + 2)
-            if ab == "i8":
+            if ab in INT_AB:
                 c, x = "i32", "i32"
                 Cl = _rand("i1000", "i32", (L, M, N), seed + 3)
                 Xl = _rand("i1000", "i32", (L, M, N), seed + 4)
@@ -196,7 +199,7 @@ def pin_bruteforce_exact(orc):
                                 for k in range(K))
                         d = (Fraction(alpha) * acc + Fraction(beta) * Fraction(cv[l, m, n])
                              + Fraction(xf) * Fraction(xv[l, m, n]))
-                        if ab == "i8":
+                        if ab in INT_AB:
                             assert Y[l, m, n] == acc and D[l, m, n] == d and S[l, m, n] == s, \
                                 (ab, a, b, cd, l, m, n)
                         else:
@@ -219,7 +222,7 @@ def pin_identity_A(orc):
             eye = torch.eye(M, dtype=torch.float32).expand(L, M, M).to(
                 synth.TORCH_DTYPE[ab])
             Bl = _rand(_dist_for(ab), ab, (L, N, K), 777)
-            if ab == "i8":
+            if ab in INT_AB:
                 c, alpha, beta = "i32", 3.0, -2.0
                 Cl = _rand("i1000", "i32", (L, M, N), 778)
             else:
@@ -244,14 +247,14 @@ def pin_identity_B(orc):
             eye = torch.eye(N, dtype=torch.float32).expand(L, N, N).to(
                 synth.TORCH_DTYPE[ab])
             Al = _rand(_dist_for(ab), ab, (L, M, K), 555)
-            c = "i32" if ab == "i8" else "f16"
-            Cl = _rand("i1000" if ab == "i8" else "normal", c, (L, M, N), 556)
+            c = "i32" if ab in INT_AB else "f16"
+            Cl = _rand("i1000" if ab in INT_AB else "normal", c, (L, M, N), 556)
             D, Y, _ = run(orc, store(Al, "A", "K"), store(eye, "B", b), Cl,
                           M=M, N=N, K=K, L=L, ab=ab, c=c, b=b, alpha=-2.0,
-                          beta=0.25 if ab != "i8" else 4.0)
+                          beta=0.25 if ab not in INT_AB else 4.0)
             av = lib_decode(Al).reshape(L, M, K)
             cv = lib_decode(Cl).reshape(L, M, N)
-            beta = 0.25 if ab != "i8" else 4.0
+            beta = 0.25 if ab not in INT_AB else 4.0
             assert np.array_equal(Y, av), (ab, b)
             assert np.array_equal(D, -2.0 * av + beta * cv), (ab, b)
 
@@ -319,7 +322,7 @@ def pin_skip_and_identity_epilogue(orc):
 
 
 def pin_integer_exact(orc):
-    """int8 and integer-valued fp16: Y equals numpy's int64 matmul."""
+    """int8, uint8 and integer-valued fp16: Y equals numpy's int64 matmul."""
     M, N, K, L = 9, 7, 300, 2
     Al = _rand("i8full", "i8", (L, M, K), 31)
     Bl = _rand("i8full", "i8", (L, N, K), 32)
@@ -335,6 +338,20 @@ def pin_integer_exact(orc):
             assert np.array_equal(Y, want.astype(np.float64)), (a, cd)
             assert np.array_equal(D, (want + Cl.numpy()).astype(np.float64))
             assert np.array_equal(S, np.matmul(np.abs(ai), np.swapaxes(np.abs(bi), 1, 2)))
+    # uint8: every value 0..255, an int64 matmul; all-255 operands give
+    # 255^2 K exactly (the largest products)
+    Au = _rand("u8full", "u8", (L, M, K), 36)
+    Bu = _rand("u8full", "u8", (L, N, K), 37)
+    for b in "KN":
+        D, Y, _ = run(orc, Au, store(Bu, "B", b), store(Cl, "C", "N"), M=M, N=N, K=K, L=L,
+                      ab="u8", c="i32", b=b, alpha=2.0, beta=-1.0)
+        want = np.matmul(Au.numpy().astype(np.int64), np.swapaxes(Bu.numpy().astype(np.int64), 1, 2))
+        assert np.array_equal(Y, want.astype(np.float64)), b
+        assert np.array_equal(D, (2 * want - Cl.numpy()).astype(np.float64)), b
+    full = torch.full((L, M, K), 255, dtype=torch.uint8)
+    fullb = torch.full((L, N, K), 255, dtype=torch.uint8)
+    _, Y, _ = run(orc, full, fullb, M=M, N=N, K=K, L=L, ab="u8")
+    assert np.all(Y == 255 * 255 * K)
     Af = _rand("int2", "f16", (L, M, K), 34)
     Bf = _rand("int2", "f16", (L, N, K), 35)
     _, Y, _ = run(orc, Af, Bf, M=M, N=N, K=K, L=L, ab="f16")

@@ -43,6 +43,8 @@ MUTANTS = [
     ("x_uses_c_type", "load(p->X, d->x_type, o)", "load(p->X, d->c_type, o)"),
     ("y_is_d", "if (yref) *yref = acc;", "if (yref) *yref = out;"),
     ("i8_unsigned", "(double)((const int8_t*)p)[i]", "(double)((const uint8_t*)p)[i]"),
+    ("u8_signed", "case ORC_U8: return (double)((const uint8_t*)p)[i];",
+     "case ORC_U8: return (double)((const int8_t*)p)[i];"),
     ("bf16_as_f16", "case ORC_BF16: return dec_bf16(", "case ORC_BF16: return dec_f16("),
     ("points_swap_mn", "element(j->p, q[0], q[1], q[2]", "element(j->p, q[0], q[2], q[1]"),
     ("e5m2_bias", "ldexp((double)(4 + f), e - 17)", "ldexp((double)(4 + f), e - 16)"),
