@@ -28,7 +28,7 @@ GEMM_EPI_ERR_HOST_ALLOC = 6
 GEMM_EPI_STATIC_SCRATCH_BYTES = 64 << 20  # include/gemm_epi.h
 
 DTYPES = {None: 0, "none": 0, "f16": 1, "bf16": 2, "e4m3": 3, "i8": 4,
-          "f32": 5, "i32": 6, "e5m2": 7}
+          "f32": 5, "i32": 6, "e5m2": 7, "u8": 8}
 MAJOR = {"K": 0, "M": 1, "N": 2}
 
 

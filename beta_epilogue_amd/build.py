@@ -19,11 +19,12 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgemm_epi.so")
 MAIN_SOURCE = os.path.join(CSRC, "gemm_epi.hip")
 SPLITK_SOURCE = os.path.join(CSRC, "gemm_epi_splitk.hip")
+U8_SOURCE = os.path.join(CSRC, "gemm_epi_u8.hip")
 PART_SOURCE = os.path.join(CSRC, "gemm_epi_part.hip")
 GEMM_EPI_PARTS = 16
-SOURCES = [MAIN_SOURCE, PART_SOURCE, SPLITK_SOURCE]
+SOURCES = [MAIN_SOURCE, PART_SOURCE, SPLITK_SOURCE, U8_SOURCE]
 HEADERS = [os.path.join(CSRC, "gemm_epi_kernel.hpp"), os.path.join(CSRC, "gemm_epi_launch.hpp"),
-           os.path.join(CSRC, "gemm_epi_splitk.hpp"),
+           os.path.join(CSRC, "gemm_epi_splitk.hpp"), os.path.join(CSRC, "gemm_epi_u8.hpp"),
            os.path.join(CSRC, "gemm_epi_variants.inc"), os.path.join(ROOT, "include", "gemm_epi.h")]
 # measurement tool used by bench.py --mfma-ceiling (not part of the GEMM path)
 CEILING_LIB = os.path.join(HERE, "libmfma_ceiling.so")
@@ -81,33 +82,45 @@ def _variant_subset(tmp: str, names) -> list:
     return ["-I", d]
 
 
-def build(verbose: bool = False, extra=(), only=None) -> str:
-    """Compile libgemm_epi.so and libmfma_ceiling.so next to this file
-    (always recompiles).  only: variant names to compile (default: every
-    variant; the GEMM_EPI_ONLY environment variable, comma-separated, sets it
-    too)."""
+def build(verbose: bool = False, extra=(), only=None, cache_dir=None) -> str:
+    """Compile libgemm_epi.so and libmfma_ceiling.so next to this file.
+    Recompiles everything, unless cache_dir names a directory of objects from
+    an earlier build with the same options: then an object newer than its
+    source and every header is reused (a development shortcut).  only:
+    variant names to compile (default: every variant; the GEMM_EPI_ONLY
+    environment variable, comma-separated, sets it too)."""
     extra = list(extra)
     if only is None and os.environ.get("GEMM_EPI_ONLY"):
         only = [n for n in os.environ["GEMM_EPI_ONLY"].split(",") if n]
     with tempfile.TemporaryDirectory(prefix="gemm_epi_build_") as tmp:
         if only:
             extra = extra + _variant_subset(tmp, set(only))
-        jobs = [(["hipcc"] + HIPCC_FLAGS + extra + INCLUDES +
-                 ["-c", "-DGEMM_EPI_PART=%d" % k, "-o", os.path.join(tmp, "part%d.o" % k), PART_SOURCE])
-                for k in range(GEMM_EPI_PARTS)]
-        jobs.append(["hipcc"] + HIPCC_FLAGS + extra + INCLUDES +
-                    ["-c", "-o", os.path.join(tmp, "main.o"), MAIN_SOURCE])
-        jobs.append(["hipcc"] + HIPCC_FLAGS + extra + INCLUDES +
-                    ["-c", "-o", os.path.join(tmp, "splitk.o"), SPLITK_SOURCE])
+        objdir = cache_dir or tmp
+        os.makedirs(objdir, exist_ok=True)
+        kernel_deps = [os.path.join(CSRC, f) for f in ("gemm_epi_kernel.hpp", "gemm_epi_launch.hpp",
+                                                        "gemm_epi_variants.inc")]
+
+        def obj(name, source, deps, defines=()):
+            out = os.path.join(objdir, name)
+            newest = max(os.path.getmtime(f) for f in [source] + deps)
+            if cache_dir and not only and os.path.exists(out) and os.path.getmtime(out) > newest:
+                return out, None
+            return out, ["hipcc"] + HIPCC_FLAGS + extra + INCLUDES + list(defines) + ["-c", "-o", out, source]
+
+        units = [obj("part%d.o" % k, PART_SOURCE, kernel_deps, ["-DGEMM_EPI_PART=%d" % k])
+                 for k in range(GEMM_EPI_PARTS)]
+        units += [obj("main.o", MAIN_SOURCE, HEADERS),
+                  obj("splitk.o", SPLITK_SOURCE, [os.path.join(CSRC, "gemm_epi_splitk.hpp")]),
+                  obj("u8.o", U8_SOURCE, [os.path.join(CSRC, "gemm_epi_u8.hpp")])]
+        jobs = [cmd for _, cmd in units if cmd]
         ceil_tmp = CEILING_LIB + ".tmp%d" % os.getpid()
         jobs.append(["hipcc"] + HIPCC_FLAGS + INCLUDES + ["-shared", "-o", ceil_tmp, CEILING_SOURCE])
         with ThreadPoolExecutor(max_workers=_jobs()) as ex:
             for f in [ex.submit(_run, c, verbose) for c in jobs]:
                 f.result()
         lib_tmp = LIB + ".tmp%d" % os.getpid()
-        objs = [os.path.join(tmp, "main.o"), os.path.join(tmp, "splitk.o")] + [os.path.join(tmp, "part%d.o" % k)
-                                                for k in range(GEMM_EPI_PARTS)]
-        _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib_tmp] + objs, verbose)
+        _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib_tmp] + [o for o, _ in units],
+             verbose)
         os.replace(ceil_tmp, CEILING_LIB)
         os.replace(lib_tmp, LIB)
     return LIB

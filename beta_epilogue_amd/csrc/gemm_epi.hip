@@ -23,6 +23,7 @@
 #include "gemm_epi_kernel.hpp"
 #include "gemm_epi_launch.hpp"
 #include "gemm_epi_splitk.hpp"
+#include "gemm_epi_u8.hpp"
 
 namespace {
 
@@ -88,7 +89,8 @@ int elem_bytes(int t) {
     case GEMM_EPI_BF16: return 2;
     case GEMM_EPI_E4M3:
     case GEMM_EPI_E5M2:
-    case GEMM_EPI_I8: return 1;
+    case GEMM_EPI_I8:
+    case GEMM_EPI_U8: return 1;
     case GEMM_EPI_F32:
     case GEMM_EPI_I32: return 4;
     default: return 0;
@@ -178,20 +180,20 @@ static int validate_desc(const gemm_epi_desc* d) {
     return fail(GEMM_EPI_ERR_INVALID_ARG, "epilogue must be LINEAR or RELU (got %d)", d->epilogue);
   const int ab = d->ab_dtype;
   if (ab != GEMM_EPI_F16 && ab != GEMM_EPI_BF16 && ab != GEMM_EPI_E4M3 && ab != GEMM_EPI_E5M2 &&
-      ab != GEMM_EPI_I8)
-    return fail(GEMM_EPI_ERR_INVALID_ARG, "ab_dtype must be F16, BF16, E4M3, E5M2 or I8");
-  const bool int_path = ab == GEMM_EPI_I8;
+      ab != GEMM_EPI_I8 && ab != GEMM_EPI_U8)
+    return fail(GEMM_EPI_ERR_INVALID_ARG, "ab_dtype must be F16, BF16, E4M3, E5M2, I8 or U8");
+  const bool int_path = ab == GEMM_EPI_I8 || ab == GEMM_EPI_U8;
   auto out_ok = [&](int t, bool allow_none) {
     if (t == GEMM_EPI_NONE) return allow_none;
     return int_path ? t == GEMM_EPI_I32 : is_float_out(t);
   };
   for (int t : {d->c_dtype, d->x_dtype, d->d_dtype, d->y_dtype})
-    if (t < GEMM_EPI_NONE || t > GEMM_EPI_E5M2)
+    if (t < GEMM_EPI_NONE || t > GEMM_EPI_U8)
       return fail(GEMM_EPI_ERR_INVALID_ARG, "unknown dtype code %d", t);
   if (!out_ok(d->c_dtype, true) || !out_ok(d->x_dtype, true) || !out_ok(d->d_dtype, false) ||
       !out_ok(d->y_dtype, true))
     return fail(GEMM_EPI_ERR_UNSUPPORTED,
-                int_path ? "int8 A/B need int32 C/X/D/Y (D required)"
+                int_path ? "int8/uint8 A/B need int32 C/X/D/Y (D required)"
                          : "float A/B need F16/BF16/F32 C/X/D/Y (D required)");
   // 16-byte rule on the contiguous extent of every tensor.
   const int es = elem_bytes(ab);
@@ -214,9 +216,11 @@ static int validate_desc(const gemm_epi_desc* d) {
 static int b_type(const gemm_epi_desc* d) { return d->b_dtype == GEMM_EPI_NONE ? d->ab_dtype : d->b_dtype; }
 static bool is_fp8(int t) { return t == GEMM_EPI_E4M3 || t == GEMM_EPI_E5M2; }
 
-// The fp8-MFMA kernel code of a problem: the common type or an fp8 pair.
+// The kernel code of a problem: the common type (uint8: the int8 kernels with
+// the byte flip and the sums in the epilogue) or an fp8 pair.
 static int exact_ab(const gemm_epi_desc* d) {
   const int a = d->ab_dtype, b = b_type(d);
+  if (a == GEMM_EPI_U8 && b == GEMM_EPI_U8) return gemm_epi::T_U8;
   if (a == b) return a;
   if (a == GEMM_EPI_E4M3 && b == GEMM_EPI_E5M2) return gemm_epi::T_E4M3_E5M2;
   if (a == GEMM_EPI_E5M2 && b == GEMM_EPI_E4M3) return gemm_epi::T_E5M2_E4M3;
@@ -303,7 +307,10 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   // K is long: each slice gets at least four K tiles, at most 16 slices.
   const int64_t ktiles = (desc->K + v.bk - 1) / v.bk;
   int64_t splits = 1;
-  if (desc->splits >= 1) {
+  const bool u8 = desc->ab_dtype == GEMM_EPI_U8;
+  if (u8) {
+    splits = 1;  // the sums of uint8 rows and columns are added once, in the epilogue
+  } else if (desc->splits >= 1) {
     splits = std::min<int64_t>(desc->splits, ktiles);
   } else if (h->tiles * 2 <= h->cus && ktiles >= 8) {
     splits = std::min<int64_t>(std::min<int64_t>(h->cus / h->tiles, ktiles / 4), 16);
@@ -313,6 +320,7 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   h->splits = (int)((desc->K + h->kslice - 1) / h->kslice);
   if (h->splits == 1) h->kslice = desc->K;
   h->ws_bytes = h->splits > 1 ? (int64_t)h->splits * desc->L * desc->M * desc->N * 4 : 0;
+  if (u8) h->ws_bytes = desc->L * (desc->M + desc->N) * 4;  // row sums of A, column sums of B
   h->grid = (int)std::min<int64_t>(h->tiles * h->splits, (int64_t)h->cus);  // one workgroup per CU
   if (scratch_address(dev, &h->ws_static) != GEMM_EPI_OK) {
     delete h;
@@ -353,7 +361,8 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
   for (const void* ptr : {A, B, (const void*)D, use_c ? C : nullptr, use_x ? X : nullptr,
                           (const void*)Y})
     if (((uintptr_t)ptr) & 15u) return fail(GEMM_EPI_ERR_ALIGNMENT, "pointer %p is not 16-byte aligned", ptr);
-  const bool int_path = d.ab_dtype == GEMM_EPI_I8;
+  const bool u8 = d.ab_dtype == GEMM_EPI_U8;
+  const bool int_path = d.ab_dtype == GEMM_EPI_I8 || u8;
   if (int_path && !(integral_24(alpha) && integral_24(beta) && integral_24(x_factor)))
     return fail(GEMM_EPI_ERR_UNSUPPORTED,
                 "int32 outputs need integral alpha, beta, x_factor with |value| <= 2^24");
@@ -400,7 +409,10 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
   p.splits = h->splits;
   p.kslice = h->kslice;
   p.ws = nullptr;
-  if (h->splits > 1) {
+  p.rsum_a = p.rsum_b = nullptr;
+  p.xor8 = 0;
+  p.u8_bias = 0;
+  if (h->ws_bytes > 0) {
     if (use_static) {
       if (h->ws_bytes > kScratchBytes)
         return fail(GEMM_EPI_ERR_UNSUPPORTED,
@@ -423,6 +435,26 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
   }
 
   (void)hipGetLastError();  // clear a stale error so the check below is ours
+  if (u8) {
+    // the sums along K of the unsigned A rows and B columns, then the GEMM on
+    // the bytes with their top bit flipped
+    int32_t* ra = (int32_t*)p.ws;
+    int32_t* rb = ra + d.L * d.M;
+    gemm_epi::launch_u8_sums((const uint8_t*)A, d.a_major == GEMM_EPI_MAJOR_K, d.L, d.M, d.K, ra,
+                             (hipStream_t)stream);
+    gemm_epi::launch_u8_sums((const uint8_t*)B, d.b_major == GEMM_EPI_MAJOR_K, d.L, d.N, d.K, rb,
+                             (hipStream_t)stream);
+    p.rsum_a = ra;
+    p.rsum_b = rb;
+    p.xor8 = 0x80808080u;
+    // The K loop runs over whole K tiles: the bytes past K are staged as 0,
+    // which the flip makes -128 in A and in B, so each of those k adds
+    // 128 * 128 too.
+    const int64_t kpad = (d.K + kVariants[h->variant].bk - 1) / kVariants[h->variant].bk *
+                         kVariants[h->variant].bk;
+    p.u8_bias = (int32_t)(uint32_t)((uint64_t)(-(int64_t)16384 * kpad) & 0xffffffffu);
+    p.ws = nullptr;
+  }
   kVariants[h->variant].launch(p, h->grid, (hipStream_t)stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GEMM_EPI_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));

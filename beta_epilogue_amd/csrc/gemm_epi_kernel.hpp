@@ -46,6 +46,9 @@ enum : int { T_E4M3_E5M2 = 8, T_E5M2_E4M3 = 9 };
 // widened to fp16 before the f16 MFMA: used when an fp32 output is asked for,
 // and for the fp8 pairings and layouts no fp8-MFMA kernel is built for.
 enum : int { T_W_F8 = 10 };
+// Kernel A/B code of uint8: the int8 MFMA on bytes with their top bit flipped,
+// and the sums along K in the int32 epilogue.
+enum : int { T_U8 = 14 };
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -89,6 +92,17 @@ struct Params {
   int32_t splits;
   int64_t kslice;
   void* ws;
+  // uint8 A/B on the int8 kernels: every operand byte is flipped by xor8
+  // (0x80808080: u -> u - 128 as a signed byte; 0 for int8), and the int32
+  // epilogue restores sum u_a*u_b = acc + 128*(rsum_a[m] + rsum_b[n]) + u8_bias
+  // with u8_bias = -16384*Kpad (wrapping), Kpad = K rounded up to whole K
+  // tiles (the zero bytes staged past K flip to -128 in both operands);
+  // rsum_a (L x M) and rsum_b (L x N) hold the sums of the unsigned bytes
+  // along K.  NULL for int8.
+  const int32_t* rsum_a;
+  const int32_t* rsum_b;
+  uint32_t xor8;
+  int32_t u8_bias;
 };
 
 // ---------------------------------------------------------------------------
@@ -249,6 +263,8 @@ struct MmaWiden : MmaLayout16 {
   }
 };
 template <> struct Mma<T_W_F8, 16> : MmaWiden {};
+template <> struct Mma<T_U8, 16> : Mma<T_I8, 16> {};
+template <> struct Mma<T_U8, 32> : Mma<T_I8, 32> {};
 
 // Compile-time kernel configuration.
 //   BM x BN     workgroup tile (multiples of 32 per wave)
@@ -268,6 +284,8 @@ struct Cfg {
   // fp8 widened to fp16: an LDS fragment (8 bytes per lane) becomes a register
   // fragment of eight fp16 values
   static constexpr bool WIDEN = AB_ == T_W_F8;
+  static constexpr bool INT = AB_ == T_I8 || AB_ == T_U8;  // int32 accumulators and epilogue
+  static constexpr bool U8 = AB_ == T_U8;
   using RAW = typename std::conditional<WIDEN, v2i, typename MM::frag_t>::type;
   static_assert(DQ >= 0 && DQ <= 4 && (STAGES_ == 2 || DQ == 0), "DQ: quarters, two-stage rings only");
   static constexpr int AB = AB_;
@@ -761,11 +779,34 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
 
   auto write_block = [&](auto blk_c) { epi_stage_block<CF, NMAJ>(acc, region, lane, decltype(blk_c)::value); };
 
+  // uint8 inputs (int32 outputs only): the sums along K of this lane's 4
+  // outputs' rows / columns of the other extent (once) and of each pass's
+  // line; empty resources, reading zero, for int8.
+  constexpr bool U8E = T == T_I32 && CF::U8;  // the uint8 sums are added
+  const bool u8 = U8E && p.rsum_a != nullptr;
+  const int64_t nalong = NMAJ ? p.N : p.M;
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+      u8 ? (void*)((NMAJ ? p.rsum_a : p.rsum_b) + (int64_t)l * nlines + line0) : p.D, (short)0,
+      u8 ? (int)(lines * 4) : 0, 0x00020000);
+  [[maybe_unused]] v4u sum_along = {};
+  [[maybe_unused]] uint32_t rlr[DIST + 1];
+  const uint32_t line_off = (uint32_t)sub * 4u;
+  if constexpr (U8E) {
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        u8 ? (void*)((NMAJ ? p.rsum_b : p.rsum_a) + (int64_t)l * nalong) : p.D, (short)0,
+        u8 ? (int)(nalong * 4) : 0, 0x00020000);
+    sum_along = __builtin_bit_cast(
+        v4u, __builtin_amdgcn_raw_buffer_load_b128(ra, lane_ok ? (int)(along * 4) : (int)0x80000000, 0, 0));
+  }
+  auto line_of = [&](int i) { return (uint32_t)((i / PASSES) * 32 + (i % PASSES) * LINES_PER_PASS); };
+
   v4u cr[DIST + 1], xr[DIST + 1];
   static_for<0, DIST>([&](auto i_c) {
     constexpr int i = decltype(i_c)::value;
     cr[i] = epi_ld<T>(rc, off(i));
     xr[i] = epi_ld<T>(rx, off(i));
+    if constexpr (U8E)
+      rlr[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, (int)(line_off + line_of(i) * 4), 0, 0);
   });
   static_for<0, NP>([&](auto i_c) {
     constexpr int i = decltype(i_c)::value, S = i % (DIST + 1);
@@ -780,10 +821,14 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
       constexpr int SN = (i + DIST) % (DIST + 1);
       cr[SN] = epi_ld<T>(rc, off(i + DIST));
       xr[SN] = epi_ld<T>(rx, off(i + DIST));
+      if constexpr (U8E)
+        rlr[SN] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, (int)(line_off + line_of(i + DIST) * 4), 0, 0);
     }
     const uint32_t o = off(i);
     if constexpr (T == T_I32) {
-      const v4u a = __builtin_bit_cast(v4u, w0);
+      // (uint8: acc + 128 * (row sum + column sum) - 16384 * Kpad, wrapping)
+      v4u a = __builtin_bit_cast(v4u, w0);
+      if constexpr (U8E) a += (sum_along + rlr[S]) * 128u + (uint32_t)p.u8_bias;
       v4u t = a * (unsigned)p.ialpha + cr[S] * (unsigned)p.ibeta;
       if (p.relu) t = relu4(t);
       t += xr[S] * (unsigned)p.ix;
@@ -972,12 +1017,13 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
   OpB opb;
   opa.setup_reader(wm * CF::WM, lane);
   opb.setup_reader(wn * CF::WN, lane);
-  // LDS fragment -> MFMA operand (fp8 widened to fp16 in the widening kernels)
+  // LDS fragments become MFMA operands at their first use in a k step (when
+  // they have long arrived): widened to fp16 in the widening kernels, their
+  // bytes' top bits flipped for uint8 on the int8 kernels (xor8 is 0 for
+  // int8).  Doing it at the read would make each read wait for its data.
   const bool a_e5m2 = p.f8a != 0, b_e5m2 = p.f8b != 0;
-  auto frag = [](typename CF::RAW raw, bool e5m2) -> frag_t {
-    if constexpr (CF::WIDEN) return __builtin_bit_cast(v4i, widen8(raw, e5m2));
-    else return raw;
-  };
+  [[maybe_unused]] const int xor8 = (int)p.xor8;
+  using raw_t = typename CF::RAW;
 
   for (int64_t t = g; t < p.tiles_total; t += G) {
     // ---- tile coordinates: K slice, batch, grouped raster inside a batch ---
@@ -1007,13 +1053,15 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < CF::FN; ++j) acc[i][j] = acc_t{};
 
-    // Fragments of one k step: A blocks then B blocks of this wave.
-    frag_t fa[2][CF::FM], fb[2][CF::FN];
-    auto load_step = [&](frag_t (&ra)[CF::FM], frag_t (&rb)[CF::FN], int st, int s) {
+    // Fragments of one k step as read from LDS: A blocks then B blocks of
+    // this wave (double-buffered); widened operands of the current step.
+    raw_t fa[2][CF::FM], fb[2][CF::FN];
+    [[maybe_unused]] frag_t wa[CF::FM], wb[CF::FN];
+    auto load_step = [&](raw_t (&ra)[CF::FM], raw_t (&rb)[CF::FN], int st, int s) {
 #pragma unroll
-      for (int i = 0; i < CF::FM; ++i) ra[i] = frag(opa.read(lds, st * A_STAGE, i, s), a_e5m2);
+      for (int i = 0; i < CF::FM; ++i) ra[i] = opa.read(lds, st * A_STAGE, i, s);
 #pragma unroll
-      for (int j = 0; j < CF::FN; ++j) rb[j] = frag(opb.read(lds, B_REGION + st * B_STAGE, j, s), b_e5m2);
+      for (int j = 0; j < CF::FN; ++j) rb[j] = opb.read(lds, B_REGION + st * B_STAGE, j, s);
     };
     static_assert(CF::KSTEPS % 2 == 0, "k steps alternate fragment buffers across K tiles");
 
@@ -1028,11 +1076,11 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       constexpr int BUF = decltype(buf_c)::value, R = decltype(r_c)::value;
       const int st = (int)st_x, ks = (int)ks_x;
       if constexpr (R == 0)
-        fa[BUF][0] = frag(opa.read(lds, st * A_STAGE, 0, ks), a_e5m2);
+        fa[BUF][0] = opa.read(lds, st * A_STAGE, 0, ks);
       else if constexpr (R <= CF::FN)
-        fb[BUF][R - 1] = frag(opb.read(lds, B_REGION + st * B_STAGE, R - 1, ks), b_e5m2);
+        fb[BUF][R - 1] = opb.read(lds, B_REGION + st * B_STAGE, R - 1, ks);
       else
-        fa[BUF][R - CF::FN] = frag(opa.read(lds, st * A_STAGE, R - CF::FN, ks), a_e5m2);
+        fa[BUF][R - CF::FN] = opa.read(lds, st * A_STAGE, R - CF::FN, ks);
     };
     // DMA instruction D of K tile k_tile into stage stg.  GUARD: the tile
     // may not exist (k_tile >= KT) or may be cut by the end of K; without
@@ -1057,7 +1105,17 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       static_for<0, MF>([&](auto idx_c) {
         constexpr int IDX = decltype(idx_c)::value;
         constexpr int I = IDX / CF::FN, J = IDX % CF::FN;
-        acc[I][J] = MM::mma(fa[CUR][I], fb[CUR][J], acc[I][J]);
+        if constexpr (CF::WIDEN) {
+          if constexpr (J == 0) wa[I] = __builtin_bit_cast(v4i, widen8(fa[CUR][I], a_e5m2));
+          if constexpr (I == 0) wb[J] = __builtin_bit_cast(v4i, widen8(fb[CUR][J], b_e5m2));
+          acc[I][J] = MM::mma(wa[I], wb[J], acc[I][J]);
+        } else {
+          if constexpr (CF::U8) {
+            if constexpr (J == 0) fa[CUR][I] ^= xor8;
+            if constexpr (I == 0) fb[CUR][J] ^= xor8;
+          }
+          acc[I][J] = MM::mma(fa[CUR][I], fb[CUR][J], acc[I][J]);
+        }
         static_for<0, NREAD>([&](auto r_c) {
           constexpr int R = decltype(r_c)::value;
           if constexpr ((R * MF) / NREAD == IDX) read_r(IntC<CUR ^ 1>{}, r_c, rst, rs);
@@ -1215,9 +1273,11 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       q.ialpha = 1;
       q.ibeta = q.ix = 0;
       q.relu = 0;
-      if constexpr (CF::AB == T_I8) epilogue_typed<CF, NM, T_I32>(q, acc, lds, wave, lane, l, emw, enw);
+      q.rsum_a = q.rsum_b = nullptr;
+      q.u8_bias = 0;
+      if constexpr (CF::INT) epilogue_typed<CF, NM, T_I32>(q, acc, lds, wave, lane, l, emw, enw);
       else epilogue_typed<CF, NM, T_F32>(q, acc, lds, wave, lane, l, emw, enw);
-    } else if constexpr (CF::AB == T_I8) {
+    } else if constexpr (CF::INT) {
       epilogue_typed<CF, NM, T_I32>(p, acc, lds, wave, lane, l, emw, enw);
     } else {
       if (p.epi_kind == T_F16) epilogue_typed<CF, NM, T_F16>(p, acc, lds, wave, lane, l, emw, enw);

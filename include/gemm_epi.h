@@ -8,8 +8,8 @@
  *     D[l] = alpha * (A[l] . B[l]^T) + beta * C[l] + x_factor * X[l]
  *
  * A is M x K x L, B is N x K x L, C, X, D and Y are M x N x L.  Inputs are
- * fp16, bf16, fp8 (OCP e4m3fn or e5m2) or int8; accumulation is fp32, or int32 for
- * int8.  The epilogue runs in fp32 (int32 for int8) on the unrounded
+ * fp16, bf16, fp8 (OCP e4m3fn or e5m2), int8 or uint8; accumulation is fp32,
+ * or int32 for int8 and uint8.  The epilogue runs in fp32 (int32 for int8) on the unrounded
  * accumulator and rounds to nearest-even into the output types.  By default
  * no ReLU is applied (the docstring's formula has none).  The desc field
  * `epilogue` selects instead the form the example's epilogue function builds
@@ -75,7 +75,8 @@ enum {
   GEMM_EPI_I8 = 4,   /* int8 (A/B only) */
   GEMM_EPI_F32 = 5,  /* binary32 (C/X/D/Y only) */
   GEMM_EPI_I32 = 6,  /* int32 (C/X/D/Y only, with int8 inputs) */
-  GEMM_EPI_E5M2 = 7  /* OCP fp8 e5m2 (A/B only) */
+  GEMM_EPI_E5M2 = 7, /* OCP fp8 e5m2 (A/B only) */
+  GEMM_EPI_U8 = 8    /* uint8 (A/B only) */
 };
 
 /* Majorness: the contiguous mode of a tensor (see the table above). */
@@ -89,10 +90,10 @@ typedef struct gemm_epi_desc {
   int32_t a_major;     /* GEMM_EPI_MAJOR_K or _M */
   int32_t b_major;     /* GEMM_EPI_MAJOR_K or _N */
   int32_t cd_major;    /* GEMM_EPI_MAJOR_N or _M: C, X, D and Y alike */
-  int32_t ab_dtype;    /* F16, BF16, E4M3, E5M2 or I8 */
-  int32_t c_dtype;     /* NONE, or F16/BF16/F32 (float A/B), I32 (int8 A/B) */
+  int32_t ab_dtype;    /* F16, BF16, E4M3, E5M2, I8 or U8 */
+  int32_t c_dtype;     /* NONE, or F16/BF16/F32 (float A/B), I32 (int8/uint8 A/B) */
   int32_t x_dtype;     /* as c_dtype */
-  int32_t d_dtype;     /* F16/BF16/F32 (float A/B) or I32 (int8 A/B) */
+  int32_t d_dtype;     /* F16/BF16/F32 (float A/B) or I32 (int8/uint8 A/B) */
   int32_t y_dtype;     /* NONE, or as d_dtype */
   int32_t epilogue;    /* GEMM_EPI_LINEAR (0) or GEMM_EPI_RELU */
   int32_t b_dtype;     /* NONE (0): B has ab_dtype.  Else the other fp8 format
@@ -172,6 +173,12 @@ int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
  * alpha, beta, x_factor : fp32 scalars.  With int32 outputs they must be
  *            integers of magnitude <= 2^24 (the epilogue is then exact int32
  *            arithmetic), else GEMM_EPI_ERR_UNSUPPORTED.
+ * uint8 A/B run on the int8 MFMA with every byte's top bit flipped (u - 128)
+ * and three small kernels before it that sum each A row and B column of the
+ * unsigned bytes along K into the handle's workspace (L*(M+N)*4 bytes,
+ * allocated like a split-K workspace; uint8 plans never split K); the int32
+ * epilogue adds 128*(row sum + column sum) - 16384*K, wrapping, which makes
+ * the result exact whenever it fits in int32.
  * Split-K plans (gemm_epi_plan.splits > 1) run two kernels on `stream`: the
  * K slices write fp32 (int32) partial sums to a workspace of
  * plan.workspace_bytes, then a second kernel adds them (in slice order) and

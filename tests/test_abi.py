@@ -81,6 +81,9 @@ BAD = [
     (dict(a_major="M", M=100), ge.GEMM_EPI_ERR_ALIGNMENT),
     (dict(M=16, N=2**21, K=64), ge.GEMM_EPI_ERR_UNSUPPORTED),    # 31-bit epilogue offsets
     (dict(splits=-1), ge.GEMM_EPI_ERR_INVALID_ARG),
+    (dict(ab="u8"), ge.GEMM_EPI_ERR_UNSUPPORTED),                 # uint8 needs int32 outs
+    (dict(ab="u8", b="i8", c="i32", x="i32", d="i32", y="i32"), ge.GEMM_EPI_ERR_INVALID_ARG),
+    (dict(ab="u8", c="i32", x="i32", d="i32", y="i32", a_major="M", M=8), ge.GEMM_EPI_ERR_ALIGNMENT),
 ]
 
 
@@ -161,7 +164,7 @@ def test_every_majorness_has_a_kernel():
         pytest.skip("a GPU is present")
     for ab, b, outs in (("f16", None, "f16"), ("bf16", None, "f32"), ("e4m3", None, "f16"),
                         ("e5m2", None, "f16"), ("e4m3", "e5m2", "f16"), ("e5m2", "e4m3", "f32"),
-                        ("i8", None, "i32")):
+                        ("i8", None, "i32"), ("u8", None, "i32")):
         for a_major in "KM":
             for b_major in "KN":
                 for cd in "NM":

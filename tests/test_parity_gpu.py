@@ -360,6 +360,39 @@ def test_split_k_not_chosen_when_tiles_fill_the_gpu():
     g.close()
 
 
+# uint8 A/B (int32 accumulation): the int8 MFMA on the bytes with their top
+# bit flipped, plus the sums of the unsigned rows and columns along K in the
+# epilogue.  Bit-exact against the oracle in every layout.
+U8 = [
+    CFG[3].replace(name="u8_kk_n", M=272, N=264, K=400, L=2, a_major="K", ab="u8",
+                   dist_ab="u8full", seed=7500),
+    CFG[3].replace(name="u8_mk_n_xy", M=272, N=264, K=4096, L=1, ab="u8", dist_ab="u8full",
+                   x="i32", y="i32", alpha=-3.0, beta=2.0, x_factor=5.0, dist_x="i1000",
+                   seed=7510),
+    CFG[3].replace(name="u8_kn_m", M=260, N=272, K=144, L=2, a_major="K", b_major="N",
+                   cd_major="M", ab="u8", dist_ab="u8full", seed=7520),
+    CFG[3].replace(name="u8_mn_m_relu", M=288, N=272, K=48, L=3, b_major="N", cd_major="M",
+                   ab="u8", dist_ab="u8full", beta=-1.0, epilogue="relu", seed=7530),
+    CFG[3].replace(name="u8_tiny", M=16, N=16, K=16, L=2, ab="u8", dist_ab="u8full", seed=7540),
+]
+
+
+@pytest.mark.parametrize("p", U8, ids=[e.name for e in U8])
+def test_parity_u8(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.a_major, p.b_major, p.cd_major)
+    (ed, ey), plan = parity_full(p)
+    assert plan["splits"] == 1 and plan["workspace_bytes"] == p.L * (p.M + p.N) * 4
+    _say("  plan", plan["name"])
+
+
+def test_parity_u8_full_size_sampled():
+    """The batched int8 workload's shape (4096^3 x 4, A M-major) in uint8."""
+    p = CFG[3].replace(name="u8_4096x4_mmajorA", ab="u8", dist_ab="u8full", seed=7550)
+    _say("case", p.name)
+    (ed, ey), plan, npts = parity_sampled(p)
+    _say("  plan", plan["name"], "points", npts)
+
+
 def test_beta_zero_does_not_read_c():
     """beta = 0 skips C: NaN in C cannot reach D (C is given but unread)."""
     p = CFG[2].replace(name="beta0_nan_c", M=256, N=264, K=64, beta=0.0, x_factor=0.0)
@@ -386,6 +419,7 @@ def test_every_variant_runs():
         "e5e4": CFG[4].replace(M=272, N=288, K=144, L=2, ab="e5m2", dist_ab="e5m2tab",
                                b_ab="e4m3", dist_b="e4m3tab"),
         "i8": CFG[3].replace(M=272, N=288, K=144, L=2),
+        "u8": CFG[3].replace(M=272, N=288, K=144, L=2, ab="u8", dist_ab="u8full"),
         # widening kernels: an fp32 output, an e5m2 x e4m3 pairing
         "f8w": CFG[4].replace(M=272, N=288, K=144, L=2, ab="e5m2", dist_ab="e5m2tab",
                               b_ab="e4m3", dist_b="e4m3tab", d="f32", x="f32", x_factor=0.5),

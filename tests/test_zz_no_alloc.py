@@ -20,6 +20,9 @@ def _say(*a):
 CASES = [
     (synth.CONFIGS[2].replace(name="static_f16_cxdy", M=512, N=520, K=4096, L=2, seed=7400), 8),
     (synth.CONFIGS[3].replace(name="static_i8_small", M=256, N=272, K=1024, L=1, seed=7410), 3),
+    # uint8: the row and column sums in the static array (no split)
+    (synth.CONFIGS[3].replace(name="static_u8_smaller", M=128, N=144, K=512, L=1, ab="u8",
+                              dist_ab="u8full", seed=7420), 0),
 ]
 
 
@@ -30,7 +33,7 @@ def test_run_static_matches_run_twice_second_smaller():
         ins = synth.make_inputs(p)
         D1, Y1, plan = run_gpu(p, ins, splits=splits)
         D2, Y2, plan2 = run_gpu(p, ins, splits=splits, static_scratch=True)
-        assert plan["splits"] == splits and plan2["splits"] == splits
+        assert plan["splits"] == max(splits, 1) and plan2["splits"] == max(splits, 1)
         assert plan["workspace_bytes"] <= ge.GEMM_EPI_STATIC_SCRATCH_BYTES
         assert torch.equal(D1.view(torch.uint8), D2.view(torch.uint8)), "static run differs"
         if Y1 is not None:
