@@ -412,6 +412,7 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
   p.rsum_a = p.rsum_b = nullptr;
   p.xor8 = 0;
   p.u8_bias = 0;
+  p.int_unit = int_path && p.ialpha == 1 && (p.ibeta == 1 || !use_c) && (p.ix == 1 || !use_x) ? 1 : 0;
   if (h->ws_bytes > 0) {
     if (use_static) {
       if (h->ws_bytes > kScratchBytes)

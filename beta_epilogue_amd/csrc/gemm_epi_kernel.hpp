@@ -103,6 +103,11 @@ struct Params {
   const int32_t* rsum_b;
   uint32_t xor8;
   int32_t u8_bias;
+  // int32 outputs whose scalars need no multiply: ialpha == 1 and ibeta (ix)
+  // is 1 or its term skipped (an empty resource reads zero), so
+  // D = acc + C + X with adds only (v_mul_lo_u32 is a quarter-rate
+  // instruction, three per output otherwise).
+  int32_t int_unit;
 };
 
 // ---------------------------------------------------------------------------
@@ -732,7 +737,7 @@ __device__ __forceinline__ void epi_st(__amdgpu_buffer_rsrc_t r, uint32_t off, v
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, EPI_NT);
 }
 
-template <class CF, bool NMAJ, int T, class ACC>
+template <class CF, bool NMAJ, int T, bool UNIT = false, class ACC>
 __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)[CF::FM][CF::FN], char* lds,
                                                int wave, int lane, int l, int mw, int nw) {
   constexpr int LINE = CF::epi_line(NMAJ), PITCH = CF::epi_pitch(NMAJ);
@@ -829,9 +834,10 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
       // (uint8: acc + 128 * (row sum + column sum) - 16384 * Kpad, wrapping)
       v4u a = __builtin_bit_cast(v4u, w0);
       if constexpr (U8E) a += (sum_along + rlr[S]) * 128u + (uint32_t)p.u8_bias;
-      v4u t = a * (unsigned)p.ialpha + cr[S] * (unsigned)p.ibeta;
+      // UNIT: the scalars are 1 or their terms read zero (int_unit)
+      v4u t = UNIT ? a + cr[S] : a * (unsigned)p.ialpha + cr[S] * (unsigned)p.ibeta;
       if (p.relu) t = relu4(t);
-      t += xr[S] * (unsigned)p.ix;
+      t += UNIT ? xr[S] : xr[S] * (unsigned)p.ix;
       epi_st<T>(rd, o, t);
       epi_st<T>(ry, o, a);
     } else {
@@ -1275,10 +1281,11 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       q.relu = 0;
       q.rsum_a = q.rsum_b = nullptr;
       q.u8_bias = 0;
-      if constexpr (CF::INT) epilogue_typed<CF, NM, T_I32>(q, acc, lds, wave, lane, l, emw, enw);
+      if constexpr (CF::INT) epilogue_typed<CF, NM, T_I32, true>(q, acc, lds, wave, lane, l, emw, enw);
       else epilogue_typed<CF, NM, T_F32>(q, acc, lds, wave, lane, l, emw, enw);
     } else if constexpr (CF::INT) {
-      epilogue_typed<CF, NM, T_I32>(p, acc, lds, wave, lane, l, emw, enw);
+      if (p.int_unit) epilogue_typed<CF, NM, T_I32, true>(p, acc, lds, wave, lane, l, emw, enw);
+      else epilogue_typed<CF, NM, T_I32, false>(p, acc, lds, wave, lane, l, emw, enw);
     } else {
       if (p.epi_kind == T_F16) epilogue_typed<CF, NM, T_F16>(p, acc, lds, wave, lane, l, emw, enw);
       else if (p.epi_kind == T_F32) epilogue_typed<CF, NM, T_F32>(p, acc, lds, wave, lane, l, emw, enw);

@@ -98,6 +98,16 @@ EDGE = [
     CFG[3].replace(name="kn_i8_xy", M=260, N=272, K=272, L=1, a_major="K", b_major="N",
                    x="i32", y="i32", alpha=-3.0, beta=2.0, x_factor=5.0, dist_x="i1000",
                    seed=7160),
+    # int32 outputs with unit scalars take the adds-only epilogue: C skipped
+    # (beta 0) with X added, and both added; a scalar of 2 takes the
+    # multiplying one
+    CFG[3].replace(name="kk_i8_unit_x_no_c", M=264, N=272, K=208, L=2, a_major="K",
+                   x="i32", y="i32", alpha=1.0, beta=0.0, x_factor=1.0, dist_x="i1000",
+                   seed=7170),
+    CFG[3].replace(name="mk_i8_unit_c_x_cdm", M=272, N=264, K=144, L=1, cd_major="M",
+                   x="i32", alpha=1.0, beta=1.0, x_factor=1.0, dist_x="i1000", seed=7180),
+    CFG[3].replace(name="mk_i8_x2_not_unit", M=272, N=264, K=144, L=1,
+                   x="i32", alpha=1.0, beta=1.0, x_factor=2.0, dist_x="i1000", seed=7190),
 ]
 
 
