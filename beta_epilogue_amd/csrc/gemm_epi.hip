@@ -108,6 +108,22 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 }  // namespace
 
+// The uint8 workspace: sums of A rows (L*M int32) and of B columns (L*N),
+// then the flipped copies of A (L*M*K bytes) and B (L*N*K), each part at a
+// 256-byte boundary.  Returns its size; with base set, the parts' addresses.
+static int64_t u8_layout(const gemm_epi_desc* d, char* base, int32_t** sums, uint8_t** flipped) {
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  const int64_t sums_bytes = up(d->L * (d->M + d->N) * 4);
+  const int64_t a_bytes = up(d->L * d->M * d->K);
+  const int64_t b_bytes = up(d->L * d->N * d->K);
+  if (base) {
+    *sums = (int32_t*)base;
+    flipped[0] = (uint8_t*)base + sums_bytes;
+    flipped[1] = (uint8_t*)base + sums_bytes + a_bytes;
+  }
+  return sums_bytes + a_bytes + b_bytes;
+}
+
 struct gemm_epi_handle {
   gemm_epi_desc desc;
   int variant;
@@ -118,7 +134,7 @@ struct gemm_epi_handle {
   int group_m;
   int splits;                       // K slices (1: no split)
   int64_t kslice;                   // K elements per slice
-  int64_t ws_bytes;                 // split-K workspace: splits * L*M*N * 4 bytes
+  int64_t ws_bytes;                 // workspace: split-K partial sums, or the uint8 sums and copies
   std::atomic<void*> ws{nullptr};   // allocated by the first gemm_epi_run, freed by destroy
   std::mutex ws_mutex;
   void* ws_static = nullptr;        // device address of the static scratch array
@@ -216,8 +232,9 @@ static int validate_desc(const gemm_epi_desc* d) {
 static int b_type(const gemm_epi_desc* d) { return d->b_dtype == GEMM_EPI_NONE ? d->ab_dtype : d->b_dtype; }
 static bool is_fp8(int t) { return t == GEMM_EPI_E4M3 || t == GEMM_EPI_E5M2; }
 
-// The kernel code of a problem: the common type (uint8: the int8 kernels with
-// the byte flip and the sums in the epilogue) or an fp8 pair.
+// The kernel code of a problem: the common type (uint8: the int8 kernels on
+// flipped copies, accumulators started at the sums' correction) or an fp8
+// pair.
 static int exact_ab(const gemm_epi_desc* d) {
   const int a = d->ab_dtype, b = b_type(d);
   if (a == GEMM_EPI_U8 && b == GEMM_EPI_U8) return gemm_epi::T_U8;
@@ -282,6 +299,9 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   if ((int64_t)(v.bm > v.bn ? v.bm : v.bn) * ld * 4 >= (int64_t(1) << 31))
     return fail(GEMM_EPI_ERR_UNSUPPORTED, "leading extent %lld of C/X/D/Y too long for 31-bit offsets",
                 (long long)ld);
+  // uint8: the row and column sums of a batch are addressed with 31-bit offsets.
+  if (desc->ab_dtype == GEMM_EPI_U8 && (desc->M >= (int64_t(1) << 29) || desc->N >= (int64_t(1) << 29)))
+    return fail(GEMM_EPI_ERR_UNSUPPORTED, "uint8 needs M and N below 2^29");
 
   // Device query (the only part that needs a GPU).
   int dev = 0;
@@ -309,7 +329,7 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   int64_t splits = 1;
   const bool u8 = desc->ab_dtype == GEMM_EPI_U8;
   if (u8) {
-    splits = 1;  // the sums of uint8 rows and columns are added once, in the epilogue
+    splits = 1;  // the uint8 correction starts the accumulator of the whole K range
   } else if (desc->splits >= 1) {
     splits = std::min<int64_t>(desc->splits, ktiles);
   } else if (h->tiles * 2 <= h->cus && ktiles >= 8) {
@@ -320,7 +340,9 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   h->splits = (int)((desc->K + h->kslice - 1) / h->kslice);
   if (h->splits == 1) h->kslice = desc->K;
   h->ws_bytes = h->splits > 1 ? (int64_t)h->splits * desc->L * desc->M * desc->N * 4 : 0;
-  if (u8) h->ws_bytes = desc->L * (desc->M + desc->N) * 4;  // row sums of A, column sums of B
+  // uint8: row sums of A and column sums of B, then the flipped copies of A
+  // and B (each at a 256-byte boundary)
+  if (u8) h->ws_bytes = u8_layout(desc, nullptr, nullptr, nullptr);
   h->grid = (int)std::min<int64_t>(h->tiles * h->splits, (int64_t)h->cus);  // one workgroup per CU
   if (scratch_address(dev, &h->ws_static) != GEMM_EPI_OK) {
     delete h;
@@ -410,14 +432,13 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
   p.kslice = h->kslice;
   p.ws = nullptr;
   p.rsum_a = p.rsum_b = nullptr;
-  p.xor8 = 0;
   p.u8_bias = 0;
   p.int_unit = int_path && p.ialpha == 1 && (p.ibeta == 1 || !use_c) && (p.ix == 1 || !use_x) ? 1 : 0;
   if (h->ws_bytes > 0) {
     if (use_static) {
       if (h->ws_bytes > kScratchBytes)
         return fail(GEMM_EPI_ERR_UNSUPPORTED,
-                    "split-K workspace of %lld bytes exceeds the static scratch of %lld bytes",
+                    "workspace of %lld bytes exceeds the static scratch of %lld bytes",
                     (long long)h->ws_bytes, (long long)kScratchBytes);
       p.ws = h->ws_static;
     } else {
@@ -427,7 +448,7 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
         p.ws = h->ws.load();
         if (!p.ws) {
           if (hipMalloc(&p.ws, (size_t)h->ws_bytes) != hipSuccess || !p.ws)
-            return fail(GEMM_EPI_ERR_DEVICE, "hipMalloc of a %lld-byte split-K workspace failed",
+            return fail(GEMM_EPI_ERR_DEVICE, "hipMalloc of a %lld-byte workspace failed",
                         (long long)h->ws_bytes);
           h->ws.store(p.ws);
         }
@@ -437,23 +458,23 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
 
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   if (u8) {
-    // the sums along K of the unsigned A rows and B columns, then the GEMM on
-    // the bytes with their top bit flipped
-    int32_t* ra = (int32_t*)p.ws;
-    int32_t* rb = ra + d.L * d.M;
-    gemm_epi::launch_u8_sums((const uint8_t*)A, d.a_major == GEMM_EPI_MAJOR_K, d.L, d.M, d.K, ra,
+    // one pass over each operand: its flipped copy (u - 128 as a signed
+    // byte) and its sums along K; the GEMM reads the copies, and every
+    // accumulator starts at 128 * (row sum + column sum) - 16384 * K
+    int32_t* sums = nullptr;
+    uint8_t* flipped[2] = {nullptr, nullptr};
+    u8_layout(&d, (char*)p.ws, &sums, flipped);
+    int32_t* ra = sums;
+    int32_t* rb = sums + d.L * d.M;
+    gemm_epi::launch_u8_prep((const uint8_t*)A, d.a_major == GEMM_EPI_MAJOR_K, d.L, d.M, d.K, flipped[0], ra,
                              (hipStream_t)stream);
-    gemm_epi::launch_u8_sums((const uint8_t*)B, d.b_major == GEMM_EPI_MAJOR_K, d.L, d.N, d.K, rb,
+    gemm_epi::launch_u8_prep((const uint8_t*)B, d.b_major == GEMM_EPI_MAJOR_K, d.L, d.N, d.K, flipped[1], rb,
                              (hipStream_t)stream);
+    p.A = flipped[0];
+    p.B = flipped[1];
     p.rsum_a = ra;
     p.rsum_b = rb;
-    p.xor8 = 0x80808080u;
-    // The K loop runs over whole K tiles: the bytes past K are staged as 0,
-    // which the flip makes -128 in A and in B, so each of those k adds
-    // 128 * 128 too.
-    const int64_t kpad = (d.K + kVariants[h->variant].bk - 1) / kVariants[h->variant].bk *
-                         kVariants[h->variant].bk;
-    p.u8_bias = (int32_t)(uint32_t)((uint64_t)(-(int64_t)16384 * kpad) & 0xffffffffu);
+    p.u8_bias = (int32_t)(uint32_t)((uint64_t)(-(int64_t)16384 * d.K) & 0xffffffffu);
     p.ws = nullptr;
   }
   kVariants[h->variant].launch(p, h->grid, (hipStream_t)stream);

@@ -46,8 +46,8 @@ enum : int { T_E4M3_E5M2 = 8, T_E5M2_E4M3 = 9 };
 // widened to fp16 before the f16 MFMA: used when an fp32 output is asked for,
 // and for the fp8 pairings and layouts no fp8-MFMA kernel is built for.
 enum : int { T_W_F8 = 10 };
-// Kernel A/B code of uint8: the int8 MFMA on bytes with their top bit flipped,
-// and the sums along K in the int32 epilogue.
+// Kernel A/B code of uint8: the int8 MFMA on copies of A and B with every
+// byte's top bit flipped, the accumulators started at the sums' correction.
 enum : int { T_U8 = 14 };
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -92,16 +92,15 @@ struct Params {
   int32_t splits;
   int64_t kslice;
   void* ws;
-  // uint8 A/B on the int8 kernels: every operand byte is flipped by xor8
-  // (0x80808080: u -> u - 128 as a signed byte; 0 for int8), and the int32
-  // epilogue restores sum u_a*u_b = acc + 128*(rsum_a[m] + rsum_b[n]) + u8_bias
-  // with u8_bias = -16384*Kpad (wrapping), Kpad = K rounded up to whole K
-  // tiles (the zero bytes staged past K flip to -128 in both operands);
-  // rsum_a (L x M) and rsum_b (L x N) hold the sums of the unsigned bytes
-  // along K.  NULL for int8.
+  // uint8 A/B on the int8 kernels: A and B here are copies of the unsigned
+  // operands with every byte's top bit flipped (u - 128 as a signed byte),
+  // so the MFMA sums (u_a - 128)(u_b - 128); each tile's accumulator starts
+  // at 128*(rsum_a[m] + rsum_b[n]) + u8_bias with u8_bias = -16384*K
+  // (wrapping), which makes it sum u_a*u_b (k past K reads zero and adds
+  // nothing).  rsum_a (L x M) and rsum_b (L x N) hold the sums along K of the
+  // unsigned bytes.  NULL for int8.
   const int32_t* rsum_a;
   const int32_t* rsum_b;
-  uint32_t xor8;
   int32_t u8_bias;
   // int32 outputs whose scalars need no multiply: ialpha == 1 and ibeta (ix)
   // is 1 or its term skipped (an empty resource reads zero), so
@@ -784,34 +783,11 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
 
   auto write_block = [&](auto blk_c) { epi_stage_block<CF, NMAJ>(acc, region, lane, decltype(blk_c)::value); };
 
-  // uint8 inputs (int32 outputs only): the sums along K of this lane's 4
-  // outputs' rows / columns of the other extent (once) and of each pass's
-  // line; empty resources, reading zero, for int8.
-  constexpr bool U8E = T == T_I32 && CF::U8;  // the uint8 sums are added
-  const bool u8 = U8E && p.rsum_a != nullptr;
-  const int64_t nalong = NMAJ ? p.N : p.M;
-  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-      u8 ? (void*)((NMAJ ? p.rsum_a : p.rsum_b) + (int64_t)l * nlines + line0) : p.D, (short)0,
-      u8 ? (int)(lines * 4) : 0, 0x00020000);
-  [[maybe_unused]] v4u sum_along = {};
-  [[maybe_unused]] uint32_t rlr[DIST + 1];
-  const uint32_t line_off = (uint32_t)sub * 4u;
-  if constexpr (U8E) {
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        u8 ? (void*)((NMAJ ? p.rsum_b : p.rsum_a) + (int64_t)l * nalong) : p.D, (short)0,
-        u8 ? (int)(nalong * 4) : 0, 0x00020000);
-    sum_along = __builtin_bit_cast(
-        v4u, __builtin_amdgcn_raw_buffer_load_b128(ra, lane_ok ? (int)(along * 4) : (int)0x80000000, 0, 0));
-  }
-  auto line_of = [&](int i) { return (uint32_t)((i / PASSES) * 32 + (i % PASSES) * LINES_PER_PASS); };
-
   v4u cr[DIST + 1], xr[DIST + 1];
   static_for<0, DIST>([&](auto i_c) {
     constexpr int i = decltype(i_c)::value;
     cr[i] = epi_ld<T>(rc, off(i));
     xr[i] = epi_ld<T>(rx, off(i));
-    if constexpr (U8E)
-      rlr[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, (int)(line_off + line_of(i) * 4), 0, 0);
   });
   static_for<0, NP>([&](auto i_c) {
     constexpr int i = decltype(i_c)::value, S = i % (DIST + 1);
@@ -826,14 +802,10 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
       constexpr int SN = (i + DIST) % (DIST + 1);
       cr[SN] = epi_ld<T>(rc, off(i + DIST));
       xr[SN] = epi_ld<T>(rx, off(i + DIST));
-      if constexpr (U8E)
-        rlr[SN] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, (int)(line_off + line_of(i + DIST) * 4), 0, 0);
     }
     const uint32_t o = off(i);
     if constexpr (T == T_I32) {
-      // (uint8: acc + 128 * (row sum + column sum) - 16384 * Kpad, wrapping)
-      v4u a = __builtin_bit_cast(v4u, w0);
-      if constexpr (U8E) a += (sum_along + rlr[S]) * 128u + (uint32_t)p.u8_bias;
+      const v4u a = __builtin_bit_cast(v4u, w0);
       // UNIT: the scalars are 1 or their terms read zero (int_unit)
       v4u t = UNIT ? a + cr[S] : a * (unsigned)p.ialpha + cr[S] * (unsigned)p.ibeta;
       if (p.relu) t = relu4(t);
@@ -985,6 +957,48 @@ __device__ __forceinline__ void epilogue_mixed(const Params& p, const ACC (&acc)
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// uint8: the accumulator of each output of this wave's tile starts at
+// 128*(rsum_a[m] + rsum_b[n]) + u8_bias (see Params).  The sums are loaded
+// before the prologue's DMA (their wait is the prologue's) and applied after
+// it, before any fragment is live.  Rows and columns past the matrix read
+// zero through the buffers' range check; their outputs are never stored.
+template <class CF>
+struct U8Init {
+  using MM = typename CF::MM;
+  static constexpr int BLK = CF::BLK, ACCN = MM::ACCN, G = ACCN / 4;
+  uint32_t cb[CF::FN];
+  v4u rr[CF::FM][G];  // four consecutive rows per accumulator register group
+
+  __device__ __forceinline__ void load(const Params& p, int l, int mw, int nw, int lane) {
+    // resources based at this wave's first row / column; per-lane offsets
+    // are one register each plus compile-time immediates
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.rsum_a + (int64_t)l * p.M + mw), (short)0, (int)((p.M - mw) * 4), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.rsum_b + (int64_t)l * p.N + nw), (short)0, (int)((p.N - nw) * 4), 0x00020000);
+    const int la = MM::acc_row(lane, 0) * 4, lb = (lane % BLK) * 4;
+#pragma unroll
+    for (int j = 0; j < CF::FN; ++j) cb[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rb, lb + j * BLK * 4, 0, 0);
+#pragma unroll
+    for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        rr[i][g] = __builtin_bit_cast(
+            v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                     ra, la + (i * BLK + MM::acc_row(0, 4 * g) - MM::acc_row(0, 0)) * 4, 0, 0));
+  }
+  template <class ACC>
+  __device__ __forceinline__ void apply(ACC (&acc)[CF::FM][CF::FN], int32_t bias) const {
+#pragma unroll
+    for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < CF::FN; ++j)
+#pragma unroll
+        for (int v = 0; v < ACCN; ++v)
+          acc[i][j][v] = (int)((rr[i][v / 4][v % 4] + cb[j]) * 128u + (uint32_t)bias);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
@@ -1024,11 +1038,9 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
   opa.setup_reader(wm * CF::WM, lane);
   opb.setup_reader(wn * CF::WN, lane);
   // LDS fragments become MFMA operands at their first use in a k step (when
-  // they have long arrived): widened to fp16 in the widening kernels, their
-  // bytes' top bits flipped for uint8 on the int8 kernels (xor8 is 0 for
-  // int8).  Doing it at the read would make each read wait for its data.
+  // they have long arrived): widened to fp16 in the widening kernels.  Doing
+  // it at the read would make each read wait for its data.
   const bool a_e5m2 = p.f8a != 0, b_e5m2 = p.f8b != 0;
-  [[maybe_unused]] const int xor8 = (int)p.xor8;
   using raw_t = typename CF::RAW;
 
   for (int64_t t = g; t < p.tiles_total; t += G) {
@@ -1058,6 +1070,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     for (int i = 0; i < CF::FM; ++i)
 #pragma unroll
       for (int j = 0; j < CF::FN; ++j) acc[i][j] = acc_t{};
+    [[maybe_unused]] U8Init<CF> u8i;
+    if constexpr (CF::U8) u8i.load(p, l, m0 + wm * CF::WM, n0 + wn * CF::WN, lane);
 
     // Fragments of one k step as read from LDS: A blocks then B blocks of
     // this wave (double-buffered); widened operands of the current step.
@@ -1116,10 +1130,6 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
           if constexpr (I == 0) wb[J] = __builtin_bit_cast(v4i, widen8(fb[CUR][J], b_e5m2));
           acc[I][J] = MM::mma(wa[I], wb[J], acc[I][J]);
         } else {
-          if constexpr (CF::U8) {
-            if constexpr (J == 0) fa[CUR][I] ^= xor8;
-            if constexpr (I == 0) fb[CUR][J] ^= xor8;
-          }
           acc[I][J] = MM::mma(fa[CUR][I], fb[CUR][J], acc[I][J]);
         }
         static_for<0, NREAD>([&](auto r_c) {
@@ -1224,6 +1234,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       static_for<0, P0>([&](auto d_c) { dma_one(d_c, IntC<1>{}, t_pro, S - 1); });
     }
     barrier_lds();
+    if constexpr (CF::U8) u8i.apply(acc, p.u8_bias);
     load_step(fa[0], fb[0], 0, 0);
     // Guarded K tiles: the first one of the two-stage ring (its tile 1 was
     // issued whole) and every K tile whose loads reach past the last whole
@@ -1279,8 +1290,6 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       q.ialpha = 1;
       q.ibeta = q.ix = 0;
       q.relu = 0;
-      q.rsum_a = q.rsum_b = nullptr;
-      q.u8_bias = 0;
       if constexpr (CF::INT) epilogue_typed<CF, NM, T_I32, true>(q, acc, lds, wave, lane, l, emw, enw);
       else epilogue_typed<CF, NM, T_F32>(q, acc, lds, wave, lane, l, emw, enw);
     } else if constexpr (CF::INT) {

@@ -1,15 +1,15 @@
-// gemm_epi_u8.hip -- the sums along K that uint8 inputs need.
+// gemm_epi_u8.hip -- the operand preparation that uint8 inputs need.
 //
 // uint8 A/B (the pipeline API card's "int8 / uint8 with int32") run on the
-// int8 MFMA: every byte u is fed as the signed byte u - 128 (its top bit
-// flipped), and since
+// int8 MFMA: the GEMM reads copies of A and B with every byte's top bit
+// flipped, i.e. the signed byte u - 128, and since
 //   sum_k u_a u_b = sum_k (u_a - 128)(u_b - 128) + 128 (sum_k u_a + sum_k u_b) - 16384 K,
-// the int32 epilogue adds 128 times the sum along K of the output's A row and
-// B column, and -16384 K (-16384 times K rounded up to whole K tiles: the
-// MFMA also sums the zero bytes staged past K, flipped to -128 x -128; int32
-// arithmetic wraps, so the result is exact whenever it fits).  These kernels compute those sums: rsum[l][r] = sum_k
-// X[l][r][k] for a K-major operand (r = m or n), or sum_k X[l][k][r] for an
-// M-major A / N-major B.
+// each output's accumulator starts at 128 times the sum along K of its A row
+// and B column, minus 16384 K (int32 arithmetic wraps, so the result is
+// exact whenever it fits).  These kernels write the flipped copies and the
+// sums in one pass over each operand: sums[l][r] = sum_k X[l][r][k] for a
+// K-major operand (r = m or n), or sum_k X[l][k][r] for an M-major A /
+// N-major B.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -21,6 +21,8 @@ namespace {
 
 typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 
+constexpr unsigned kFlip = 0x80808080u;
+
 // Sum of the four bytes of each word, added to acc.
 __device__ __forceinline__ unsigned bytesum(v4u_t w, unsigned acc) {
   acc = __builtin_amdgcn_udot4(w.x, 0x01010101u, acc, false);
@@ -31,43 +33,66 @@ __device__ __forceinline__ unsigned bytesum(v4u_t w, unsigned acc) {
 
 // K-major: one wave per row, 16 bytes per lane and step (K bytes per row are
 // a multiple of 16), then a sum across the wave.
-__global__ __launch_bounds__(256) void sums_kmajor(const uint8_t* x, int64_t rows, int64_t K, int32_t* out) {
+__global__ __launch_bounds__(256) void prep_kmajor(const uint8_t* x, int64_t rows, int64_t K, uint8_t* flipped,
+                                                   int32_t* sums) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // over L * R rows
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
   const v4u_t* p = (const v4u_t*)(x + row * K);
+  v4u_t* q = (v4u_t*)(flipped + row * K);
   unsigned acc = 0;
-  for (int64_t c = lane; c < K / 16; c += 64) acc = bytesum(__builtin_nontemporal_load(p + c), acc);
+  for (int64_t c = lane; c < K / 16; c += 64) {
+    const v4u_t w = __builtin_nontemporal_load(p + c);
+    q[c] = w ^ kFlip;
+    acc = bytesum(w, acc);
+  }
   for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 64);
-  if (lane == 0) out[row] = (int32_t)acc;
+  if (lane == 0) sums[row] = (int32_t)acc;
 }
 
-// M-major A / N-major B: a thread owns 16 consecutive r (R is a multiple of
-// 16) and a chunk of k-rows; its sums are added into out with atomics
-// (out starts at zero).
-__global__ __launch_bounds__(256) void sums_mnmajor(const uint8_t* x, int64_t R, int64_t K, int64_t kchunk,
-                                                    int32_t* out) {
-  const int64_t r16 = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 16 r
+// M-major A / N-major B: a block covers 256 consecutive r (16 groups of 16)
+// and a chunk of kchunk k-rows; thread t owns the 16 r of group t % 16 and
+// every 16th k-row of the chunk from t / 16 on (a wave reads four k-rows of
+// 256 contiguous bytes).  The 16 partial sums per r are added through LDS,
+// and one atomic per r and block adds the chunk's sum into sums (zeroed
+// first).
+constexpr int kMnChunk = 512;
+__global__ __launch_bounds__(256) void prep_mnmajor(const uint8_t* x, int64_t R, int64_t K, uint8_t* flipped,
+                                                    int32_t* sums) {
+  __shared__ unsigned part[16][16][17];  // [k-lane][r group][r in group], padded
+  const int t = threadIdx.x, grp = t % 16, kl = t / 16;
+  const int64_t r16 = (int64_t)blockIdx.x * 16 + grp;  // group of 16 r
   const int l = blockIdx.z;
-  if (r16 * 16 >= R) return;
-  const int64_t k0 = (int64_t)blockIdx.y * kchunk;
-  const int64_t k1 = k0 + kchunk < K ? k0 + kchunk : K;
-  const uint8_t* base = x + (int64_t)l * K * R + r16 * 16;
+  const bool live = r16 * 16 < R;
+  const int64_t k0 = (int64_t)blockIdx.y * kMnChunk;
+  const int64_t k1 = k0 + kMnChunk < K ? k0 + kMnChunk : K;
+  const int64_t base = (int64_t)l * K * R + r16 * 16;
   unsigned s[16] = {};
-  for (int64_t k = k0; k < k1; ++k) {
-    const v4u_t w = __builtin_nontemporal_load((const v4u_t*)(base + k * R));
+  if (live) {
+#pragma unroll 8
+    for (int64_t k = k0 + kl; k < k1; k += 16) {
+      const v4u_t w = __builtin_nontemporal_load((const v4u_t*)(x + base + k * R));
+      *(v4u_t*)(flipped + base + k * R) = w ^ kFlip;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned v = w[j];
-      s[4 * j + 0] += v & 0xff;
-      s[4 * j + 1] += (v >> 8) & 0xff;
-      s[4 * j + 2] += (v >> 16) & 0xff;
-      s[4 * j + 3] += v >> 24;
+      for (int j = 0; j < 4; ++j) {
+        const unsigned v = w[j];
+        s[4 * j + 0] += v & 0xff;
+        s[4 * j + 1] += (v >> 8) & 0xff;
+        s[4 * j + 2] += (v >> 16) & 0xff;
+        s[4 * j + 3] += v >> 24;
+      }
     }
   }
-  int32_t* o = out + (int64_t)l * R + r16 * 16;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) atomicAdd(o + j, (int32_t)s[j]);
+  for (int j = 0; j < 16; ++j) part[kl][grp][j] = s[j];
+  __syncthreads();
+  // thread t adds up r = 16 * (t / 16) + t % 16 of this block over the k-lanes
+  const int g2 = t / 16, j2 = t % 16;
+  unsigned sum = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) sum += part[k][g2][j2];
+  const int64_t r = ((int64_t)blockIdx.x * 16 + g2) * 16 + j2;
+  if (r < R) atomicAdd(sums + (int64_t)l * R + r, (int32_t)sum);
 }
 
 __global__ __launch_bounds__(256) void fill_zero(int32_t* p, int64_t n) {
@@ -76,18 +101,17 @@ __global__ __launch_bounds__(256) void fill_zero(int32_t* p, int64_t n) {
 
 }  // namespace
 
-void launch_u8_sums(const uint8_t* x, bool kmajor, int64_t L, int64_t R, int64_t K, int32_t* out,
-                    hipStream_t s) {
+void launch_u8_prep(const uint8_t* x, bool kmajor, int64_t L, int64_t R, int64_t K, uint8_t* flipped,
+                    int32_t* sums, hipStream_t s) {
   if (kmajor) {
     const int64_t rows = L * R;
-    hipLaunchKernelGGL(sums_kmajor, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, x, rows, K, out);
+    hipLaunchKernelGGL(prep_kmajor, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, x, rows, K, flipped, sums);
   } else {
     const int64_t n = L * R;
     hipLaunchKernelGGL(fill_zero, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)), dim3(256), 0,
-                       s, out, n);
-    const int64_t kchunk = 64;
-    const dim3 grid((unsigned)((R / 16 + 255) / 256), (unsigned)((K + kchunk - 1) / kchunk), (unsigned)L);
-    hipLaunchKernelGGL(sums_mnmajor, grid, dim3(256), 0, s, x, R, K, kchunk, out);
+                       s, sums, n);
+    const dim3 grid((unsigned)((R + 255) / 256), (unsigned)((K + kMnChunk - 1) / kMnChunk), (unsigned)L);
+    hipLaunchKernelGGL(prep_mnmajor, grid, dim3(256), 0, s, x, R, K, flipped, sums);
   }
 }
 

@@ -117,7 +117,9 @@ typedef struct gemm_epi_plan {
   int32_t lds_bytes;    /* LDS per workgroup */
   int32_t cus;          /* compute units of the device */
   int32_t splits;       /* K slices (1: no split-K) */
-  int64_t workspace_bytes; /* split-K partial sums: splits * L*M*N * 4 (0 if none) */
+  int64_t workspace_bytes; /* device workspace of a run (0 if none): split-K
+                              partial sums (splits * L*M*N * 4), or the uint8
+                              sums and flipped copies (see gemm_epi_run) */
   char name[64];        /* kernel variant name */
 } gemm_epi_plan;
 
@@ -173,12 +175,14 @@ int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
  * alpha, beta, x_factor : fp32 scalars.  With int32 outputs they must be
  *            integers of magnitude <= 2^24 (the epilogue is then exact int32
  *            arithmetic), else GEMM_EPI_ERR_UNSUPPORTED.
- * uint8 A/B run on the int8 MFMA with every byte's top bit flipped (u - 128)
- * and three small kernels before it that sum each A row and B column of the
- * unsigned bytes along K into the handle's workspace (L*(M+N)*4 bytes,
- * allocated like a split-K workspace; uint8 plans never split K); the int32
- * epilogue adds 128*(row sum + column sum) - 16384*K, wrapping, which makes
- * the result exact whenever it fits in int32.
+ * uint8 A/B run on the int8 MFMA: small kernels before the GEMM write copies
+ * of A and B with every byte's top bit flipped (u - 128) and the sums of
+ * each A row and B column of the unsigned bytes along K into the handle's
+ * workspace (L*(M+N)*4 bytes of sums, then L*M*K and L*N*K bytes of copies,
+ * each part at a 256-byte boundary; allocated like a split-K workspace;
+ * uint8 plans never split K, and M and N must be below 2^29); every
+ * accumulator starts at 128*(row sum + column sum) - 16384*K, wrapping,
+ * which makes the result exact whenever it fits in int32.
  * Split-K plans (gemm_epi_plan.splits > 1) run two kernels on `stream`: the
  * K slices write fp32 (int32) partial sums to a workspace of
  * plan.workspace_bytes, then a second kernel adds them (in slice order) and
