@@ -19,12 +19,12 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgemm_epi.so")
 MAIN_SOURCE = os.path.join(CSRC, "gemm_epi.hip")
 SPLITK_SOURCE = os.path.join(CSRC, "gemm_epi_splitk.hip")
-U8_SOURCE = os.path.join(CSRC, "gemm_epi_u8.hip")
+PREP_SOURCE = os.path.join(CSRC, "gemm_epi_prep.hip")
 PART_SOURCE = os.path.join(CSRC, "gemm_epi_part.hip")
 GEMM_EPI_PARTS = 16
-SOURCES = [MAIN_SOURCE, PART_SOURCE, SPLITK_SOURCE, U8_SOURCE]
+SOURCES = [MAIN_SOURCE, PART_SOURCE, SPLITK_SOURCE, PREP_SOURCE]
 HEADERS = [os.path.join(CSRC, "gemm_epi_kernel.hpp"), os.path.join(CSRC, "gemm_epi_launch.hpp"),
-           os.path.join(CSRC, "gemm_epi_splitk.hpp"), os.path.join(CSRC, "gemm_epi_u8.hpp"),
+           os.path.join(CSRC, "gemm_epi_splitk.hpp"), os.path.join(CSRC, "gemm_epi_prep.hpp"),
            os.path.join(CSRC, "gemm_epi_variants.inc"), os.path.join(ROOT, "include", "gemm_epi.h")]
 # measurement tool used by bench.py --mfma-ceiling (not part of the GEMM path)
 CEILING_LIB = os.path.join(HERE, "libmfma_ceiling.so")
@@ -111,7 +111,7 @@ def build(verbose: bool = False, extra=(), only=None, cache_dir=None) -> str:
                  for k in range(GEMM_EPI_PARTS)]
         units += [obj("main.o", MAIN_SOURCE, HEADERS),
                   obj("splitk.o", SPLITK_SOURCE, [os.path.join(CSRC, "gemm_epi_splitk.hpp")]),
-                  obj("u8.o", U8_SOURCE, [os.path.join(CSRC, "gemm_epi_u8.hpp")])]
+                  obj("prep.o", PREP_SOURCE, [os.path.join(CSRC, "gemm_epi_prep.hpp")])]
         jobs = [cmd for _, cmd in units if cmd]
         ceil_tmp = CEILING_LIB + ".tmp%d" % os.getpid()
         jobs.append(["hipcc"] + HIPCC_FLAGS + INCLUDES + ["-shared", "-o", ceil_tmp, CEILING_SOURCE])

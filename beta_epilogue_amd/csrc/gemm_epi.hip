@@ -23,7 +23,7 @@
 #include "gemm_epi_kernel.hpp"
 #include "gemm_epi_launch.hpp"
 #include "gemm_epi_splitk.hpp"
-#include "gemm_epi_u8.hpp"
+#include "gemm_epi_prep.hpp"
 
 namespace {
 
@@ -134,7 +134,9 @@ struct gemm_epi_handle {
   int group_m;
   int splits;                       // K slices (1: no split)
   int64_t kslice;                   // K elements per slice
-  int64_t ws_bytes;                 // workspace: split-K partial sums, or the uint8 sums and copies
+  int64_t ws_bytes;                 // workspace: split-K partial sums, then the prepared operands
+  bool widen;                       // fp8 A/B run as fp16 copies
+  int64_t prep_off;                 // the prepared operands (uint8 sums and copies, fp16 copies)
   std::atomic<void*> ws{nullptr};   // allocated by the first gemm_epi_run, freed by destroy
   std::mutex ws_mutex;
   void* ws_static = nullptr;        // device address of the static scratch array
@@ -244,19 +246,28 @@ static int exact_ab(const gemm_epi_desc* d) {
   return -1;
 }
 
-// Whether variant v runs the problem.  fp8 A/B with an fp32 D or Y run only
-// the kernels that widen fp8 to fp16 before an f16 MFMA (exact conversion,
-// fp32 sums), so the fp32 outputs keep fp32's precision; other fp8 problems
-// run an fp8-MFMA kernel of their pairing and layout, or, for the pairings
-// and layouts that have none, a widening kernel.
+static bool same_layout(const Variant& v, const gemm_epi_desc* d) {
+  return v.a_major == d->a_major && v.b_major == d->b_major && v.cd_major == d->cd_major;
+}
+
+// fp8 A/B that run widened: a preparation pass converts A and B to fp16
+// copies (exact: every e4m3 and e5m2 value is an fp16 value) and an fp16
+// kernel of the same layout runs on them.  So it is for an fp32 D or Y (the
+// fp8 MFMA sums a group of products with fewer fraction bits than fp32
+// keeps) and for the pairings and layouts no fp8-MFMA kernel is built for.
+static bool widened(const gemm_epi_desc* d) {
+  if (!is_fp8(d->ab_dtype) || !is_fp8(b_type(d))) return false;
+  if (d->d_dtype == GEMM_EPI_F32 || d->y_dtype == GEMM_EPI_F32) return true;
+  for (int i = 0; i < kNumVariants; ++i)
+    if (kVariants[i].ab == exact_ab(d) && same_layout(kVariants[i], d)) return false;
+  return true;
+}
+
+// Whether variant v runs the problem: the layout's kernel of the problem's
+// type, or of fp16 for a widened fp8 problem.
 static bool variant_fits(const Variant& v, const gemm_epi_desc* d) {
-  if (v.a_major != d->a_major || v.b_major != d->b_major || v.cd_major != d->cd_major) return false;
-  if (is_fp8(d->ab_dtype) && is_fp8(b_type(d))) {
-    const bool f32_out = d->d_dtype == GEMM_EPI_F32 || d->y_dtype == GEMM_EPI_F32;
-    if (v.ab == gemm_epi::T_W_F8) return true;
-    return !f32_out && v.ab == exact_ab(d);
-  }
-  return v.ab == exact_ab(d);
+  if (!same_layout(v, d)) return false;
+  return v.ab == (widened(d) ? gemm_epi::T_F16 : exact_ab(d));
 }
 
 extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
@@ -283,8 +294,9 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
                 kVariants[variant].name);
   }
   const Variant& v = kVariants[variant];
-  // Buffer offsets within one tile's rows are 32-bit.
-  const int es = elem_bytes(desc->ab_dtype);
+  // Buffer offsets within one tile's rows are 32-bit (a widened fp8 operand
+  // is read as its fp16 copy).
+  const int es = widened(desc) ? 2 : elem_bytes(desc->ab_dtype);
   if ((int64_t)v.bm * desc->K * es >= (int64_t(1) << 31) ||
       (int64_t)v.bn * desc->K * es >= (int64_t(1) << 31))
     return fail(GEMM_EPI_ERR_UNSUPPORTED, "K too large for 32-bit tile offsets");
@@ -339,10 +351,17 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   h->kslice = ((ktiles + splits - 1) / splits) * v.bk;
   h->splits = (int)((desc->K + h->kslice - 1) / h->kslice);
   if (h->splits == 1) h->kslice = desc->K;
+  // Workspace: the split-K partial sums, then (at a 256-byte boundary) the
+  // prepared operands: for uint8 the row sums of A, the column sums of B and
+  // the flipped copies of A and B, for widened fp8 the fp16 copies of A and
+  // B (each part at a 256-byte boundary).
+  h->widen = widened(desc);
   h->ws_bytes = h->splits > 1 ? (int64_t)h->splits * desc->L * desc->M * desc->N * 4 : 0;
-  // uint8: row sums of A and column sums of B, then the flipped copies of A
-  // and B (each at a 256-byte boundary)
-  if (u8) h->ws_bytes = u8_layout(desc, nullptr, nullptr, nullptr);
+  h->prep_off = (h->ws_bytes + 255) / 256 * 256;
+  if (u8) h->ws_bytes = h->prep_off + u8_layout(desc, nullptr, nullptr, nullptr);
+  if (h->widen)
+    h->ws_bytes = h->prep_off + (desc->L * desc->M * desc->K * 2 + 255) / 256 * 256 +
+                  (desc->L * desc->N * desc->K * 2 + 255) / 256 * 256;
   h->grid = (int)std::min<int64_t>(h->tiles * h->splits, (int64_t)h->cus);  // one workgroup per CU
   if (scratch_address(dev, &h->ws_static) != GEMM_EPI_OK) {
     delete h;
@@ -420,8 +439,6 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
   p.ix = int_path ? (int32_t)x_factor : 0;
   p.xcd_remap = (h->grid % 8 == 0) ? 1 : 0;
   p.relu = d.epilogue == GEMM_EPI_RELU ? 1 : 0;
-  p.f8a = d.ab_dtype == GEMM_EPI_E5M2 ? 1 : 0;
-  p.f8b = b_type(&d) == GEMM_EPI_E5M2 ? 1 : 0;
   // Element type shared by every C/X/D/Y in use (one-type epilogue), else 0
   // (mixed-type epilogue).
   int kind = d.d_dtype;
@@ -457,13 +474,24 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
   }
 
   (void)hipGetLastError();  // clear a stale error so the check below is ours
+  if (h->widen) {
+    // fp16 copies of the fp8 operands (exact), read by the fp16 kernel
+    uint16_t* wa = (uint16_t*)((char*)p.ws + h->prep_off);
+    uint16_t* wb = (uint16_t*)((char*)wa + (d.L * d.M * d.K * 2 + 255) / 256 * 256);
+    gemm_epi::launch_f8_widen((const uint8_t*)A, d.L * d.M * d.K, d.ab_dtype == GEMM_EPI_E5M2, wa,
+                              (hipStream_t)stream);
+    gemm_epi::launch_f8_widen((const uint8_t*)B, d.L * d.N * d.K, b_type(&d) == GEMM_EPI_E5M2, wb,
+                              (hipStream_t)stream);
+    p.A = wa;
+    p.B = wb;
+  }
   if (u8) {
     // one pass over each operand: its flipped copy (u - 128 as a signed
     // byte) and its sums along K; the GEMM reads the copies, and every
     // accumulator starts at 128 * (row sum + column sum) - 16384 * K
     int32_t* sums = nullptr;
     uint8_t* flipped[2] = {nullptr, nullptr};
-    u8_layout(&d, (char*)p.ws, &sums, flipped);
+    u8_layout(&d, (char*)p.ws + h->prep_off, &sums, flipped);
     int32_t* ra = sums;
     int32_t* rb = sums + d.L * d.M;
     gemm_epi::launch_u8_prep((const uint8_t*)A, d.a_major == GEMM_EPI_MAJOR_K, d.L, d.M, d.K, flipped[0], ra,

@@ -42,10 +42,6 @@ namespace gemm_epi {
 enum : int { T_NONE = 0, T_F16 = 1, T_BF16 = 2, T_E4M3 = 3, T_I8 = 4, T_F32 = 5, T_I32 = 6, T_E5M2 = 7 };
 // Kernel A/B codes of the fp8 pairs (A's format x B's).
 enum : int { T_E4M3_E5M2 = 8, T_E5M2_E4M3 = 9 };
-// Kernel A/B code of fp8 operands (any pairing, formats chosen at run time)
-// widened to fp16 before the f16 MFMA: used when an fp32 output is asked for,
-// and for the fp8 pairings and layouts no fp8-MFMA kernel is built for.
-enum : int { T_W_F8 = 10 };
 // Kernel A/B code of uint8: the int8 MFMA on copies of A and B with every
 // byte's top bit flipped, the accumulators started at the sums' correction.
 enum : int { T_U8 = 14 };
@@ -83,7 +79,6 @@ struct Params {
   int32_t xcd_remap;          // grid is a multiple of 8: remap ids per XCD
   int32_t epi_kind;           // element type shared by every C/X/D/Y in use (0: mixed)
   int32_t relu;               // D = max(0, alpha*acc + beta*C) + x_factor*X
-  int32_t f8a, f8b;           // widening kernels: fp8 format of A, B (0 e4m3, 1 e5m2)
   // Split K: the K range is cut into `splits` slices of kslice elements (a
   // multiple of the K tile; the last one may be shorter).  With splits > 1 a
   // tile of slice s writes its fp32 (int32) partial sums to ws + s * L*M*N
@@ -225,48 +220,6 @@ struct MmaF8Pair : MmaLayout32 {
 template <> struct Mma<T_E4M3_E5M2, 32> : MmaF8Pair<0, 1> {};
 template <> struct Mma<T_E5M2_E4M3, 32> : MmaF8Pair<1, 0> {};
 
-// Eight fp8 values (format F: 0 e4m3, 1 e5m2) widened to fp16.  Every finite
-// e4m3 and e5m2 value, subnormals included, is an fp16 value (e4m3: |v| <= 448,
-// steps down to 2^-9; e5m2: |v| <= 57344, steps down to 2^-16), so with a scale
-// of 1 the conversion is exact, and NaN stays NaN.  Byte i of the input is
-// element i of the result.
-template <int F>
-__device__ __forceinline__ v8h widen8(v2i x) {
-  v2h h[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const unsigned w = (unsigned)(i < 2 ? x.x : x.y);
-    if constexpr (F == 0)
-      h[i] = (i & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
-                     : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
-    else
-      h[i] = (i & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, true)
-                     : __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, false);
-  }
-  return v8h{h[0].x, h[0].y, h[1].x, h[1].y, h[2].x, h[2].y, h[3].x, h[3].y};
-}
-
-// fp8 operands in LDS, widened to fp16 in registers for the 16x16x32 f16
-// MFMA: the products and their fp32 sums are those of fp16 inputs, so fp32
-// outputs keep fp32's precision (the fp8 MFMA sums a group of products with
-// fewer fraction bits).  The formats of A and B (Params::f8a, f8b) are
-// uniform run-time values: each conversion computes both decodings and keeps
-// one, so one kernel serves every pairing.  A k step is 32 bytes of an LDS
-// row; lane group q = l / 16 takes bytes [8q, 8q + 8).
-__device__ __forceinline__ v8h widen8(v2i x, bool e5m2) {
-  const v8h a = widen8<0>(x), b = widen8<1>(x);
-  return e5m2 ? b : a;
-}
-struct MmaWiden : MmaLayout16 {
-  typedef v4f acc_t;
-  typedef v4i frag_t;  // eight fp16 values, after widening
-  static constexpr int ESIZE = 1, KSB = 32;
-  static __device__ __forceinline__ acc_t mma(frag_t a, frag_t b, acc_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c,
-                                                  0, 0, 0);
-  }
-};
-template <> struct Mma<T_W_F8, 16> : MmaWiden {};
 template <> struct Mma<T_U8, 16> : Mma<T_I8, 16> {};
 template <> struct Mma<T_U8, 32> : Mma<T_I8, 32> {};
 
@@ -285,12 +238,9 @@ struct Cfg {
   static constexpr int BLK = BLK_;
   using MM = Mma<AB_, BLK_>;
   static constexpr int DQ = DQ_;
-  // fp8 widened to fp16: an LDS fragment (8 bytes per lane) becomes a register
-  // fragment of eight fp16 values
-  static constexpr bool WIDEN = AB_ == T_W_F8;
   static constexpr bool INT = AB_ == T_I8 || AB_ == T_U8;  // int32 accumulators and epilogue
   static constexpr bool U8 = AB_ == T_U8;
-  using RAW = typename std::conditional<WIDEN, v2i, typename MM::frag_t>::type;
+  using RAW = typename MM::frag_t;  // a fragment as read from LDS
   static_assert(DQ >= 0 && DQ <= 4 && (STAGES_ == 2 || DQ == 0), "DQ: quarters, two-stage rings only");
   static constexpr int AB = AB_;
   static constexpr bool A_KMAJOR = A_KMAJOR_, B_KMAJOR = B_KMAJOR_, CD_NMAJOR = CD_NMAJOR_;
@@ -305,10 +255,9 @@ struct Cfg {
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile
   static constexpr int FM = WM / BLK, FN = WN / BLK;         // MFMA output blocks
   // bytes of one k step per lane: lane group q = l / BLK reads bytes
-  // [q*BPL, q*BPL + BPL) of the step, i.e. CPL whole 16-byte chunks (or, for
-  // BPL = 8, half of chunk q / 2)
+  // [q*BPL, q*BPL + BPL) of the step, i.e. CPL whole 16-byte chunks
   static constexpr int BPL = MM::KSB / (64 / BLK);
-  static constexpr int CPL = BPL >= 16 ? BPL / 16 : 1;
+  static constexpr int CPL = BPL / 16;
   static constexpr int STAGES = STAGES_;
   static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
   static constexpr int PIPE_BYTES = STAGES * STAGE_BYTES;
@@ -323,7 +272,7 @@ struct Cfg {
   static constexpr int LDS_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
   static constexpr int KSTEPS = ROWB / MM::KSB;
   static_assert(KSTEPS >= 1, "a stage must hold at least one MFMA k step");
-  static_assert(BPL * (64 / BLK) == MM::KSB && (BPL == 8 || BPL == 16 || BPL == 32),
+  static_assert(BPL * (64 / BLK) == MM::KSB && (BPL == 16 || BPL == 32),
                 "k step must split evenly over lane groups");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32-line epilogue blocks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
@@ -478,10 +427,7 @@ struct KMajorOperand {
     static_assert(CF::BLK % (CF::CH << CF::SWZ_SHIFT) == 0, "block rows span whole swizzle periods");
     const char* rp = lds + off + row0 * CF::ROWB + blk * (CF::BLK * CF::ROWB);
     const int sw = swz<CF>(row0);
-    if constexpr (CF::BPL == 8) {
-      const int c = s * (CF::MM::KSB / 16) + (q >> 1);
-      return *(const v2i*)(rp + ((c ^ sw) << 4) + (q & 1) * 8);
-    } else if constexpr (CF::CPL == 1) {
+    if constexpr (CF::CPL == 1) {
       const int c = s * (CF::MM::KSB / 16) + q;
       return *(const v4i*)(rp + ((c ^ sw) << 4));
     } else {
@@ -514,15 +460,12 @@ struct MNSwizzle {
   //   2-byte, 16x16 blocks: k-rows {0..3, 8..11} (+4), 2 chunks each;
   //   2-byte, 32x32 blocks: k-rows {0..3} (+4), 4 chunks each;
   //   1-byte, 16x16 blocks, 16 B per lane: k-rows {0..7, 16..23} (+8), 1 chunk;
-  //   1-byte, 16x16 blocks, 8 B per lane (widened fp8): k-rows {0..15}, 1 chunk;
   //   1-byte, 32x32 blocks: k-rows {0..7} (+8), 2 chunks each.
   static constexpr __host__ __device__ int of(int k) {
     if constexpr (CF::MM::ESIZE == 2)
       return CF::BLK == 16 ? 2 * ((k & 3) | ((k >> 1) & 4)) : 4 * (k & 3);
     else if constexpr (CF::BLK == 32)
       return 2 * (k & 7);
-    else if constexpr (CF::BPL == 8)
-      return k & 15;
     else
       return (k & 7) | ((k >> 1) & 8);
   }
@@ -611,8 +554,7 @@ struct MNMajorOperand {
       r[2 * h] = v.x;
       r[2 * h + 1] = v.y;
     }
-    if constexpr (NR == 1) return v2i{r[0], r[1]};
-    else if constexpr (NR == 2) return v4i{r[0], r[1], r[2], r[3]};
+    if constexpr (NR == 2) return v4i{r[0], r[1], r[2], r[3]};
     else return v8i{r[0], r[1], r[2], r[3], r[4], r[5], r[6], r[7]};
   }
 };
@@ -1037,10 +979,6 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
   OpB opb;
   opa.setup_reader(wm * CF::WM, lane);
   opb.setup_reader(wn * CF::WN, lane);
-  // LDS fragments become MFMA operands at their first use in a k step (when
-  // they have long arrived): widened to fp16 in the widening kernels.  Doing
-  // it at the read would make each read wait for its data.
-  const bool a_e5m2 = p.f8a != 0, b_e5m2 = p.f8b != 0;
   using raw_t = typename CF::RAW;
 
   for (int64_t t = g; t < p.tiles_total; t += G) {
@@ -1074,9 +1012,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     if constexpr (CF::U8) u8i.load(p, l, m0 + wm * CF::WM, n0 + wn * CF::WN, lane);
 
     // Fragments of one k step as read from LDS: A blocks then B blocks of
-    // this wave (double-buffered); widened operands of the current step.
+    // this wave (double-buffered).
     raw_t fa[2][CF::FM], fb[2][CF::FN];
-    [[maybe_unused]] frag_t wa[CF::FM], wb[CF::FN];
     auto load_step = [&](raw_t (&ra)[CF::FM], raw_t (&rb)[CF::FN], int st, int s) {
 #pragma unroll
       for (int i = 0; i < CF::FM; ++i) ra[i] = opa.read(lds, st * A_STAGE, i, s);
@@ -1125,13 +1062,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       static_for<0, MF>([&](auto idx_c) {
         constexpr int IDX = decltype(idx_c)::value;
         constexpr int I = IDX / CF::FN, J = IDX % CF::FN;
-        if constexpr (CF::WIDEN) {
-          if constexpr (J == 0) wa[I] = __builtin_bit_cast(v4i, widen8(fa[CUR][I], a_e5m2));
-          if constexpr (I == 0) wb[J] = __builtin_bit_cast(v4i, widen8(fb[CUR][J], b_e5m2));
-          acc[I][J] = MM::mma(wa[I], wb[J], acc[I][J]);
-        } else {
-          acc[I][J] = MM::mma(fa[CUR][I], fb[CUR][J], acc[I][J]);
-        }
+        acc[I][J] = MM::mma(fa[CUR][I], fb[CUR][J], acc[I][J]);
         static_for<0, NREAD>([&](auto r_c) {
           constexpr int R = decltype(r_c)::value;
           if constexpr ((R * MF) / NREAD == IDX) read_r(IntC<CUR ^ 1>{}, r_c, rst, rs);

@@ -1,4 +1,5 @@
-// gemm_epi_u8.hip -- the operand preparation that uint8 inputs need.
+// gemm_epi_prep.hip -- the operand preparation passes that uint8 inputs and
+// widened fp8 inputs need.
 //
 // uint8 A/B (the pipeline API card's "int8 / uint8 with int32") run on the
 // int8 MFMA: the GEMM reads copies of A and B with every byte's top bit
@@ -13,7 +14,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "gemm_epi_u8.hpp"
+#include "gemm_epi_prep.hpp"
 
 namespace gemm_epi {
 
@@ -95,11 +96,54 @@ __global__ __launch_bounds__(256) void prep_mnmajor(const uint8_t* x, int64_t R,
   if (r < R) atomicAdd(sums + (int64_t)l * R + r, (int32_t)sum);
 }
 
+// fp8 -> fp16, 16 elements per thread and step.  Every finite e4m3 and e5m2
+// value, subnormals included, is an fp16 value (e4m3: |v| <= 448, steps down
+// to 2^-9; e5m2: |v| <= 57344, steps down to 2^-16), so the conversion with a
+// scale of 1 is exact, and NaN stays NaN.
+typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
+template <bool E5M2>
+__device__ __forceinline__ unsigned widen2(unsigned w, bool hi) {
+  v2h_t h;
+  if constexpr (E5M2)
+    h = hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, true) : __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, false);
+  else
+    h = hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true) : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(unsigned, h);
+}
+template <bool E5M2>
+__global__ __launch_bounds__(256) void widen_f8(const uint8_t* x, int64_t groups, uint16_t* out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups; g += stride) {
+    const v4u_t w = __builtin_nontemporal_load((const v4u_t*)x + g);
+    v4u_t lo, hi;
+    lo.x = widen2<E5M2>(w.x, false);
+    lo.y = widen2<E5M2>(w.x, true);
+    lo.z = widen2<E5M2>(w.y, false);
+    lo.w = widen2<E5M2>(w.y, true);
+    hi.x = widen2<E5M2>(w.z, false);
+    hi.y = widen2<E5M2>(w.z, true);
+    hi.z = widen2<E5M2>(w.w, false);
+    hi.w = widen2<E5M2>(w.w, true);
+    ((v4u_t*)out)[2 * g] = lo;
+    ((v4u_t*)out)[2 * g + 1] = hi;
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_zero(int32_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
 }
 
 }  // namespace
+
+void launch_f8_widen(const uint8_t* x, int64_t n, bool e5m2, uint16_t* out, hipStream_t s) {
+  const int64_t groups = n / 16;
+  const int64_t blocks = (groups + 255) / 256;
+  const dim3 grid((unsigned)(blocks < 8192 ? blocks : 8192));
+  if (e5m2)
+    hipLaunchKernelGGL(widen_f8<true>, grid, dim3(256), 0, s, x, groups, out);
+  else
+    hipLaunchKernelGGL(widen_f8<false>, grid, dim3(256), 0, s, x, groups, out);
+}
 
 void launch_u8_prep(const uint8_t* x, bool kmajor, int64_t L, int64_t R, int64_t K, uint8_t* flipped,
                     int32_t* sums, hipStream_t s) {

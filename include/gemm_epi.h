@@ -118,8 +118,10 @@ typedef struct gemm_epi_plan {
   int32_t cus;          /* compute units of the device */
   int32_t splits;       /* K slices (1: no split-K) */
   int64_t workspace_bytes; /* device workspace of a run (0 if none): split-K
-                              partial sums (splits * L*M*N * 4), or the uint8
-                              sums and flipped copies (see gemm_epi_run) */
+                              partial sums (splits * L*M*N * 4), then the
+                              uint8 sums and flipped copies (see gemm_epi_run)
+                              or the fp16 copies of widened fp8 operands (see
+                              gemm_epi_create) */
   char name[64];        /* kernel variant name */
 } gemm_epi_plan;
 
@@ -147,8 +149,12 @@ typedef struct gemm_epi_plan {
  * the current HIP device is queried once (compute units, architecture);
  * anything but gfx950 is GEMM_EPI_ERR_DEVICE.  Allocates only the host
  * object (GEMM_EPI_ERR_HOST_ALLOC if that fails).  fp8 A/B with an fp32 D or
- * Y select kernels that widen fp8 to fp16 in registers (exact) before an
- * f16 MFMA.  Returns GEMM_EPI_OK or an error code.
+ * Y, and fp8 pairings and layouts without an fp8 kernel, run widened: each
+ * run first converts A and B to fp16 copies in the workspace (exact: every
+ * e4m3 and e5m2 value is an fp16 value; L*M*K*2 and L*N*K*2 bytes, each at
+ * a 256-byte boundary, after any split-K partial sums) and an fp16 kernel
+ * of the layout runs on them (so the plan names an f16 variant).  Returns
+ * GEMM_EPI_OK or an error code.
  */
 int gemm_epi_create(const gemm_epi_desc* desc, gemm_epi_handle** out);
 
@@ -186,10 +192,10 @@ int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
  * Split-K plans (gemm_epi_plan.splits > 1) run two kernels on `stream`: the
  * K slices write fp32 (int32) partial sums to a workspace of
  * plan.workspace_bytes, then a second kernel adds them (in slice order) and
- * applies the epilogue.  The first such run allocates the workspace
- * (hipMalloc; it belongs to the handle and gemm_epi_destroy frees it), so
- * runs of one split-K handle that overlap in time on different streams race
- * on it.
+ * applies the epilogue.  Any plan with a workspace (split K, uint8, widened
+ * fp8) gets it at its first run (hipMalloc; it belongs to the handle and
+ * gemm_epi_destroy frees it), so runs of one such handle that overlap in
+ * time on different streams race on it.
  * Every pointer must be 16-byte aligned.  D may be C itself (the same
  * pointer, with d_dtype == c_dtype): an in-place update, since each output
  * element's C is read before its D is written by the same lane.  No other

@@ -133,19 +133,27 @@ def test_mixed_epilogue_types_run_on_every_block_shape():
         assert h.value is None
 
 
-def test_fp8_with_fp32_outputs_only_on_widening_variants():
-    """fp8 A/B with an fp32 D or Y run the kernels that widen fp8 to fp16: an
-    fp8-MFMA variant refuses such a problem, a widening one accepts it (and
-    also accepts fp8 problems without fp32 outputs, any pairing)."""
+def test_fp8_with_fp32_outputs_only_widened():
+    """fp8 A/B with an fp32 D or Y run widened: an fp16 kernel of the layout
+    on fp16 copies of A and B.  An fp8-MFMA variant refuses such a problem,
+    the fp16 one accepts it; without fp32 outputs the fp8 kernel of the
+    pairing runs and the fp16 one is refused, unless the pairing has no fp8
+    kernel for the layout (then the fp16 one runs it)."""
     names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
     f8 = names.index("e4m3_kk_n_256x256_r128_w4_s2")
-    w = names.index("f8w_kk_n_256x256_r128_w4_s2_b16")
+    e45 = names.index("e4e5_kk_n_256x256_r128_w4_s2")
+    f16 = names.index("f16_kk_n_256x256_r128_w4_s2_b16")
+    f16_mn = names.index("f16_mn_n_256x256_r128_w4_s2_q2")
     h = ctypes.c_void_p()
-    for d, y, v, ok, b in (("f32", None, f8, False, None), ("f16", "f32", f8, False, None),
-                           ("f32", None, w, True, None), ("f16", "f32", w, True, None),
-                           ("f16", None, w, True, None), ("f16", None, f8, True, None),
-                           ("f16", None, w, True, "e5m2"), ("f16", None, f8, False, "e5m2")):
-        desc = ge.make_desc(256, 256, 256, 1, ab="e4m3", c="f16", d=d, y=y, b=b)
+    cases = (("f32", None, f8, False, None, "K", "K"), ("f16", "f32", f8, False, None, "K", "K"),
+             ("f32", None, f16, True, None, "K", "K"), ("f16", "f32", f16, True, None, "K", "K"),
+             ("f16", None, f16, False, None, "K", "K"), ("f16", None, f8, True, None, "K", "K"),
+             ("f16", None, e45, True, "e5m2", "K", "K"), ("f16", None, f16, False, "e5m2", "K", "K"),
+             ("f16", None, f8, False, "e5m2", "K", "K"),
+             # the e4m3 x e5m2 pairing has no fp8 kernel with M-major A and N-major B
+             ("f16", None, f16_mn, True, "e5m2", "M", "N"))
+    for d, y, v, ok, b, am, bm in cases:
+        desc = ge.make_desc(256, 256, 256, 1, ab="e4m3", c="f16", d=d, y=y, b=b, a_major=am, b_major=bm)
         rc = ge.lib().gemm_epi_create_variant(ctypes.byref(desc), v, ctypes.byref(h))
         if ok:
             assert rc in (ge.GEMM_EPI_OK, ge.GEMM_EPI_ERR_DEVICE), (d, y, names[v])
