@@ -48,7 +48,6 @@ enum : int { T_U8 = 14 };
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -326,16 +325,6 @@ __device__ __forceinline__ void barrier_lds() {
 // KiB, written to LDS linearly; the swizzle of a layout is applied on the
 // global side (lane j fetches whichever chunk belongs in LDS chunk j).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(lds_addr), "v"(voff), "s"(rsrc)
-      : "memory", "m0");
-}
-
 // The mainloop form: LDS address m0 = sbase + IMM (IMM a compile-time
 // constant folded into the m0 write), global offset voff (per lane) + soff
 // (the K tile's byte offset, a scalar), so one load costs three issue slots
