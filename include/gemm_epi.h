@@ -211,13 +211,15 @@ int gemm_epi_run(const gemm_epi_handle* h, const void* A, const void* B,
 /*
  * For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): gemm_epi_run with the
- * same arguments, checks and results, which never allocates.  A split-K plan
- * uses a file-scope device array of GEMM_EPI_STATIC_SCRATCH_BYTES (one per
- * GPU, held until the process ends) as its workspace instead of the
- * handle's; a plan whose workspace is larger is GEMM_EPI_ERR_UNSUPPORTED.
- * Every call on one GPU shares that array (the partial sums of a call are
- * fully written before they are read, so nothing needs clearing), so calls
- * of split-K plans that overlap in time on one GPU race.
+ * same arguments, checks and results, which never allocates.  A plan with a
+ * workspace (split K, uint8, widened fp8) uses a file-scope device array of
+ * GEMM_EPI_STATIC_SCRATCH_BYTES (one per GPU, held until the process ends)
+ * as its workspace instead of the handle's; a plan whose workspace is larger
+ * is GEMM_EPI_ERR_UNSUPPORTED.  Every call on one GPU shares that array
+ * (everything a call reads there it wrote first in the same call, except the
+ * uint8 sums of an M-major A / N-major B, which a kernel of the call zeroes
+ * first, so nothing needs clearing), so calls of such plans that overlap in
+ * time on one GPU race.
  */
 int gemm_epi_run_static(const gemm_epi_handle* h, const void* A, const void* B,
                         const void* C, const void* X, void* D, void* Y,

@@ -1,6 +1,8 @@
-"""gemm_epi_run_static: the allocation-free run (split-K workspace in the
+"""gemm_epi_run_static: the allocation-free run (the workspace -- split-K
+partial sums, uint8 sums and copies, fp16 copies of widened fp8 -- in the
 library's static device array) against gemm_epi_run (the handle's own
-workspace), bit for bit, on two calls in a row, the second smaller."""
+workspace), bit for bit, on calls in a row, each smaller than the one
+before."""
 import sys
 
 import numpy as np
@@ -23,6 +25,9 @@ CASES = [
     # uint8: the row and column sums in the static array (no split)
     (synth.CONFIGS[3].replace(name="static_u8_smaller", M=128, N=144, K=512, L=1, ab="u8",
                               dist_ab="u8full", seed=7420), 0),
+    # fp8 with fp32 outputs: split-K partial sums, then the fp16 copies of A and B
+    (synth.CONFIGS[4].replace(name="static_e4m3_f32_widened", M=96, N=128, K=512, L=1, c="f32",
+                              d="f32", seed=7430), 2),
 ]
 
 
