@@ -903,10 +903,12 @@ struct U8Init {
   __device__ __forceinline__ void load(const Params& p, int l, int mw, int nw, int lane) {
     // resources based at this wave's first row / column; per-lane offsets
     // are one register each plus compile-time immediates
+    // (a wave whose first row or column lies past the matrix gets an empty
+    // resource: all its loads read zero)
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.rsum_a + (int64_t)l * p.M + mw), (short)0, (int)((p.M - mw) * 4), 0x00020000);
+        (void*)(p.rsum_a + (int64_t)l * p.M + mw), (short)0, (int)(max(p.M - mw, (int64_t)0) * 4), 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.rsum_b + (int64_t)l * p.N + nw), (short)0, (int)((p.N - nw) * 4), 0x00020000);
+        (void*)(p.rsum_b + (int64_t)l * p.N + nw), (short)0, (int)(max(p.N - nw, (int64_t)0) * 4), 0x00020000);
     const int la = MM::acc_row(lane, 0) * 4, lb = (lane % BLK) * 4;
 #pragma unroll
     for (int j = 0; j < CF::FN; ++j) cb[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rb, lb + j * BLK * 4, 0, 0);
