@@ -95,36 +95,63 @@ def cpu_baseline(p, ins, target_s: float):
                       "plus the epilogue each), %.1f s" % (rows, rows * p.N, p.K, dt)}
 
 
-def mfma_ceiling(iters: int = 80000, rounds: int = 3, kinds=("constant", "random"), blocks=(32, 16)):
-    """Steady clock and rate of v_mfma_f32_32x32x16_f16 (block 32) and
-    v_mfma_f32_16x16x32_f16 (block 16) with no memory traffic, constant vs
-    uniformly random fp16 operands, alternated `rounds` times."""
+CEILING_TYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "i8": 4}
+CEILING_INSTR = {"f16": ("v_mfma_f32_32x32x16_f16", "v_mfma_f32_16x16x32_f16"),
+                 "bf16": ("v_mfma_f32_32x32x16_bf16", "v_mfma_f32_16x16x32_bf16"),
+                 "e4m3": ("v_mfma_scale_f32_32x32x64_f8f6f4", "v_mfma_scale_f32_16x16x128_f8f6f4"),
+                 "i8": ("v_mfma_i32_32x32x32_i8", "v_mfma_i32_16x16x64_i8")}
+
+
+def mfma_ceiling(iters: int = 80000, rounds: int = 3, kinds=("constant", "random"), blocks=(32, 16),
+                 types=("f16",)):
+    """Steady clock and rate of register-only MFMA streams (block 32: the
+    32x32 instruction, block 16: the 16x16 one) with no memory traffic,
+    constant vs random operands (libmfma_ceiling.so), alternated `rounds`
+    times, for each operand type in `types` (f16, bf16, e4m3, i8)."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "beta_epilogue_amd", "libmfma_ceiling.so"))
-    fn = lib.mfma_ceiling_run
-    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
-                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    fn = lib.mfma_ceiling_run_type
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double),
+                   ctypes.POINTER(ctypes.c_double)]
     fn.restype = ctypes.c_int
-    runs = {"%s_%dx%d" % (k, b, b): [] for b in blocks for k in kinds}
-    for _ in range(rounds):
-        for blk in blocks:
-            for kind, rnd in (("constant", 0), ("random", 1)):
-                key = "%s_%dx%d" % (kind, blk, blk)
-                if key not in runs:
-                    continue
-                ms, ghz, tf = ctypes.c_float(), ctypes.c_double(), ctypes.c_double()
-                rc = fn(blk, rnd, iters, 3, ctypes.byref(ms), ctypes.byref(ghz), ctypes.byref(tf))
-                if rc != 0:
-                    raise RuntimeError("mfma_ceiling_run failed with HIP error %d" % rc)
-                runs[key].append({"ms": round(ms.value, 3), "ghz": round(ghz.value, 3),
-                                  "tflops": round(tf.value, 1)})
-    out = {"metric": "register-only fp16 MFMA stream, 8 waves per CU "
-                     "(32x32: v_mfma_f32_32x32x16_f16, 16x16: v_mfma_f32_16x16x32_f16)",
-           "unit": "TFLOP/s"}
-    for key, r in runs.items():
-        out[key] = {"tflops": round(sum(x["tflops"] for x in r) / len(r), 1),
-                    "ghz": round(sum(x["ghz"] for x in r) / len(r), 3), "runs": r}
-    return out
+    out = {}
+    for t in types:
+        # int8 and fp8 instructions do 2x and 4x the FLOP of the fp16 ones per
+        # step; fewer steps keep every launch near the same length
+        n = iters if t in ("f16", "bf16") else iters // 2
+        runs = {"%s_%dx%d" % (k, b, b): [] for b in blocks for k in kinds}
+        for _ in range(rounds):
+            for blk in blocks:
+                for kind, rnd in (("constant", 0), ("random", 1)):
+                    key = "%s_%dx%d" % (kind, blk, blk)
+                    if key not in runs:
+                        continue
+                    ms, ghz, tf = ctypes.c_float(), ctypes.c_double(), ctypes.c_double()
+                    rc = fn(CEILING_TYPES[t], blk, rnd, n, 3, ctypes.byref(ms), ctypes.byref(ghz),
+                            ctypes.byref(tf))
+                    if rc != 0:
+                        raise RuntimeError("mfma_ceiling_run_type failed with HIP error %d" % rc)
+                    runs[key].append({"ms": round(ms.value, 3), "ghz": round(ghz.value, 3),
+                                      "tflops": round(tf.value, 1)})
+        res = {"instructions": {"32x32": CEILING_INSTR[t][0], "16x16": CEILING_INSTR[t][1]},
+               "unit": "TOP/s" if t == "i8" else "TFLOP/s", "peak": PEAK[t]}
+        for key, r in runs.items():
+            res[key] = {"tflops": round(sum(x["tflops"] for x in r) / len(r), 1),
+                        "ghz": round(sum(x["ghz"] for x in r) / len(r), 3), "runs": r}
+        out[t] = res
+    return {"metric": "register-only MFMA stream, 8 waves per CU, constant vs random operands", "types": out}
+
+
+def attainable_rate(ab: str, achieved: float):
+    """The faster random-operand stream of the workload's operand type, as
+    measured now, and the kernel's fraction of it."""
+    cr = mfma_ceiling(rounds=2, kinds=("random",), types=(ab,))["types"][ab]
+    key, c = max(((k, v) for k, v in cr.items() if k.startswith("random_")), key=lambda kv: kv[1]["tflops"])
+    return {"tflops": c["tflops"], "ghz": c["ghz"], "frac": round(achieved / c["tflops"], 4),
+            "shape": key.split("_")[1], "instruction": cr["instructions"][key.split("_")[1]],
+            "how": "the faster of the 32x32 and 16x16 register-only MFMA streams of this operand type on "
+                   "every CU, seeded random operands, same run (bench.py --mfma-ceiling)"}
 
 
 def main():
@@ -141,8 +168,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true",
-                    help="only measure a register-only fp16 MFMA stream on every CU with "
-                         "constant and with random operands (steady clock and TFLOP/s)")
+                    help="only measure register-only MFMA streams (fp16, bf16, e4m3, int8) on every "
+                         "CU with constant and with random operands (steady clock and rate)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the MFMA-ceiling measurement of the default run")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -163,7 +190,7 @@ def main():
     import beta_epilogue_amd as ge
 
     if args.mfma_ceiling:
-        print(json.dumps(mfma_ceiling()), flush=True)
+        print(json.dumps(mfma_ceiling(types=tuple(CEILING_TYPES))), flush=True)
         return
 
     if args.copy_calibration:
@@ -228,20 +255,13 @@ def main():
                                          min(launch_ms), max(launch_ms), wall,
                                          plan["name"]), file=sys.stderr, flush=True)
 
-    # The attainable MFMA rate on this machine for fp16 data like the workload's
-    # (random operands; the power cap sets the clock), measured right after.
+    # The attainable MFMA rate on this machine for operands like the workload's
+    # (random data; the power cap sets the clock), measured right after.
     abytes = p.algorithmic_bytes()
     mfma_bound = flops / abytes >= peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     attainable = None
-    if p.ab == "f16" and mfma_bound and not args.no_ceiling:
-        cr = mfma_ceiling(rounds=2, kinds=("random",))
-        key, c = max(((k, v) for k, v in cr.items() if k.startswith("random_")),
-                     key=lambda kv: kv[1]["tflops"])
-        attainable = {"tflops": c["tflops"], "ghz": c["ghz"],
-                      "frac": round(achieved / c["tflops"], 4), "shape": key.split("_")[1],
-                      "how": "the faster of register-only v_mfma_f32_32x32x16_f16 and "
-                             "v_mfma_f32_16x16x32_f16 streams on every CU, uniformly random fp16 "
-                             "operands, same run (bench.py --mfma-ceiling)"}
+    if p.ab in CEILING_TYPES and mfma_bound and not args.no_ceiling:
+        attainable = attainable_rate(p.ab, achieved)
 
     # MFMA-bound unless the arithmetic intensity (FLOP per algorithmic byte)
     # is under the ridge point peak / HBM bandwidth; then GB/s against HBM.

@@ -49,7 +49,8 @@ class gemm_epi_plan(ctypes.Structure):
                 ("threads", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("tiles", ctypes.c_int64), ("lds_bytes", ctypes.c_int32),
                 ("cus", ctypes.c_int32), ("splits", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_int64), ("name", ctypes.c_char * 64)]
+                ("workspace_bytes", ctypes.c_int64), ("split_tiles", ctypes.c_int64),
+                ("name", ctypes.c_char * 64)]
 
 
 class GemmEpiError(RuntimeError):
@@ -163,7 +164,7 @@ def gemm_epi_get_plan(h: int) -> dict:
     return {"variant": p.variant, "tile_m": p.tile_m, "tile_n": p.tile_n,
             "tile_k": p.tile_k, "threads": p.threads, "grid": p.grid,
             "tiles": p.tiles, "lds_bytes": p.lds_bytes, "cus": p.cus,
-            "splits": p.splits, "workspace_bytes": p.workspace_bytes,
+            "splits": p.splits, "workspace_bytes": p.workspace_bytes, "split_tiles": p.split_tiles,
             "name": p.name.decode()}
 
 

@@ -25,7 +25,8 @@ GEMM_EPI_PARTS = 16
 SOURCES = [MAIN_SOURCE, PART_SOURCE, SPLITK_SOURCE, PREP_SOURCE]
 HEADERS = [os.path.join(CSRC, "gemm_epi_kernel.hpp"), os.path.join(CSRC, "gemm_epi_launch.hpp"),
            os.path.join(CSRC, "gemm_epi_splitk.hpp"), os.path.join(CSRC, "gemm_epi_prep.hpp"),
-           os.path.join(CSRC, "gemm_epi_variants.inc"), os.path.join(ROOT, "include", "gemm_epi.h")]
+           os.path.join(CSRC, "gemm_epi_raster.hpp"), os.path.join(CSRC, "gemm_epi_variants.inc"),
+           os.path.join(ROOT, "include", "gemm_epi.h")]
 # measurement tool used by bench.py --mfma-ceiling (not part of the GEMM path)
 CEILING_LIB = os.path.join(HERE, "libmfma_ceiling.so")
 CEILING_SOURCE = os.path.join(CSRC, "mfma_ceiling.hip")
@@ -98,7 +99,7 @@ def build(verbose: bool = False, extra=(), only=None, cache_dir=None) -> str:
         objdir = cache_dir or tmp
         os.makedirs(objdir, exist_ok=True)
         kernel_deps = [os.path.join(CSRC, f) for f in ("gemm_epi_kernel.hpp", "gemm_epi_launch.hpp",
-                                                        "gemm_epi_variants.inc")]
+                                                        "gemm_epi_raster.hpp", "gemm_epi_variants.inc")]
 
         def obj(name, source, deps, defines=()):
             out = os.path.join(objdir, name)
@@ -110,7 +111,8 @@ def build(verbose: bool = False, extra=(), only=None, cache_dir=None) -> str:
         units = [obj("part%d.o" % k, PART_SOURCE, kernel_deps, ["-DGEMM_EPI_PART=%d" % k])
                  for k in range(GEMM_EPI_PARTS)]
         units += [obj("main.o", MAIN_SOURCE, HEADERS),
-                  obj("splitk.o", SPLITK_SOURCE, [os.path.join(CSRC, "gemm_epi_splitk.hpp")]),
+                  obj("splitk.o", SPLITK_SOURCE, [os.path.join(CSRC, "gemm_epi_splitk.hpp"),
+                                                  os.path.join(CSRC, "gemm_epi_raster.hpp")]),
                   obj("prep.o", PREP_SOURCE, [os.path.join(CSRC, "gemm_epi_prep.hpp")])]
         jobs = [cmd for _, cmd in units if cmd]
         ceil_tmp = CEILING_LIB + ".tmp%d" % os.getpid()

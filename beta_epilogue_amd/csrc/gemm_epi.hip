@@ -132,8 +132,10 @@ struct gemm_epi_handle {
   int device;
   int64_t tiles_m, tiles_n, tiles;  // output tiles (one K slice)
   int group_m;
-  int splits;                       // K slices (1: no split)
+  int splits;                       // K slices of a split tile (1: no split)
   int64_t kslice;                   // K elements per slice
+  int64_t dp_tiles, tail_tiles;     // whole tiles first, then the split ones
+  int64_t items;                    // work items: dp_tiles + tail_tiles * splits
   int64_t ws_bytes;                 // workspace: split-K partial sums, then the prepared operands
   bool widen;                       // fp8 A/B run as fp16 copies
   int64_t prep_off;                 // the prepared operands (uint8 sums and copies, fp16 copies)
@@ -335,34 +337,71 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   h->tiles_n = (desc->N + v.bn - 1) / v.bn;
   h->tiles = h->tiles_m * h->tiles_n * desc->L;
   h->group_m = 4;
-  // Split K when the output tiles cannot fill half of the compute units and
-  // K is long: each slice gets at least four K tiles, at most 16 slices.
+  // Split K.  The library's choice (desc->splits == 0): when the last round
+  // of tiles (tiles % cus of them, all tiles when there are fewer than the
+  // compute units) would leave at least half of the compute units idle, those
+  // tiles may run in S K slices after whole-K rounds of the others.  S (2 ..
+  // min(cus / last, K tiles / 4, 16)) maximises the time saved in the last
+  // round, (K tiles - ceil(K tiles / S)) * 1.1 us, less the reduction
+  // kernel's cost, 4 us + (S slots of partial sums + C, X, D, Y per split
+  // tile) / 5 TB/s: a model fitted to MI355X runs of 256x256 tiles with 16 to
+  // 128 K tiles; no S with a positive balance, no split.  desc->splits >= 2
+  // splits every tile into that many slices.
   const int64_t ktiles = (desc->K + v.bk - 1) / v.bk;
-  int64_t splits = 1;
+  int64_t splits = 1, tail = 0;
   const bool u8 = desc->ab_dtype == GEMM_EPI_U8;
   if (u8) {
     splits = 1;  // the uint8 correction starts the accumulator of the whole K range
   } else if (desc->splits >= 1) {
     splits = std::min<int64_t>(desc->splits, ktiles);
-  } else if (h->tiles * 2 <= h->cus && ktiles >= 8) {
-    splits = std::min<int64_t>(std::min<int64_t>(h->cus / h->tiles, ktiles / 4), 16);
+    tail = h->tiles;
+  } else {
+    const int64_t last = h->tiles % h->cus;  // tiles of the partial last round
+    if (last > 0 && last * 2 <= h->cus) {
+      const double slot_bytes = 4.0 * v.bm * v.bn;
+      double epi_bytes = 0.0;
+      for (int t : {desc->c_dtype, desc->x_dtype, desc->d_dtype, desc->y_dtype})
+        if (t != GEMM_EPI_NONE) epi_bytes += (double)elem_bytes(t) * v.bm * v.bn;
+      const int64_t smax = std::min<int64_t>(std::min<int64_t>(h->cus / last, ktiles / 4), 16);
+      double best = 0.0;
+      for (int64_t s = 2; s <= smax; ++s) {
+        const double saved_us = (double)(ktiles - (ktiles + s - 1) / s) * 1.1;
+        const double cost_us = 4.0 + (double)last * (s * slot_bytes + epi_bytes) / 5.0e6;
+        if (saved_us - cost_us > best) {
+          best = saved_us - cost_us;
+          splits = s;
+        }
+      }
+      if (splits > 1) tail = last;
+    }
   }
   if (splits < 1) splits = 1;
   h->kslice = ((ktiles + splits - 1) / splits) * v.bk;
   h->splits = (int)((desc->K + h->kslice - 1) / h->kslice);
-  if (h->splits == 1) h->kslice = desc->K;
+  if (h->splits == 1) {
+    h->kslice = desc->K;
+    tail = 0;
+  }
+  h->tail_tiles = tail;
+  h->dp_tiles = h->tiles - tail;
   // Workspace: the split-K partial sums, then (at a 256-byte boundary) the
   // prepared operands: for uint8 the row sums of A, the column sums of B and
   // the flipped copies of A and B, for widened fp8 the fp16 copies of A and
   // B (each part at a 256-byte boundary).
   h->widen = widened(desc);
-  h->ws_bytes = h->splits > 1 ? (int64_t)h->splits * desc->L * desc->M * desc->N * 4 : 0;
+  h->ws_bytes = h->splits > 1 ? (int64_t)h->splits * h->tail_tiles * v.bm * v.bn * 4 : 0;
   h->prep_off = (h->ws_bytes + 255) / 256 * 256;
   if (u8) h->ws_bytes = h->prep_off + u8_layout(desc, nullptr, nullptr, nullptr);
   if (h->widen)
     h->ws_bytes = h->prep_off + (desc->L * desc->M * desc->K * 2 + 255) / 256 * 256 +
                   (desc->L * desc->N * desc->K * 2 + 255) / 256 * 256;
-  h->grid = (int)std::min<int64_t>(h->tiles * h->splits, (int64_t)h->cus);  // one workgroup per CU
+  h->items = h->dp_tiles + h->tail_tiles * h->splits;
+  if (h->items >= ((int64_t)1 << 31)) {
+    delete h;
+    return fail(GEMM_EPI_ERR_UNSUPPORTED, "%lld work items (tiles times K slices): at most 2^31 - 1",
+                (long long)(h->tiles - tail + tail * splits));
+  }
+  h->grid = (int)std::min<int64_t>(h->items, (int64_t)h->cus);  // one workgroup per CU
   if (scratch_address(dev, &h->ws_static) != GEMM_EPI_OK) {
     delete h;
     return GEMM_EPI_ERR_DEVICE;
@@ -422,7 +461,7 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
   p.M = d.M;
   p.N = d.N;
   p.K = d.K;
-  p.tiles_total = h->tiles * h->splits;
+  p.tiles_total = (int32_t)h->items;
   p.L = (int32_t)d.L;
   p.tiles_m = (int32_t)h->tiles_m;
   p.tiles_n = (int32_t)h->tiles_n;
@@ -445,6 +484,8 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
   for (int t : {use_c ? d.c_dtype : 0, use_x ? d.x_dtype : 0, d.y_dtype})
     if (t != GEMM_EPI_NONE && t != kind) kind = 0;
   p.epi_kind = kind;
+  p.dp_tiles = (int32_t)h->dp_tiles;
+  p.tail_tiles = (int32_t)h->tail_tiles;
   p.splits = h->splits;
   p.kslice = h->kslice;
   p.ws = nullptr;
@@ -516,7 +557,16 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
     q.X = p.X;
     q.D = D;
     q.Y = Y;
-    q.groups = d.L * d.M * d.N / 4;
+    q.M = d.M;
+    q.N = d.N;
+    q.dp_tiles = (int32_t)h->dp_tiles;
+    q.tail_tiles = (int32_t)h->tail_tiles;
+    q.tiles_m = (int32_t)h->tiles_m;
+    q.tiles_n = (int32_t)h->tiles_n;
+    q.group_m = h->group_m;
+    q.tile_m = kVariants[h->variant].bm;
+    q.tile_n = kVariants[h->variant].bn;
+    q.cd_nmajor = d.cd_major == GEMM_EPI_MAJOR_N ? 1 : 0;
     q.splits = h->splits;
     q.c_dtype = p.c_dtype;
     q.x_dtype = p.x_dtype;
@@ -530,7 +580,7 @@ static int run_impl(const gemm_epi_handle* hc, const void* A, const void* B, con
     q.ibeta = p.ibeta;
     q.ix = p.ix;
     q.relu = p.relu;
-    const int64_t blocks = (q.groups + 255) / 256;
+    const int64_t blocks = (h->tail_tiles * q.tile_m * q.tile_n / 4 + 255) / 256;
     gemm_epi::launch_splitk_epilogue(q, (int)std::min<int64_t>(blocks, (int64_t)h->cus * 8), (hipStream_t)stream);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(GEMM_EPI_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
@@ -571,6 +621,7 @@ extern "C" int gemm_epi_get_plan(const gemm_epi_handle* h, gemm_epi_plan* out) {
   out->cus = h->cus;
   out->splits = h->splits;
   out->workspace_bytes = h->ws_bytes;
+  out->split_tiles = h->splits > 1 ? h->tail_tiles : 0;
   std::snprintf(out->name, sizeof out->name, "%s", v.name);
   return GEMM_EPI_OK;
 }

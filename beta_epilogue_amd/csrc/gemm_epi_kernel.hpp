@@ -10,31 +10,38 @@
 //     the A row panels and B column panels of concurrently running tiles in
 //     that XCD's L2 (the persistent tile loop of the Blackwell pipeline API
 //     card, "Device side", made XCD-aware);
-//   * global -> LDS staging into a STAGES-deep ring: each LDS row holds ROWB
-//     bytes of K of one tile row as 16-byte chunks stored at chunk ^ swz(row)
-//     so that the MFMA fragment reads of 16 consecutive rows hit 16 distinct
-//     16-byte bank groups of the 64-bank LDS.  K-major operands go straight
-//     to LDS with buffer_load_dwordx4 ... lds (the buffer's range check turns
-//     rows past M/N and chunks past K into zeros); M-major int8 A is loaded
-//     to registers, transposed 8x8 bytes with v_perm and written with
-//     ds_write_b64.  Each K tile waits only for its own stage (counted
-//     vmcnt), so STAGES-1 tiles stay in flight (the multi-stage pipeline of
-//     the API card's "Depth and shared memory");
-//   * MFMA mainloop: v_mfma_f32_32x32x16_{f16,bf16}, v_mfma_f32_32x32x64_f8f6f4
-//     (e4m3 x e4m3) or v_mfma_i32_32x32x32_i8 on 32x32 accumulator blocks in
-//     AGPRs; the fragments of k step s+1 are read while step s multiplies;
+//   * global -> LDS staging into a STAGES-deep ring by buffer_load_dwordx4
+//     ... lds (the buffer's range check turns rows past M/N and chunks past K
+//     into zeros).  K-major operands: each LDS row holds ROWB bytes of K of
+//     one tile row as 16-byte chunks stored at chunk ^ swz(row), so the
+//     MFMA fragment reads of 16 consecutive rows hit 16 distinct 16-byte
+//     bank groups of the 64-bank LDS.  M-major A / N-major B: swizzled
+//     k-rows, read back with the transposing ds_read_b64_tr_b16/_tr_b8.
+//     Each K tile waits only for its own stage (counted vmcnt), so STAGES-1
+//     tiles stay in flight (the multi-stage pipeline of the API card's
+//     "Depth and shared memory");
+//   * MFMA mainloop on 16x16 or 32x32 accumulator blocks in AGPRs:
+//     v_mfma_f32_{16x16x32,32x32x16}_{f16,bf16},
+//     v_mfma_scale_f32_{16x16x128,32x32x64}_f8f6f4 (per-operand fp8 format
+//     selectors, scales fixed at 1) or v_mfma_i32_{16x16x64,32x32x32}_i8;
+//     the fragments of k step s+1 are read while step s multiplies;
 //   * fused epilogue on the fp32 (int32) accumulator: Y = acc, D = alpha*acc
 //     + beta*C + x_factor*X, rounded to nearest-even into the output types;
 //     each 32-wide block of the accumulator is re-laid out through a small
-//     per-wave LDS region so C/X loads and D/Y stores move 4 contiguous
-//     elements per lane; all loads of an element precede its stores (the
-//     example's epilogue comment) and C and X are only read.
+//     per-wave LDS region so C/X loads and D/Y stores move 16 contiguous
+//     bytes per lane; all loads of an element precede its stores (the
+//     example's epilogue comment) and C and X are only read;
+//   * split K: a work item is a whole tile, or one K slice of a tile whose
+//     fp32 (int32) partial sums go to a workspace slot; a second kernel adds
+//     the slices and applies the epilogue (gemm_epi_splitk.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <type_traits>
+
+#include "gemm_epi_raster.hpp"
 
 namespace gemm_epi {
 
@@ -70,7 +77,7 @@ struct Params {
   void* D;
   void* Y;        // NULL when Y is not written
   int64_t M, N, K;
-  int64_t tiles_total;
+  int32_t tiles_total;  // work items (below 2^31)
   int32_t L, tiles_m, tiles_n, group_m;
   int32_t c_dtype, x_dtype, d_dtype, y_dtype;  // T_NONE for skipped terms
   float alpha, beta, xf;
@@ -78,11 +85,17 @@ struct Params {
   int32_t xcd_remap;          // grid is a multiple of 8: remap ids per XCD
   int32_t epi_kind;           // element type shared by every C/X/D/Y in use (0: mixed)
   int32_t relu;               // D = max(0, alpha*acc + beta*C) + x_factor*X
-  // Split K: the K range is cut into `splits` slices of kslice elements (a
-  // multiple of the K tile; the last one may be shorter).  With splits > 1 a
-  // tile of slice s writes its fp32 (int32) partial sums to ws + s * L*M*N
-  // (D's layout) instead of running the epilogue; a second kernel adds the
-  // slices and applies the epilogue.  splits == 1: kslice == K, ws unused.
+  // Split K.  Work items 0 .. dp_tiles-1 are the first dp_tiles tiles of
+  // the raster, each over the whole K range with the epilogue.  The other
+  // tail_tiles tiles are cut into `splits` K slices of kslice elements (a
+  // multiple of the K tile; the last one may be shorter): item dp_tiles +
+  // s*tail_tiles + j is slice s of tile dp_tiles + j, and it writes its fp32
+  // (int32) partial sums, unscaled, to workspace slot s*tail_tiles + j
+  // (tile_m*tile_n*4 bytes at ws + slot*tile_m*tile_n*4, holding the tile's
+  // rows x cols inside the matrix packed in D's majorness) instead of running
+  // the epilogue; a second kernel adds the slices and applies the epilogue.
+  // No split: dp_tiles == all tiles, tail_tiles == 0, ws unused.
+  int32_t dp_tiles, tail_tiles;
   int32_t splits;
   int64_t kslice;
   void* ws;
@@ -954,9 +967,6 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
   const int bid = blockIdx.x;
   const int g = p.xcd_remap ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
 
-  const int64_t tiles_mn = (int64_t)p.tiles_m * p.tiles_n;
-  const int64_t tiles_split = (int64_t)p.L * tiles_mn;  // tiles of one K slice
-
   using OpA = Operand<CF, BM, CF::WM, CF::A_KMAJOR>;
   using OpB = Operand<CF, BN, CF::WN, CF::B_KMAJOR>;
   // DMA instructions per wave per stage (for the counted waits)
@@ -972,23 +982,21 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
   opb.setup_reader(wn * CF::WN, lane);
   using raw_t = typename CF::RAW;
 
-  for (int64_t t = g; t < p.tiles_total; t += G) {
-    // ---- tile coordinates: K slice, batch, grouped raster inside a batch ---
-    const int split = (int)(t / tiles_split);
-    const int64_t ts = t - (int64_t)split * tiles_split;
-    const int l = (int)(ts / tiles_mn);
-    const int64_t r = ts - (int64_t)l * tiles_mn;
-    const int64_t kbeg = (int64_t)split * p.kslice;
-    const int64_t kbytes = min(p.K - kbeg, p.kslice) * ES;  // this slice's K, in bytes
+  for (int t = g; t < p.tiles_total; t += G) {
+    // ---- work item: a whole tile, or K slice `split` of tile ts ----------
+    int split = -1;  // whole K range, epilogue here
+    int ts = t;
+    if (t >= p.dp_tiles) {
+      const int u = t - p.dp_tiles;  // the item's workspace slot
+      split = (int)((unsigned)u / (unsigned)p.tail_tiles);
+      ts = p.dp_tiles + (u - split * p.tail_tiles);
+    }
+    const TileRC tc = raster_tile(ts, p.tiles_m, p.tiles_n, p.group_m);
+    const int l = tc.l;
+    const int64_t kbeg = split > 0 ? (int64_t)split * p.kslice : 0;
+    const int64_t kbytes = (split < 0 ? p.K : min(p.K - kbeg, p.kslice)) * ES;  // this item's K, in bytes
     const int KT = (int)((kbytes + CF::ROWB - 1) / CF::ROWB);
-    const int64_t gsize = (int64_t)p.group_m * p.tiles_n;
-    const int gid = (int)(r / gsize);
-    const int first_m = gid * p.group_m;
-    const int gm = min(p.tiles_m - first_m, p.group_m);
-    const int within = (int)(r - (int64_t)gid * gsize);
-    const int tm = first_m + within % gm;
-    const int tn = within / gm;
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = tc.tm * BM, n0 = tc.tn * BN;
 
     // ---- staging set-up --------------------------------------------------
     opa.setup((const char*)p.A + (int64_t)l * p.M * p.K * ES, p.M, p.K, kbeg, m0, wave, lane);
@@ -1201,10 +1209,14 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
     // otherwise (bf16 included) the mixed-type one (4 elements per lane).
     constexpr bool NM = CF::CD_NMAJOR;
     const int emw = m0 + wm * CF::WM, enw = n0 + wn * CF::WN;
-    if (p.splits > 1) {
-      // a K slice: its partial sums, unscaled, into the slice's workspace
+    if (t >= p.dp_tiles) {
+      // a K slice: its partial sums, unscaled, into its workspace slot, as a
+      // rows x cols matrix of its own (the tile's part inside the matrix)
       Params q = p;
-      q.D = (char*)p.ws + (int64_t)split * p.L * p.M * p.N * 4;
+      q.D = (char*)p.ws + (int64_t)(t - p.dp_tiles) * (BM * BN * 4);
+      q.M = min(p.M - m0, (int64_t)BM);
+      q.N = min(p.N - n0, (int64_t)BN);
+      q.L = 1;
       q.C = q.X = nullptr;
       q.Y = nullptr;
       q.alpha = 1.0f;
@@ -1212,8 +1224,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_epi_kernel(Params p) {
       q.ialpha = 1;
       q.ibeta = q.ix = 0;
       q.relu = 0;
-      if constexpr (CF::INT) epilogue_typed<CF, NM, T_I32, true>(q, acc, lds, wave, lane, l, emw, enw);
-      else epilogue_typed<CF, NM, T_F32>(q, acc, lds, wave, lane, l, emw, enw);
+      if constexpr (CF::INT) epilogue_typed<CF, NM, T_I32, true>(q, acc, lds, wave, lane, 0, emw - m0, enw - n0);
+      else epilogue_typed<CF, NM, T_F32>(q, acc, lds, wave, lane, 0, emw - m0, enw - n0);
     } else if constexpr (CF::INT) {
       if (p.int_unit) epilogue_typed<CF, NM, T_I32, true>(p, acc, lds, wave, lane, l, emw, enw);
       else epilogue_typed<CF, NM, T_I32, false>(p, acc, lds, wave, lane, l, emw, enw);

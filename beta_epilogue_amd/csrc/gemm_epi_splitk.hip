@@ -1,21 +1,23 @@
 // gemm_epi_splitk.hip -- the second kernel of a split-K launch: adds the K
-// slices' partial sums and applies the fused epilogue.
+// slices' partial sums of the split tiles and applies the fused epilogue.
 //
-// With split K, slice s of the GEMM writes its fp32 (int32 for int8 inputs)
-// partial accumulator for every output to ws + s * L*M*N, in D's layout.  The
+// Slice s of split tile dp_tiles + j wrote its fp32 (int32 for int8 inputs)
+// partial accumulator to workspace slot s*tail_tiles + j: the tile's
+// rows x cols part inside the matrix, packed in D's majorness.  The
 // accumulator of an output is the sum of its slices (fp32 sums in slice
 // order; int32 sums wrap, so they are exact whenever the result fits), and
 // the epilogue is the one the GEMM kernel applies otherwise (CuTe DSL
 // example custom_epilogue_dense_gemm.py, module docstring and its epilogue
 // function):
 //   Y = acc,  D = alpha*acc + beta*C + x_factor*X   (or the clamped form)
-// C, X, D, Y and ws share one packed layout, so output element i of every
-// array is element i of the flat range.  Each thread takes four consecutive
-// elements: 16 bytes of every slice, 8 or 16 bytes of C, X, D, Y.  The flat
-// length is a multiple of 4 (the 16-byte rule on the contiguous extent).
+// Each thread takes four consecutive elements along the contiguous dimension:
+// 16 bytes of every slice, 8 or 16 bytes of C, X, D, Y.  The contiguous
+// extent is a multiple of 4 elements (the 16-byte rule) and tiles start at
+// multiples of 4, so a group of four lies in the matrix or wholly outside.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_epi_raster.hpp"
 #include "gemm_epi_splitk.hpp"
 
 namespace gemm_epi {
@@ -59,23 +61,42 @@ __device__ __forceinline__ void st4(void* base, int dt, int64_t i, v4f_t v) {
 }
 
 __global__ __launch_bounds__(256) void splitk_epilogue_kernel(SplitkParams p) {
+  const int64_t per_tile = (int64_t)p.tile_m * p.tile_n / 4;  // groups of a slot
+  const int64_t groups = (int64_t)p.tail_tiles * per_tile;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < p.groups; g += stride) {
-    const int64_t i = g * 4;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < groups; q += stride) {
+    const int j = (int)(q / per_tile);
+    const int g = (int)(q - (int64_t)j * per_tile);
+    const TileRC tc = raster_tile(p.dp_tiles + j, p.tiles_m, p.tiles_n, p.group_m);
+    const int64_t m0 = (int64_t)tc.tm * p.tile_m, n0 = (int64_t)tc.tn * p.tile_n;
+    const int rows = (int)min(p.M - m0, (int64_t)p.tile_m), cols = (int)min(p.N - n0, (int64_t)p.tile_n);
+    // line (a row if N-major, a column if M-major) and position along it
+    const int along_len = p.cd_nmajor ? cols : rows, lines = p.cd_nmajor ? rows : cols;
+    const int per_line = (p.cd_nmajor ? p.tile_n : p.tile_m) / 4;
+    const int line = g / per_line, pos = (g - line * per_line) * 4;
+    if (line >= lines || pos >= along_len) continue;
+    const int64_t e = (int64_t)line * along_len + pos;  // element of the slot
+    const int64_t i = (int64_t)tc.l * p.M * p.N +
+                      (p.cd_nmajor ? (m0 + line) * p.N + n0 + pos : (n0 + line) * p.M + m0 + pos);
+    const int64_t slot_elems = (int64_t)p.tile_m * p.tile_n;
     if (p.int_path) {
-      v4u_t a = __builtin_nontemporal_load((const v4u_t*)p.ws + g);
-      for (int s = 1; s < p.splits; ++s) a += __builtin_nontemporal_load((const v4u_t*)p.ws + s * p.groups + g);
+      const uint32_t* w = (const uint32_t*)p.ws + (int64_t)j * slot_elems + e;
+      v4u_t a = __builtin_nontemporal_load((const v4u_t*)w);
+      for (int s = 1; s < p.splits; ++s)
+        a += __builtin_nontemporal_load((const v4u_t*)(w + (int64_t)s * p.tail_tiles * slot_elems));
       v4u_t t = a * (unsigned)p.ialpha;
       if (p.C) t += ld4(p.C, SK_I32, i) * (unsigned)p.ibeta;
       if (p.relu)
         t = v4u_t{(int)t.x > 0 ? t.x : 0u, (int)t.y > 0 ? t.y : 0u, (int)t.z > 0 ? t.z : 0u,
                   (int)t.w > 0 ? t.w : 0u};
       if (p.X) t += ld4(p.X, SK_I32, i) * (unsigned)p.ix;
-      __builtin_nontemporal_store(t, (v4u_t*)p.D + g);
-      if (p.Y) __builtin_nontemporal_store(a, (v4u_t*)p.Y + g);
+      __builtin_nontemporal_store(t, (v4u_t*)((uint32_t*)p.D + i));
+      if (p.Y) __builtin_nontemporal_store(a, (v4u_t*)((uint32_t*)p.Y + i));
     } else {
-      v4f_t a = __builtin_nontemporal_load((const v4f_t*)p.ws + g);
-      for (int s = 1; s < p.splits; ++s) a += __builtin_nontemporal_load((const v4f_t*)p.ws + s * p.groups + g);
+      const float* w = (const float*)p.ws + (int64_t)j * slot_elems + e;
+      v4f_t a = __builtin_nontemporal_load((const v4f_t*)w);
+      for (int s = 1; s < p.splits; ++s)
+        a += __builtin_nontemporal_load((const v4f_t*)(w + (int64_t)s * p.tail_tiles * slot_elems));
       // D = alpha * acc + beta * C (clamped at 0 in the ReLU form) + x_factor * X
       v4f_t t = a * p.alpha;
       if (p.C) {

@@ -99,10 +99,13 @@ typedef struct gemm_epi_desc {
   int32_t b_dtype;     /* NONE (0): B has ab_dtype.  Else the other fp8 format
                           for an fp8 ab_dtype: E4M3 x E5M2 or E5M2 x E4M3
                           (A's format x B's) */
-  int32_t splits;      /* K split: 0 = chosen by the library (split when the
-                          output tiles fill less than half of the GPU and K
-                          is long), 1 = never, n >= 2 = n slices (fewer if K
-                          has fewer K tiles) */
+  int32_t splits;      /* K split: 0 = chosen by the library (when K is
+                          long, the tiles of a last round that would leave
+                          at least half of the compute units idle run in K
+                          slices, after whole-K rounds of the other tiles;
+                          with few tiles that is all of them), 1 = never,
+                          n >= 2 = every tile in n slices (fewer if K has
+                          fewer K tiles) */
 } gemm_epi_desc;
 
 typedef struct gemm_epi_handle gemm_epi_handle;
@@ -116,12 +119,15 @@ typedef struct gemm_epi_plan {
   int64_t tiles;        /* L * ceil(M/tile_m) * ceil(N/tile_n) */
   int32_t lds_bytes;    /* LDS per workgroup */
   int32_t cus;          /* compute units of the device */
-  int32_t splits;       /* K slices (1: no split-K) */
+  int32_t splits;       /* K slices of a split tile (1: no split-K) */
   int64_t workspace_bytes; /* device workspace of a run (0 if none): split-K
-                              partial sums (splits * L*M*N * 4), then the
-                              uint8 sums and flipped copies (see gemm_epi_run)
-                              or the fp16 copies of widened fp8 operands (see
-                              gemm_epi_create) */
+                              partial sums (splits * split_tiles * tile_m *
+                              tile_n * 4), then the uint8 sums and flipped
+                              copies (see gemm_epi_run) or the fp16 copies of
+                              widened fp8 operands (see gemm_epi_create) */
+  int64_t split_tiles;  /* output tiles computed in K slices (0: none): the
+                           last tiles of the raster, after whole-K rounds of
+                           the others (all tiles when splits were asked for) */
   char name[64];        /* kernel variant name */
 } gemm_epi_plan;
 

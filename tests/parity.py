@@ -182,13 +182,13 @@ def flat_index(p: synth.Problem, pts):
     return l * p.M * p.N + n * p.M + m
 
 
-def parity_sampled(p: synth.Problem, variant=-1, n_random=2048, ins=None):
+def parity_sampled(p: synth.Problem, variant=-1, n_random=2048, ins=None, sub=128):
     """Full-size run, compared at sampled outputs the oracle computes one by
-    one (edge and middle rows/columns, a point in every quadrant of every
-    output tile, random points)."""
+    one (edge and middle rows/columns, a point in every sub x sub block of
+    every output tile, random points)."""
     ins = ins if ins is not None else synth.make_inputs(p)
     D, Y, plan = run_gpu(p, ins, variant)
-    pts = sample_points(p, n_random)
+    pts = sample_points(p, n_random, sub=sub)
     Dref, Yref, S = oracle.gemm_epi_points(
         p.M, p.N, p.K, p.L, ins["A"], ins["B"], ins["C"], ins["X"], points=pts,
         ab=p.ab, b=p.b_ab, c=p.c, x=p.x, a_major=p.a_major, b_major=p.b_major,

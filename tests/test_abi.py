@@ -33,7 +33,7 @@ def test_measurement_library_exports_its_declared_symbol():
     text = open(os.path.join(ROOT, "include", "mfma_ceiling.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(mfma_ceiling_\w+)\s*\(", text)))
-    assert names == ["mfma_ceiling_run"]
+    assert names == ["mfma_ceiling_run", "mfma_ceiling_run_type"]
     lib = ctypes.CDLL(os.path.join(ROOT, "beta_epilogue_amd", "libmfma_ceiling.so"))
     for n in names:
         assert hasattr(lib, n), "missing export " + n

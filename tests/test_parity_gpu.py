@@ -351,11 +351,12 @@ SPLITK = [
 def test_parity_split_k(p, splits):
     _say("case", p.name, p.M, p.N, p.K, p.L, "splits", splits)
     (ed, ey), plan = parity_full(p, exact=p.ab == "i8", splits=splits)
-    assert plan["splits"] == splits, plan
-    # the slices' partial sums, then (fp8 with fp32 outputs, widened) the fp16
-    # copies of A and B, each part at a 256-byte boundary
+    assert plan["splits"] == splits and plan["split_tiles"] == plan["tiles"], plan
+    # one tile-sized slot of partial sums per slice of every tile, then (fp8
+    # with fp32 outputs, widened) the fp16 copies of A and B, each part at a
+    # 256-byte boundary
     up = lambda x: (x + 255) // 256 * 256
-    ws = splits * p.L * p.M * p.N * 4
+    ws = splits * plan["tiles"] * plan["tile_m"] * plan["tile_n"] * 4
     if p.ab in ("e4m3", "e5m2") and "f32" in (p.d, p.y):
         ws = up(ws) + up(p.L * p.M * p.K * 2) + up(p.L * p.N * p.K * 2)
     assert plan["workspace_bytes"] == ws
@@ -368,14 +369,52 @@ def test_split_k_chosen_for_few_long_tiles():
     p = CFG[2].replace(name="splitk_auto_512", M=512, N=512, K=8192, seed=7360)
     _say("case", p.name)
     (ed, ey), plan = parity_full(p)
-    assert plan["splits"] == 16 and plan["grid"] == 64, plan
+    assert plan["splits"] == 16 and plan["grid"] == 64 and plan["split_tiles"] == 4, plan
     _say("  plan", plan["name"], "splits", plan["splits"], "err D %.3g Y %.3g" % (ed, ey))
 
 
 def test_split_k_not_chosen_when_tiles_fill_the_gpu():
     import beta_epilogue_amd as ge
     g = ge.FusedGemm(8192, 8192, 8192, ab="f16", c="f16", x="f16", d="f16", y="f16")
-    assert g.plan["splits"] == 1 and g.plan["workspace_bytes"] == 0
+    assert g.plan["splits"] == 1 and g.plan["workspace_bytes"] == 0 and g.plan["split_tiles"] == 0
+    g.close()
+
+
+# A last round of tiles that would leave most compute units idle: whole-K
+# rounds of the other tiles, then the last round's tiles in K slices (the
+# library's choice).  Ragged edges, both C/D majornesses, int8 exact, a
+# batched bf16 -> fp32 case.  Sampled parity with a point in every 32 x 32
+# block of every output tile (a slot added to the wrong tile or at a wrong
+# pitch fails), whole edge rows and columns, and random points.
+SPLIT_TAIL = [
+    CFG[2].replace(name="tail_f16_4100", M=4100, N=4104, K=4096, seed=7370),
+    CFG[3].replace(name="tail_i8_mmajorA_cdm", M=4112, N=4100, K=8192, L=1, cd_major="M", seed=7380),
+    CFG[1].replace(name="tail_bf16_f32_l2", M=2100, N=3848, K=4096, L=2, seed=7390),
+]
+
+
+@pytest.mark.parametrize("p", SPLIT_TAIL, ids=[e.name for e in SPLIT_TAIL])
+def test_parity_split_last_round(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L, p.cd_major)
+    (ed, ey), plan, npts = parity_sampled(p, sub=32)
+    cus = plan["cus"]
+    tail = plan["tiles"] % cus
+    ktiles = -(-p.K // plan["tile_k"])
+    s = plan["splits"]
+    assert plan["tiles"] > cus and 0 < tail <= cus // 2, plan
+    assert plan["split_tiles"] == tail and 2 <= s <= min(cus // tail, ktiles // 4, 16), plan
+    assert plan["grid"] == cus
+    assert plan["workspace_bytes"] == s * tail * plan["tile_m"] * plan["tile_n"] * 4
+    _say("  plan", plan["name"], "split tiles", tail, "splits", s, "points", npts,
+         "err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_split_not_chosen_for_a_short_last_round():
+    """The same last round with K = 512: slicing saves less than the
+    reduction kernel costs, so every tile runs whole."""
+    import beta_epilogue_amd as ge
+    g = ge.FusedGemm(4100, 4104, 512, ab="f16", c="f16", x="f16", d="f16", y="f16")
+    assert g.plan["splits"] == 1 and g.plan["split_tiles"] == 0 and g.plan["workspace_bytes"] == 0
     g.close()
 
 
