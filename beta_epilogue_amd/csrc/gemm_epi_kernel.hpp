@@ -727,58 +727,70 @@ __device__ __forceinline__ void epilogue_typed(const Params& p, const ACC (&acc)
 
   auto write_block = [&](auto blk_c) { epi_stage_block<CF, NMAJ>(acc, region, lane, decltype(blk_c)::value); };
 
-  v4u cr[DIST + 1], xr[DIST + 1];
-  static_for<0, DIST>([&](auto i_c) {
-    constexpr int i = decltype(i_c)::value;
-    cr[i] = epi_ld<T>(rc, off(i));
-    xr[i] = epi_ld<T>(rx, off(i));
-  });
-  static_for<0, NP>([&](auto i_c) {
-    constexpr int i = decltype(i_c)::value, S = i % (DIST + 1);
-    constexpr int blk = i / PASSES, ps = i % PASSES;
-    // this wave's reads of the previous block are issued before these
-    // writes, and LDS serves one wave's operations in order
-    if constexpr (ps == 0) write_block(IntC<blk>{});
-    const float* wp = region + (ps * LINES_PER_PASS + sub) * PITCH + e;
-    const v4f w0 = *(const v4f*)wp;
-    const v4f w1 = VEC == 8 ? *(const v4f*)(wp + 4) : v4f{};
-    if constexpr (i + DIST < NP) {
-      constexpr int SN = (i + DIST) % (DIST + 1);
-      cr[SN] = epi_ld<T>(rc, off(i + DIST));
-      xr[SN] = epi_ld<T>(rx, off(i + DIST));
-    }
-    const uint32_t o = off(i);
-    if constexpr (T == T_I32) {
-      const v4u a = __builtin_bit_cast(v4u, w0);
-      // UNIT: the scalars are 1 or their terms read zero (int_unit)
-      v4u t = UNIT ? a + cr[S] : a * (unsigned)p.ialpha + cr[S] * (unsigned)p.ibeta;
-      if (p.relu) t = relu4(t);
-      t += UNIT ? xr[S] : xr[S] * (unsigned)p.ix;
-      epi_st<T>(rd, o, t);
-      epi_st<T>(ry, o, a);
-    } else {
-      // D = alpha * acc + beta * C (clamped at 0 in the ReLU form) + x_factor * X,
-      // in this order
-      auto fin = [&](v4f w, int h) {
-        const v4f c = epi_dec<T>(cr[S], h), x = epi_dec<T>(xr[S], h);
-        v4f t = w * p.alpha;
-        t.x = __builtin_fmaf(beta, c.x, t.x);
-        t.y = __builtin_fmaf(beta, c.y, t.y);
-        t.z = __builtin_fmaf(beta, c.z, t.z);
-        t.w = __builtin_fmaf(beta, c.w, t.w);
+  // Absent arrays read as zero (C, X) or are not written (Y) through empty
+  // resources, except in the common form without X and Y: there the passes
+  // run in a copy that issues no X loads and no Y stores at all, since even
+  // accesses to an empty resource occupy the memory pipeline.  Both copies
+  // are free of branches.
+  auto passes = [&](auto xy_c) {
+    constexpr bool XY = decltype(xy_c)::value != 0;
+    v4u cr[DIST + 1], xr[DIST + 1];
+    static_for<0, DIST>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      cr[i] = epi_ld<T>(rc, off(i));
+      xr[i] = XY ? epi_ld<T>(rx, off(i)) : v4u{};
+    });
+    static_for<0, NP>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value, S = i % (DIST + 1);
+      constexpr int blk = i / PASSES, ps = i % PASSES;
+      // this wave's reads of the previous block are issued before these
+      // writes, and LDS serves one wave's operations in order
+      if constexpr (ps == 0) write_block(IntC<blk>{});
+      const float* wp = region + (ps * LINES_PER_PASS + sub) * PITCH + e;
+      const v4f w0 = *(const v4f*)wp;
+      const v4f w1 = VEC == 8 ? *(const v4f*)(wp + 4) : v4f{};
+      if constexpr (i + DIST < NP) {
+        constexpr int SN = (i + DIST) % (DIST + 1);
+        cr[SN] = epi_ld<T>(rc, off(i + DIST));
+        xr[SN] = XY ? epi_ld<T>(rx, off(i + DIST)) : v4u{};
+      }
+      const uint32_t o = off(i);
+      if constexpr (T == T_I32) {
+        const v4u a = __builtin_bit_cast(v4u, w0);
+        // UNIT: the scalars are 1 or their terms read zero (int_unit)
+        v4u t = UNIT ? a + cr[S] : a * (unsigned)p.ialpha + cr[S] * (unsigned)p.ibeta;
         if (p.relu) t = relu4(t);
-        t.x = __builtin_fmaf(xf, x.x, t.x);
-        t.y = __builtin_fmaf(xf, x.y, t.y);
-        t.z = __builtin_fmaf(xf, x.z, t.z);
-        t.w = __builtin_fmaf(xf, x.w, t.w);
-        return t;
-      };
-      const v4f d0 = fin(w0, 0);
-      const v4f d1 = VEC == 8 ? fin(w1, 1) : v4f{};
-      epi_st<T>(rd, o, epi_pack<T>(d0, d1));
-      epi_st<T>(ry, o, epi_pack<T>(w0, w1));
-    }
-  });
+        t += UNIT ? xr[S] : xr[S] * (unsigned)p.ix;
+        epi_st<T>(rd, o, t);
+        if constexpr (XY) epi_st<T>(ry, o, a);
+      } else {
+        // D = alpha * acc + beta * C (clamped at 0 in the ReLU form) + x_factor * X,
+        // in this order
+        auto fin = [&](v4f w, int h) {
+          const v4f c = epi_dec<T>(cr[S], h), x = epi_dec<T>(xr[S], h);
+          v4f t = w * p.alpha;
+          t.x = __builtin_fmaf(beta, c.x, t.x);
+          t.y = __builtin_fmaf(beta, c.y, t.y);
+          t.z = __builtin_fmaf(beta, c.z, t.z);
+          t.w = __builtin_fmaf(beta, c.w, t.w);
+          if (p.relu) t = relu4(t);
+          t.x = __builtin_fmaf(xf, x.x, t.x);
+          t.y = __builtin_fmaf(xf, x.y, t.y);
+          t.z = __builtin_fmaf(xf, x.z, t.z);
+          t.w = __builtin_fmaf(xf, x.w, t.w);
+          return t;
+        };
+        const v4f d0 = fin(w0, 0);
+        const v4f d1 = VEC == 8 ? fin(w1, 1) : v4f{};
+        epi_st<T>(rd, o, epi_pack<T>(d0, d1));
+        if constexpr (XY) epi_st<T>(ry, o, epi_pack<T>(w0, w1));
+      }
+      // passes stay in program order: each issues its loads DIST passes ahead
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  if (p.X || p.Y) passes(IntC<1>{});
+  else passes(IntC<0>{});
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
