@@ -39,6 +39,7 @@ def kernel_source_sha() -> str:
                 "beta_epilogue_amd/csrc/gemm_epi.hip",
                 "beta_epilogue_amd/csrc/gemm_epi_part.hip",
                 "beta_epilogue_amd/csrc/gemm_epi_launch.hpp",
+                "beta_epilogue_amd/csrc/gemm_epi_raster.hpp",
                 "beta_epilogue_amd/csrc/gemm_epi_variants.inc"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())

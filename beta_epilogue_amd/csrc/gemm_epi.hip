@@ -397,9 +397,9 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
                   (desc->L * desc->N * desc->K * 2 + 255) / 256 * 256;
   h->items = h->dp_tiles + h->tail_tiles * h->splits;
   if (h->items >= ((int64_t)1 << 31)) {
+    const long long items = (long long)h->items;
     delete h;
-    return fail(GEMM_EPI_ERR_UNSUPPORTED, "%lld work items (tiles times K slices): at most 2^31 - 1",
-                (long long)(h->tiles - tail + tail * splits));
+    return fail(GEMM_EPI_ERR_UNSUPPORTED, "%lld work items (tiles and K slices): at most 2^31 - 1", items);
   }
   h->grid = (int)std::min<int64_t>(h->items, (int64_t)h->cus);  // one workgroup per CU
   if (scratch_address(dev, &h->ws_static) != GEMM_EPI_OK) {

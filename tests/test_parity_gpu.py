@@ -409,6 +409,15 @@ def test_parity_split_last_round(p):
          "err D %.3g Y %.3g" % (ed, ey))
 
 
+def test_create_refuses_more_than_2_31_work_items():
+    """Tile and work-item numbers are 32-bit in the kernels: a plan of 2^31
+    or more work items is refused at create (no tensor is allocated)."""
+    import beta_epilogue_amd as ge
+    with pytest.raises(ge.GemmEpiError) as e:
+        ge.FusedGemm(1 << 19, 1 << 19, 64, 600, ab="f16", d="f16")
+    assert e.value.code == ge.GEMM_EPI_ERR_UNSUPPORTED and "work items" in str(e.value), str(e.value)
+
+
 def test_split_not_chosen_for_a_short_last_round():
     """The same last round with K = 512: slicing saves less than the
     reduction kernel costs, so every tile runs whole."""
