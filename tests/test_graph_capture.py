@@ -27,6 +27,9 @@ CASES = [
     # fp8 with an fp32 output: the widening passes, then the fp16 kernel
     (synth.CONFIGS[4].replace(name="graph_e4m3_f32", M=264, N=256, K=512, L=1, c="f32", d="f32",
                               seed=7630), 0),
+    # whole-K rounds, then the last round's tiles in K slices (289 tiles on 256 CUs)
+    (synth.CONFIGS[2].replace(name="graph_f16_split_last_round", M=4352, N=4352, K=4096, L=1,
+                              seed=7640), 0),
 ]
 
 
@@ -39,6 +42,8 @@ def test_run_static_replays_match_eager(p, splits):
     g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, a_major=p.a_major, b_major=p.b_major,
                      cd_major=p.cd_major, c=p.c, x=p.x, d=p.d, y=p.y, splits=splits)
     assert g.plan["workspace_bytes"] <= ge.GEMM_EPI_STATIC_SCRATCH_BYTES
+    if p.name.endswith("split_last_round"):
+        assert 0 < g.plan["split_tiles"] < g.plan["tiles"] and g.plan["splits"] > 1, g.plan
     shape = p.storage_shape("D")
 
     def outputs():
