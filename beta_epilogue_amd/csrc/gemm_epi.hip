@@ -281,6 +281,7 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   if (rc) return rc;
   if (variant < -1 || variant >= kNumVariants)
     return fail(GEMM_EPI_ERR_INVALID_ARG, "variant %d out of range", variant);
+  const bool auto_variant = variant == -1;
   if (variant == -1) {
     for (int i = 0; i < kNumVariants; ++i)
       if (variant_fits(kVariants[i], desc)) {
@@ -295,22 +296,22 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
     return fail(GEMM_EPI_ERR_UNSUPPORTED, "variant %s cannot run this problem",
                 kVariants[variant].name);
   }
-  const Variant& v = kVariants[variant];
+  const Variant* vp = &kVariants[variant];
   // Buffer offsets within one tile's rows are 32-bit (a widened fp8 operand
   // is read as its fp16 copy).
   const int es = widened(desc) ? 2 : elem_bytes(desc->ab_dtype);
-  if ((int64_t)v.bm * desc->K * es >= (int64_t(1) << 31) ||
-      (int64_t)v.bn * desc->K * es >= (int64_t(1) << 31))
+  if ((int64_t)vp->bm * desc->K * es >= (int64_t(1) << 31) ||
+      (int64_t)vp->bn * desc->K * es >= (int64_t(1) << 31))
     return fail(GEMM_EPI_ERR_UNSUPPORTED, "K too large for 32-bit tile offsets");
   // An M-major A or N-major B is addressed with 32-bit offsets over all of K.
-  const int64_t kpad = desc->K + 2 * (int64_t)v.bk;
+  const int64_t kpad = desc->K + 2 * (int64_t)vp->bk;
   if ((desc->a_major == GEMM_EPI_MAJOR_M && kpad * desc->M * es >= (int64_t(1) << 31)) ||
       (desc->b_major == GEMM_EPI_MAJOR_N && kpad * desc->N * es >= (int64_t(1) << 31)))
     return fail(GEMM_EPI_ERR_UNSUPPORTED, "M-major A / N-major B larger than 2 GiB per batch");
   // The epilogue addresses a wave's output lines (at most a tile's BM or BN
   // lines of the leading extent) with 31-bit byte offsets.
   const int64_t ld = desc->cd_major == GEMM_EPI_MAJOR_N ? desc->N : desc->M;
-  if ((int64_t)(v.bm > v.bn ? v.bm : v.bn) * ld * 4 >= (int64_t(1) << 31))
+  if ((int64_t)(vp->bm > vp->bn ? vp->bm : vp->bn) * ld * 4 >= (int64_t(1) << 31))
     return fail(GEMM_EPI_ERR_UNSUPPORTED, "leading extent %lld of C/X/D/Y too long for 31-bit offsets",
                 (long long)ld);
   // uint8: the row and column sums of a batch are addressed with 31-bit offsets.
@@ -327,6 +328,26 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
     return fail(GEMM_EPI_ERR_DEVICE, "device %d is %s, this library is built for gfx950", dev,
                 prop.gcnArchName);
 
+  // Small problems: when the default's tiles would fill at most a quarter of
+  // the compute units, a 128x128-tile variant of the same layout and type
+  // (if one is built) takes the problem: four times the tiles, so more of
+  // the GPU works, at about half the per-CU MFMA rate of the 256x256 tile.
+  // Measured on MI355X (fp16 with C, X, D, Y): 1024^3 88 -> 175, 2048^3
+  // 366 -> 582, 2048^2 x 512 165 -> 346, 1024^2 x 8192 428 -> 534 TFLOP/s;
+  // 3072^3 (144 tiles) stays faster with 256x256 tiles (767 against 609).
+  if (auto_variant) {
+    const int64_t tiles_default =
+        ((desc->M + vp->bm - 1) / vp->bm) * ((desc->N + vp->bn - 1) / vp->bn) * desc->L;
+    if (tiles_default * 4 <= prop.multiProcessorCount)
+      for (int i = 0; i < kNumVariants; ++i)
+        if (kVariants[i].bm == 128 && kVariants[i].bn == 128 && variant_fits(kVariants[i], desc)) {
+          variant = i;
+          vp = &kVariants[i];
+          break;
+        }
+  }
+  const Variant& v = *vp;
+
   gemm_epi_handle* h = new (std::nothrow) gemm_epi_handle;
   if (!h) return fail(GEMM_EPI_ERR_HOST_ALLOC, "out of host memory");
   h->desc = *desc;
@@ -342,10 +363,11 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   // compute units) would leave at least half of the compute units idle, those
   // tiles may run in S K slices after whole-K rounds of the others.  S (2 ..
   // min(cus / last, K tiles / 4, 16)) maximises the time saved in the last
-  // round, (K tiles - ceil(K tiles / S)) * 1.1 us, less the reduction
-  // kernel's cost, 4 us + (S slots of partial sums + C, X, D, Y per split
-  // tile) / 5 TB/s: a model fitted to MI355X runs of 256x256 tiles with 16 to
-  // 128 K tiles; no S with a positive balance, no split.  desc->splits >= 2
+  // round, (K tiles - ceil(K tiles / S)) times a K tile's time (1.1 us for a
+  // 256x256 tile, 0.6 us for 128x128), less the reduction kernel's cost,
+  // 4 us + (S slots of partial sums + C, X, D, Y per split tile) / 5 TB/s: a
+  // model fitted to MI355X runs with 8 to 128 K tiles; no S with a positive
+  // balance, no split.  desc->splits >= 2
   // splits every tile into that many slices.
   const int64_t ktiles = (desc->K + v.bk - 1) / v.bk;
   int64_t splits = 1, tail = 0;
@@ -364,8 +386,10 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
         if (t != GEMM_EPI_NONE) epi_bytes += (double)elem_bytes(t) * v.bm * v.bn;
       const int64_t smax = std::min<int64_t>(std::min<int64_t>(h->cus / last, ktiles / 4), 16);
       double best = 0.0;
+      // one K tile of one tile: 1.1 us for 256x256, 0.6 us for 128x128
+      const double ktile_us = v.bm * v.bn >= 256 * 256 ? 1.1 : 0.6;
       for (int64_t s = 2; s <= smax; ++s) {
-        const double saved_us = (double)(ktiles - (ktiles + s - 1) / s) * 1.1;
+        const double saved_us = (double)(ktiles - (ktiles + s - 1) / s) * ktile_us;
         const double cost_us = 4.0 + (double)last * (s * slot_bytes + epi_bytes) / 5.0e6;
         if (saved_us - cost_us > best) {
           best = saved_us - cost_us;

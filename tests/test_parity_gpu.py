@@ -113,13 +113,15 @@ EDGE = [
 
 def test_general_epilogue_both_block_shapes_ragged_n():
     """Mixed C/X/D/Y types run the mixed-type epilogue on the 16x16-block
-    default and on a 32x32-block variant alike (N-major: 16x16; M-major
+    kernels (256x256 and the 128x128 tiles the plan takes for this small
+    problem) and on a 32x32-block variant alike (N-major: 16x16; M-major
     C/D: 32x32; forced 32x32 for f16 N-major): linear and ReLU forms, a
     ragged N tile, with and without Y, batched.  (M = 191, N = 344 with f32
     C and bf16 D/Y once gave wrong values with 16x16 blocks.)"""
     import beta_epilogue_amd as ge
     names = [ge.gemm_epi_variant_name(i) for i in range(ge.gemm_epi_variant_count())]
-    for cd, v in (("N", "bf16_kk_n_256x256_r128_w4_s2_b16"), ("M", "bf16_kk_m_256x256_r128_w4_s2_q2")):
+    for cd, v in (("N", "bf16_kk_n_256x256_r128_w4_s2_b16"), ("N", "bf16_kk_n_128x128_r128_w4_s2_b16"),
+                  ("M", "bf16_kk_m_256x256_r128_w4_s2_q2")):
         for epi in ("linear", "relu"):
             for y in (None, "bf16"):
                 p = CFG[1].replace(name="general_%s_%s_%s" % (v, epi, y), M=192 if cd == "M" else 191,
@@ -127,8 +129,15 @@ def test_general_epilogue_both_block_shapes_ragged_n():
                                    d="bf16" if y else "f32", x_factor=0.5, cd_major=cd,
                                    beta=-1.0 if epi == "relu" else 1.0, epilogue=epi, seed=7070)
                 _say("case", p.name)
-                _, plan = parity_full(p)
+                _, plan = parity_full(p, variant=names.index(v))
                 assert plan["name"] == v, plan["name"]
+    # the plan's own choice for this size: the 128x128 tiles (N-major), the
+    # 256x256 default (M-major C/D, no 128x128 kernel)
+    for cd, v in (("N", "bf16_kk_n_128x128_r128_w4_s2_b16"), ("M", "bf16_kk_m_256x256_r128_w4_s2_q2")):
+        p = CFG[1].replace(name="general_auto_" + cd, M=192, N=344, K=200, L=2, c="f32", x="bf16", y="bf16",
+                           d="bf16", x_factor=0.5, cd_major=cd, seed=7072)
+        _, plan = parity_full(p)
+        assert plan["name"] == v, plan["name"]
     v = "f16_kk_n_256x256_r128_w4_s2_q2"
     p = CFG[2].replace(name="general_" + v, M=191, N=344, K=200, L=2, c="f32", x="bf16",
                        y="f16", d="bf16", x_factor=0.5, seed=7071)
@@ -364,13 +373,48 @@ def test_parity_split_k(p, splits):
 
 
 def test_split_k_chosen_for_few_long_tiles():
-    """512 x 512 x 8192: four output tiles, so the library splits K (16
-    slices of eight K tiles) and fills the GPU; whole-output parity."""
+    """512 x 512 x 8192: sixteen 128x128 output tiles (four of 256x256), so
+    the library splits K (16 slices of eight K tiles) and fills the GPU;
+    whole-output parity."""
     p = CFG[2].replace(name="splitk_auto_512", M=512, N=512, K=8192, seed=7360)
     _say("case", p.name)
     (ed, ey), plan = parity_full(p)
-    assert plan["splits"] == 16 and plan["grid"] == 64 and plan["split_tiles"] == 4, plan
+    assert plan["tile_m"] == plan["tile_n"] == 128 and plan["tiles"] == 16, plan
+    assert plan["splits"] == 16 and plan["grid"] == 256 and plan["split_tiles"] == 16, plan
     _say("  plan", plan["name"], "splits", plan["splits"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+# Small problems: when 256x256 tiles would fill at most a quarter of the
+# compute units, the plan takes the 128x128-tile kernel of the layout
+# (K-major A and B, N-major C/D) where one is built.
+SMALL = [
+    CFG[2].replace(name="small_f16_cxdy", M=776, N=648, K=520, seed=7700),
+    CFG[1].replace(name="small_bf16_f32_l3", M=392, N=264, K=1032, L=3, seed=7710),
+    CFG[3].replace(name="small_i8_kk", M=520, N=392, K=1040, L=2, a_major="K", seed=7720),
+    CFG[4].replace(name="small_e4m3_f16", M=392, N=520, K=1056, seed=7730),
+    CFG[4].replace(name="small_e4m3_f32_widened", M=392, N=264, K=528, c="f32", d="f32", seed=7740),
+]
+
+
+@pytest.mark.parametrize("p", SMALL, ids=[e.name for e in SMALL])
+def test_parity_small_problem_tiles(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L)
+    (ed, ey), plan = parity_full(p, exact=p.ab == "i8")
+    assert plan["tile_m"] == plan["tile_n"] == 128 and "_128x128_" in plan["name"], plan
+    _say("  plan", plan["name"], "tiles", plan["tiles"], "splits", plan["splits"], "err D %.3g Y %.3g" % (ed, ey))
+
+
+def test_small_tiles_not_chosen_beyond_a_quarter_of_the_gpu():
+    import beta_epilogue_amd as ge
+    g = ge.FusedGemm(3072, 3072, 3072, ab="f16", c="f16", x="f16", d="f16", y="f16")
+    assert g.plan["tile_m"] == g.plan["tile_n"] == 256, g.plan  # 144 tiles of 256x256
+    g.close()
+    g = ge.FusedGemm(2048, 2048, 2048, ab="f16", c="f16", x="f16", d="f16", y="f16")
+    assert g.plan["tile_m"] == 128 and g.plan["tiles"] == 256, g.plan  # 64 tiles of 256x256
+    g.close()
+    g = ge.FusedGemm(512, 512, 512, ab="f16", d="f16", cd_major="M")
+    assert g.plan["tile_m"] == 256, g.plan  # no 128x128 kernel for M-major C/D
+    g.close()
 
 
 def test_split_k_not_chosen_when_tiles_fill_the_gpu():
