@@ -159,15 +159,19 @@ typedef struct gemm_epi_plan {
  * run first converts A and B to fp16 copies in the workspace (exact: every
  * e4m3 and e5m2 value is an fp16 value; L*M*K*2 and L*N*K*2 bytes, each at
  * a 256-byte boundary, after any split-K partial sums) and an fp16 kernel
- * of the layout runs on them (so the plan names an f16 variant).  Returns
- * GEMM_EPI_OK or an error code.
+ * of the layout runs on them (so the plan names an f16 variant).  The
+ * kernel is the layout's 256x256-tile variant, or, when its tiles would fill
+ * at most a quarter of the compute units, the layout's 128x128-tile variant
+ * where one is built (K-major A and B with N-major C/D: fp16, bf16, e4m3,
+ * int8).  A plan of 2^31 or more work items (tiles and K slices) is
+ * GEMM_EPI_ERR_UNSUPPORTED.  Returns GEMM_EPI_OK or an error code.
  */
 int gemm_epi_create(const gemm_epi_desc* desc, gemm_epi_handle** out);
 
 /*
  * As gemm_epi_create (same passages), but forces kernel variant `variant` (0 <=
- * variant < gemm_epi_variant_count()); -1 picks the default variant.  A
- * variant that cannot run the problem is GEMM_EPI_ERR_UNSUPPORTED.
+ * variant < gemm_epi_variant_count()); -1 picks the variant gemm_epi_create
+ * would.  A variant that cannot run the problem is GEMM_EPI_ERR_UNSUPPORTED.
  */
 int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
                             gemm_epi_handle** out);
