@@ -357,7 +357,11 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   h->tiles_m = (desc->M + v.bm - 1) / v.bm;
   h->tiles_n = (desc->N + v.bn - 1) / v.bn;
   h->tiles = h->tiles_m * h->tiles_n * desc->L;
-  h->group_m = 4;
+  // Grouped raster: a workgroup's XCD takes 32 consecutive tiles, group_m
+  // tile rows by 32 / group_m columns (4 x 8 or 8 x 4: 12 panels of A and B
+  // either way); with more than 32 tile columns 8 rows also keep a round of
+  // tiles nearer square (12288^3 fp16: +8 %; 8192^3 and narrower: equal).
+  h->group_m = h->tiles_n > 32 ? 8 : 4;
   // Split K.  The library's choice (desc->splits == 0): when the last round
   // of tiles (tiles % cus of them, all tiles when there are fewer than the
   // compute units) would leave at least half of the compute units idle, those
