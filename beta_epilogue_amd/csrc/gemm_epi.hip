@@ -272,6 +272,58 @@ static bool variant_fits(const Variant& v, const gemm_epi_desc* d) {
   return v.ab == (widened(d) ? gemm_epi::T_F16 : exact_ab(d));
 }
 
+// Plan cost model (measured on MI355X, fp16 with C, X, D, Y; times in us).
+// A K tile of one output tile takes 1.1 us with 256x256 tiles, three
+// quarters of that at 0.9 of the per-CU rate with 192x256 tiles, and 0.6 us
+// with 128x128 tiles (four wave tiles of 64x64 run at about half the per-CU
+// rate).  The split-K reduction costs 4 us plus its bytes (S partial-sum
+// slots and C, X, D, Y per split tile) at 5 TB/s.
+static double ktile_us(const Variant& v) {
+  if (v.bm == 256 && v.bn == 256) return 1.1;
+  if (v.bm == 192 && v.bn == 256) return 1.1 * 0.75 / 0.9;
+  return 0.6;
+}
+
+struct SplitChoice {
+  int64_t splits, tail;  // K slices of the split tiles (1: none), split tiles
+  double us;             // modelled time of the launch
+};
+
+// The library's split choice for variant v and the modelled time: when the
+// last round of tiles (tiles % cus, all of them with fewer tiles than CUs)
+// would leave at least half of the CUs idle, those tiles may run in S K
+// slices after whole-K rounds of the others; S (2 .. min(cus / last,
+// K tiles / 4, 16)) maximises the time saved in the last round,
+// (K tiles - ceil(K tiles / S)) K-tile times, less the reduction's cost; no S
+// with a positive balance, no split.
+static SplitChoice split_choice(const Variant& v, const gemm_epi_desc* d, int64_t cus) {
+  const int64_t tiles = ((d->M + v.bm - 1) / v.bm) * ((d->N + v.bn - 1) / v.bn) * d->L;
+  const int64_t ktiles = (d->K + v.bk - 1) / v.bk;
+  const double tk = ktile_us(v);
+  const int64_t last = tiles % cus;
+  SplitChoice c{1, 0, (double)((tiles + cus - 1) / cus) * ktiles * tk};
+  if (last == 0 || last * 2 > cus || d->ab_dtype == GEMM_EPI_U8) return c;
+  const double slot_bytes = 4.0 * v.bm * v.bn;
+  double epi_bytes = 0.0;
+  for (int t : {d->c_dtype, d->x_dtype, d->d_dtype, d->y_dtype})
+    if (t != GEMM_EPI_NONE) epi_bytes += (double)elem_bytes(t) * v.bm * v.bn;
+  const int64_t smax = std::min<int64_t>(std::min<int64_t>(cus / last, ktiles / 4), 16);
+  double best = 0.0;
+  for (int64_t s = 2; s <= smax; ++s) {
+    const double saved_us = (double)(ktiles - (ktiles + s - 1) / s) * tk;
+    const double cost_us = 4.0 + (double)last * (s * slot_bytes + epi_bytes) / 5.0e6;
+    if (saved_us - cost_us > best) {
+      best = saved_us - cost_us;
+      c.splits = s;
+    }
+  }
+  if (c.splits > 1) {
+    c.tail = last;
+    c.us -= best;
+  }
+  return c;
+}
+
 extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
                                        gemm_epi_handle** out) {
   g_last_error[0] = 0;
@@ -328,23 +380,33 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
     return fail(GEMM_EPI_ERR_DEVICE, "device %d is %s, this library is built for gfx950", dev,
                 prop.gcnArchName);
 
-  // Small problems: when the default's tiles would fill at most a quarter of
-  // the compute units, a 128x128-tile variant of the same layout and type
-  // (if one is built) takes the problem: four times the tiles, so more of
-  // the GPU works, at about half the per-CU MFMA rate of the 256x256 tile.
-  // Measured on MI355X (fp16 with C, X, D, Y): 1024^3 88 -> 175, 2048^3
-  // 366 -> 582, 2048^2 x 512 165 -> 346, 1024^2 x 8192 428 -> 534 TFLOP/s;
-  // 3072^3 (144 tiles) stays faster with 256x256 tiles (767 against 609).
-  if (auto_variant) {
+  // Tile shape (the library's choice, where the layout has the smaller
+  // kernels: K-major A and B, N-major C/D).  128x128 tiles when the
+  // 256x256 ones would fill at most a quarter of the CUs: four times the
+  // tiles at about half the per-CU rate (fp16 with C, X, D, Y, TFLOP/s:
+  // 1024^3 88 -> 193, 2048^3 366 -> 553, 2048^2 x 512 165 -> 346, 1024^2 x
+  // 8192 428 -> 534).  192x256 tiles when neither plan splits K, the
+  // 256x256 tiles leave a partial round and the cost model gives the
+  // 192x256 plan below 0.95 of the 256x256 one's time (3072^3 718 -> 854,
+  // 3072^2 x 8192 947 -> 1133, 2560^3; 4096^3, 3584^3 and 8192^3 keep
+  // 256x256).
+  auto find_tile = [&](int bm, int bn) {
+    for (int i = 0; i < kNumVariants; ++i)
+      if (kVariants[i].bm == bm && kVariants[i].bn == bn && variant_fits(kVariants[i], desc)) return i;
+    return -1;
+  };
+  if (auto_variant && desc->splits == 0) {
+    const int64_t cus = prop.multiProcessorCount;
     const int64_t tiles_default =
         ((desc->M + vp->bm - 1) / vp->bm) * ((desc->N + vp->bn - 1) / vp->bn) * desc->L;
-    if (tiles_default * 4 <= prop.multiProcessorCount)
-      for (int i = 0; i < kNumVariants; ++i)
-        if (kVariants[i].bm == 128 && kVariants[i].bn == 128 && variant_fits(kVariants[i], desc)) {
-          variant = i;
-          vp = &kVariants[i];
-          break;
-        }
+    const int small = find_tile(128, 128), mid = find_tile(192, 256);
+    if (small >= 0 && tiles_default * 4 <= cus) {
+      variant = small;
+    } else if (mid >= 0 && tiles_default % cus != 0) {
+      const SplitChoice d = split_choice(*vp, desc, cus), m = split_choice(kVariants[mid], desc, cus);
+      if (d.splits == 1 && m.splits == 1 && m.us < 0.95 * d.us) variant = mid;
+    }
+    vp = &kVariants[variant];
   }
   const Variant& v = *vp;
 
@@ -362,46 +424,21 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   // either way); with more than 32 tile columns 8 rows also keep a round of
   // tiles nearer square (12288^3 fp16: +8 %; 8192^3 and narrower: equal).
   h->group_m = h->tiles_n > 32 ? 8 : 4;
-  // Split K.  The library's choice (desc->splits == 0): when the last round
-  // of tiles (tiles % cus of them, all tiles when there are fewer than the
-  // compute units) would leave at least half of the compute units idle, those
-  // tiles may run in S K slices after whole-K rounds of the others.  S (2 ..
-  // min(cus / last, K tiles / 4, 16)) maximises the time saved in the last
-  // round, (K tiles - ceil(K tiles / S)) times a K tile's time (1.1 us for a
-  // 256x256 tile, 0.6 us for 128x128), less the reduction kernel's cost,
-  // 4 us + (S slots of partial sums + C, X, D, Y per split tile) / 5 TB/s: a
-  // model fitted to MI355X runs with 8 to 128 K tiles; no S with a positive
-  // balance, no split.  desc->splits >= 2
-  // splits every tile into that many slices.
+  // Split K: the library's choice (split_choice, desc->splits == 0); uint8
+  // never (its correction starts the accumulator of the whole K range);
+  // desc->splits >= 2 splits every tile into that many slices.
   const int64_t ktiles = (desc->K + v.bk - 1) / v.bk;
   int64_t splits = 1, tail = 0;
   const bool u8 = desc->ab_dtype == GEMM_EPI_U8;
   if (u8) {
-    splits = 1;  // the uint8 correction starts the accumulator of the whole K range
+    splits = 1;
   } else if (desc->splits >= 1) {
     splits = std::min<int64_t>(desc->splits, ktiles);
     tail = h->tiles;
   } else {
-    const int64_t last = h->tiles % h->cus;  // tiles of the partial last round
-    if (last > 0 && last * 2 <= h->cus) {
-      const double slot_bytes = 4.0 * v.bm * v.bn;
-      double epi_bytes = 0.0;
-      for (int t : {desc->c_dtype, desc->x_dtype, desc->d_dtype, desc->y_dtype})
-        if (t != GEMM_EPI_NONE) epi_bytes += (double)elem_bytes(t) * v.bm * v.bn;
-      const int64_t smax = std::min<int64_t>(std::min<int64_t>(h->cus / last, ktiles / 4), 16);
-      double best = 0.0;
-      // one K tile of one tile: 1.1 us for 256x256, 0.6 us for 128x128
-      const double ktile_us = v.bm * v.bn >= 256 * 256 ? 1.1 : 0.6;
-      for (int64_t s = 2; s <= smax; ++s) {
-        const double saved_us = (double)(ktiles - (ktiles + s - 1) / s) * ktile_us;
-        const double cost_us = 4.0 + (double)last * (s * slot_bytes + epi_bytes) / 5.0e6;
-        if (saved_us - cost_us > best) {
-          best = saved_us - cost_us;
-          splits = s;
-        }
-      }
-      if (splits > 1) tail = last;
-    }
+    const SplitChoice c = split_choice(v, desc, h->cus);
+    splits = c.splits;
+    tail = c.tail;
   }
   if (splits < 1) splits = 1;
   h->kslice = ((ktiles + splits - 1) / splits) * v.bk;

@@ -160,11 +160,13 @@ typedef struct gemm_epi_plan {
  * e4m3 and e5m2 value is an fp16 value; L*M*K*2 and L*N*K*2 bytes, each at
  * a 256-byte boundary, after any split-K partial sums) and an fp16 kernel
  * of the layout runs on them (so the plan names an f16 variant).  The
- * kernel is the layout's 256x256-tile variant, or, when its tiles would fill
- * at most a quarter of the compute units, the layout's 128x128-tile variant
- * where one is built (K-major A and B with N-major C/D: fp16, bf16, e4m3,
- * int8).  A plan of 2^31 or more work items (tiles and K slices) is
- * GEMM_EPI_ERR_UNSUPPORTED.  Returns GEMM_EPI_OK or an error code.
+ * kernel is the layout's 256x256-tile variant; with desc->splits == 0 and
+ * K-major A and B with N-major C/D, a smaller tile where built: 128x128
+ * (fp16, bf16, e4m3, int8) when the 256x256 tiles would fill at most a
+ * quarter of the compute units, 192x256 (fp16, bf16) when the 256x256 tiles
+ * leave a partial round that the 192x256 ones fill better.  A plan of 2^31
+ * or more work items (tiles and K slices) is GEMM_EPI_ERR_UNSUPPORTED.
+ * Returns GEMM_EPI_OK or an error code.
  */
 int gemm_epi_create(const gemm_epi_desc* desc, gemm_epi_handle** out);
 

@@ -404,10 +404,33 @@ def test_parity_small_problem_tiles(p):
     _say("  plan", plan["name"], "tiles", plan["tiles"], "splits", plan["splits"], "err D %.3g Y %.3g" % (ed, ey))
 
 
+# A partial last round more than half full (so not split) with 256x256
+# tiles: the plan takes 192x256 tiles where they fill the rounds better.
+PARTIAL_ROUND = [
+    CFG[2].replace(name="round_f16_3000", M=3000, N=3000, K=520, seed=7750),
+    CFG[1].replace(name="round_bf16_f32_3000x2960", M=3000, N=2960, K=1032, seed=7760),
+]
+
+
+@pytest.mark.parametrize("p", PARTIAL_ROUND, ids=[e.name for e in PARTIAL_ROUND])
+def test_parity_partial_round_tiles(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L)
+    (ed, ey), plan, npts = parity_sampled(p, sub=32)
+    assert plan["tile_m"] == 192 and plan["tile_n"] == 256 and plan["splits"] == 1, plan
+    assert plan["tiles"] == -(-p.M // 192) * -(-p.N // 256) * p.L
+    _say("  plan", plan["name"], "tiles", plan["tiles"], "points", npts, "err D %.3g Y %.3g" % (ed, ey))
+
+
 def test_small_tiles_not_chosen_beyond_a_quarter_of_the_gpu():
     import beta_epilogue_amd as ge
     g = ge.FusedGemm(3072, 3072, 3072, ab="f16", c="f16", x="f16", d="f16", y="f16")
-    assert g.plan["tile_m"] == g.plan["tile_n"] == 256, g.plan  # 144 tiles of 256x256
+    assert g.plan["tile_m"] == 192, g.plan  # 144 tiles of 256x256: 192 of 192x256
+    g.close()
+    g = ge.FusedGemm(4096, 4096, 4096, ab="f16", c="f16", x="f16", d="f16", y="f16")
+    assert g.plan["tile_m"] == g.plan["tile_n"] == 256, g.plan  # one whole round
+    g.close()
+    g = ge.FusedGemm(3584, 3584, 3584, ab="f16", c="f16", x="f16", d="f16", y="f16")
+    assert g.plan["tile_m"] == g.plan["tile_n"] == 256, g.plan  # 192x256: 266 tiles, a 10-tile round
     g.close()
     g = ge.FusedGemm(2048, 2048, 2048, ab="f16", c="f16", x="f16", d="f16", y="f16")
     assert g.plan["tile_m"] == 128 and g.plan["tiles"] == 256, g.plan  # 64 tiles of 256x256
