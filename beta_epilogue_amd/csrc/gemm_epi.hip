@@ -273,14 +273,15 @@ static bool variant_fits(const Variant& v, const gemm_epi_desc* d) {
 }
 
 // Plan cost model (measured on MI355X, fp16 with C, X, D, Y; times in us).
-// A K tile of one output tile takes 1.1 us with 256x256 tiles, three
-// quarters of that at 0.9 of the per-CU rate with 192x256 tiles, and 0.6 us
-// with 128x128 tiles (four wave tiles of 64x64 run at about half the per-CU
-// rate).  The split-K reduction costs 4 us plus its bytes (S partial-sum
-// slots and C, X, D, Y per split tile) at 5 TB/s.
+// A K tile of one output tile takes 1.1 us with 256x256 tiles; with the
+// smaller tiles their share of the work at a lower per-CU rate (192x256:
+// 0.75 at 0.9, 128x256: 0.5 at 0.67, 128x128: 0.25 at ~0.46).  The split-K
+// reduction costs 4 us plus its bytes (S partial-sum slots and C, X, D, Y
+// per split tile) at 5 TB/s.
 static double ktile_us(const Variant& v) {
   if (v.bm == 256 && v.bn == 256) return 1.1;
   if (v.bm == 192 && v.bn == 256) return 1.1 * 0.75 / 0.9;
+  if (v.bm == 128 && v.bn == 256) return 1.1 * 0.75;
   return 0.6;
 }
 
@@ -385,11 +386,11 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
   // 256x256 ones would fill at most a quarter of the CUs: four times the
   // tiles at about half the per-CU rate (fp16 with C, X, D, Y, TFLOP/s:
   // 1024^3 88 -> 193, 2048^3 366 -> 553, 2048^2 x 512 165 -> 346, 1024^2 x
-  // 8192 428 -> 534).  192x256 tiles when neither plan splits K, the
-  // 256x256 tiles leave a partial round and the cost model gives the
-  // 192x256 plan below 0.95 of the 256x256 one's time (3072^3 718 -> 854,
-  // 3072^2 x 8192 947 -> 1133, 2560^3; 4096^3, 3584^3 and 8192^3 keep
-  // 256x256).
+  // 8192 428 -> 534).  Otherwise, when the 256x256 tiles leave a partial
+  // round, the 192x256 or 128x256 plan with the lowest modelled time (its
+  // own split choice included) if below 0.95 of the 256x256 plan's (3072^3
+  // 718 -> 854 with 192x256, 2560^3 506 -> 675 and 2048 x 4096 x 4096
+  // 774 -> 970 with 128x256; 4096^3, 3584^3 and 8192^3 keep 256x256).
   auto find_tile = [&](int bm, int bn) {
     for (int i = 0; i < kNumVariants; ++i)
       if (kVariants[i].bm == bm && kVariants[i].bn == bn && variant_fits(kVariants[i], desc)) return i;
@@ -399,12 +400,19 @@ extern "C" int gemm_epi_create_variant(const gemm_epi_desc* desc, int variant,
     const int64_t cus = prop.multiProcessorCount;
     const int64_t tiles_default =
         ((desc->M + vp->bm - 1) / vp->bm) * ((desc->N + vp->bn - 1) / vp->bn) * desc->L;
-    const int small = find_tile(128, 128), mid = find_tile(192, 256);
+    const int small = find_tile(128, 128);
     if (small >= 0 && tiles_default * 4 <= cus) {
       variant = small;
-    } else if (mid >= 0 && tiles_default % cus != 0) {
-      const SplitChoice d = split_choice(*vp, desc, cus), m = split_choice(kVariants[mid], desc, cus);
-      if (d.splits == 1 && m.splits == 1 && m.us < 0.95 * d.us) variant = mid;
+    } else if (tiles_default % cus != 0) {
+      double best = 0.95 * split_choice(*vp, desc, cus).us;
+      for (const int cand : {find_tile(192, 256), find_tile(128, 256)}) {
+        if (cand < 0) continue;
+        const double t = split_choice(kVariants[cand], desc, cus).us;
+        if (t < best) {
+          best = t;
+          variant = cand;
+        }
+      }
     }
     vp = &kVariants[variant];
   }
