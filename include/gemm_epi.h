@@ -163,8 +163,9 @@ typedef struct gemm_epi_plan {
  * kernel is the layout's 256x256-tile variant; with desc->splits == 0 and
  * K-major A and B with N-major C/D, a smaller tile where built: 128x128
  * (fp16, bf16, e4m3, int8) when the 256x256 tiles would fill at most a
- * quarter of the compute units, 192x256 (fp16, bf16, e4m3, int8) when the
- * 256x256 tiles leave a partial round that the 192x256 ones fill better.  A plan of 2^31
+ * quarter of the compute units, 192x256 or 128x256 (fp16, bf16, e4m3,
+ * int8) when the 256x256 tiles leave a partial round that those fill
+ * better.  A plan of 2^31
  * or more work items (tiles and K slices) is GEMM_EPI_ERR_UNSUPPORTED.
  * Returns GEMM_EPI_OK or an error code.
  */
