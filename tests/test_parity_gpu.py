@@ -421,6 +421,24 @@ def test_parity_partial_round_tiles(p):
     _say("  plan", plan["name"], "tiles", plan["tiles"], "points", npts, "err D %.3g Y %.3g" % (ed, ey))
 
 
+# A partial round that 128x256 tiles fill in one round: fp16 with a ragged K
+# tail, int8 with K-major A and ragged M and N, e4m3.
+WIDE_TILE = [
+    CFG[2].replace(name="wide_f16_2560", M=2560, N=2560, K=1032, seed=7770),
+    CFG[3].replace(name="wide_i8_kk_2568x2544", M=2568, N=2544, K=2048, L=1, a_major="K", seed=7780),
+    CFG[4].replace(name="wide_e4m3_2552x2560", M=2552, N=2560, K=1024, seed=7790),
+]
+
+
+@pytest.mark.parametrize("p", WIDE_TILE, ids=[e.name for e in WIDE_TILE])
+def test_parity_wide_tiles(p):
+    _say("case", p.name, p.M, p.N, p.K, p.L)
+    (ed, ey), plan, npts = parity_sampled(p, sub=32)
+    assert plan["tile_m"] == 128 and plan["tile_n"] == 256, plan
+    assert plan["tiles"] == -(-p.M // 128) * -(-p.N // 256) * p.L
+    _say("  plan", plan["name"], "tiles", plan["tiles"], "points", npts, "err D %.3g Y %.3g" % (ed, ey))
+
+
 def test_small_tiles_not_chosen_beyond_a_quarter_of_the_gpu():
     import beta_epilogue_amd as ge
     g = ge.FusedGemm(3072, 3072, 3072, ab="f16", c="f16", x="f16", d="f16", y="f16")
