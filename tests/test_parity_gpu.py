@@ -62,6 +62,13 @@ def test_config0_bit_exact():
 
 
 EDGE = [
+    # 4-byte C/D without X and Y, lines 4 mod 8 elements long (each line
+    # ends half-way through a 32-byte group)
+    CFG[3].replace(name="i32_no_xy_n_4mod8", M=136, N=260, K=128, L=2, a_major="K", seed=6050),
+    CFG[3].replace(name="i32_no_xy_cdm_m_4mod8", M=260, N=136, K=128, L=1, a_major="K", cd_major="M",
+                   beta=-2.0, seed=6060),
+    CFG[1].replace(name="f32_no_xy_n_4mod8_relu", M=200, N=268, K=136, epilogue="relu", beta=-1.0, seed=6070),
+    CFG[1].replace(name="f32_no_xy_cdm_m_4mod8", M=268, N=200, K=136, cd_major="M", seed=6080),
     CFG[2].replace(name="one_row", M=1, N=8, K=8, L=1),
     CFG[2].replace(name="tiny_batched", M=3, N=16, K=24, L=3),
     CFG[2].replace(name="k_tail_only", M=256, N=256, K=72, L=1),
