@@ -155,6 +155,29 @@ def attainable_rate(ab: str, achieved: float):
                    "every CU, seeded random operands, same run (bench.py --mfma-ceiling)"}
 
 
+def attainable_copy_rate(nbytes: int, achieved_gbs: float, reps: int = 40):
+    """HBM context for a bandwidth-bound workload: torch's device-to-device
+    copy moving the same number of bytes (half read, half written), timed
+    with HIP events over reps launches, and the kernel's fraction of it."""
+    import torch
+    n = max(nbytes // 2, 1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    del a, b
+    return {"gbs": round(gbs, 1), "frac": round(achieved_gbs / gbs, 4),
+            "how": "torch device copy of the same bytes (read + written), %d launches, same run" % reps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,7 +195,7 @@ def main():
                     help="only measure register-only MFMA streams (fp16, bf16, e4m3, int8) on every "
                          "CU with constant and with random operands (steady clock and rate)")
     ap.add_argument("--no-ceiling", action="store_true",
-                    help="skip the MFMA-ceiling measurement of the default run")
+                    help="skip the attainable-rate measurements (MFMA streams; a device copy of the same bytes for an HBM-bound workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes "
                          "--steps times (scales the HBM byte counters)")
@@ -276,7 +299,8 @@ def main():
         gbs = abytes / (avg_launch_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), **common,
-                    "tflops": round(achieved, 2)}
+                    "tflops": round(achieved, 2),
+                    "attainable_device_copy": None if args.no_ceiling else attainable_copy_rate(abytes, gbs)}
 
     cpu = None
     if not args.no_cpu_baseline:
