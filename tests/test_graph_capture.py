@@ -30,6 +30,9 @@ CASES = [
     # whole-K rounds, then the last round's tiles in K slices (289 tiles on 256 CUs)
     (synth.CONFIGS[2].replace(name="graph_f16_split_last_round", M=4352, N=4352, K=4096, L=1,
                               seed=7640), 0),
+    # a small problem on 128x128 tiles whose K is split (workspace slots of the smaller tile)
+    (synth.CONFIGS[2].replace(name="graph_f16_small_tiles_split", M=1024, N=1024, K=8192, L=1,
+                              seed=7650), 0),
 ]
 
 
@@ -44,6 +47,8 @@ def test_run_static_replays_match_eager(p, splits):
     assert g.plan["workspace_bytes"] <= ge.GEMM_EPI_STATIC_SCRATCH_BYTES
     if p.name.endswith("split_last_round"):
         assert 0 < g.plan["split_tiles"] < g.plan["tiles"] and g.plan["splits"] > 1, g.plan
+    if p.name.endswith("small_tiles_split"):
+        assert "128x128" in g.plan["name"] and g.plan["splits"] > 1 and g.plan["workspace_bytes"] > 0, g.plan
     shape = p.storage_shape("D")
 
     def outputs():
