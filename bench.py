@@ -185,6 +185,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2,
                     help="workload index 0..4 (2 = 8192^3 fp16 with C, X, D, Y); 5 = the same at K=256 (HBM-bound)")
+    ap.add_argument("--shape", default=None, metavar="M,N,K,L",
+                    help="other sizes for the workload's types, layouts and scalars (a shape study, "
+                         "not the metric's workload)")
     ap.add_argument("--epilogue", choices=("linear", "relu"), default="linear",
                     help="relu: D = max(0, alpha*A.B^T + beta*C) + x_factor*X")
     ap.add_argument("--variant", default="-1",
@@ -229,6 +232,9 @@ def main():
         return
 
     p = synth.CONFIGS[args.config]
+    if args.shape:
+        M, N, Kd, L = (int(v) for v in args.shape.split(","))
+        p = p.replace(name="%s_at_%dx%dx%dx%d" % (p.name, M, N, Kd, L), M=M, N=N, K=Kd, L=L)
     if args.epilogue != "linear":
         p = p.replace(name=p.name + "_" + args.epilogue, epilogue=args.epilogue)
     print("bench: workload %s M=%d N=%d K=%d L=%d" % (p.name, p.M, p.N, p.K, p.L),
