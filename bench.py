@@ -188,6 +188,8 @@ def main():
     ap.add_argument("--shape", default=None, metavar="M,N,K,L",
                     help="other sizes for the workload's types, layouts and scalars (a shape study, "
                          "not the metric's workload)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="K slices per split tile (0: the library's choice; 1: no split)")
     ap.add_argument("--epilogue", choices=("linear", "relu"), default="linear",
                     help="relu: D = max(0, alpha*A.B^T + beta*C) + x_factor*X")
     ap.add_argument("--variant", default="-1",
@@ -250,8 +252,11 @@ def main():
         variant = names.index(variant)
     g = ge.FusedGemm(p.M, p.N, p.K, p.L, ab=p.ab, a_major=p.a_major,
                      b_major=p.b_major, cd_major=p.cd_major, c=p.c, x=p.x,
-                     d=p.d, y=p.y, variant=int(variant), epilogue=p.epilogue)
+                     d=p.d, y=p.y, variant=int(variant), epilogue=p.epilogue, splits=args.splits)
     plan = g.plan
+    print("bench: plan %s, %d tiles, grid %d, %d K slice(s) on %d split tile(s), workspace %d bytes"
+          % (plan["name"], plan["tiles"], plan["grid"], plan["splits"], plan["split_tiles"],
+             plan["workspace_bytes"]), file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
 
     def step():
