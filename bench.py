@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "TFLOP/s and % of MFMA dense peak, 8192³ fp16 GEMM w/ fused epilogue"
 # MI355X datasheet dense MFMA peaks, TFLOP/s (TOP/s for int8)
-PEAK = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "e5m2": 5000.0, "i8": 5000.0}
+PEAK = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "e5m2": 5000.0, "i8": 5000.0, "u8": 5000.0}
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -188,6 +188,9 @@ def main():
     ap.add_argument("--shape", default=None, metavar="M,N,K,L",
                     help="other sizes for the workload's types, layouts and scalars (a shape study, "
                          "not the metric's workload)")
+    ap.add_argument("--uint8", action="store_true",
+                    help="with an int8 workload: the same shape and layouts with uint8 A and B "
+                         "(integers in [0, 255])")
     ap.add_argument("--splits", type=int, default=0,
                     help="K slices per split tile (0: the library's choice; 1: no split)")
     ap.add_argument("--epilogue", choices=("linear", "relu"), default="linear",
@@ -237,6 +240,10 @@ def main():
     if args.shape:
         M, N, Kd, L = (int(v) for v in args.shape.split(","))
         p = p.replace(name="%s_at_%dx%dx%dx%d" % (p.name, M, N, Kd, L), M=M, N=N, K=Kd, L=L)
+    if args.uint8:
+        if p.ab != "i8":
+            sys.exit("--uint8 takes an int8 workload")
+        p = p.replace(name=p.name.replace("i8", "u8", 1), ab="u8", dist_ab="u8full")
     if args.epilogue != "linear":
         p = p.replace(name=p.name + "_" + args.epilogue, epilogue=args.epilogue)
     print("bench: workload %s M=%d N=%d K=%d L=%d" % (p.name, p.M, p.N, p.K, p.L),
