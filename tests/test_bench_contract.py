@@ -57,3 +57,21 @@ def test_bench_line_hbm_bound_shape():
     cp = r["attainable_device_copy"]
     assert cp["gbs"] > 0 and abs(cp["frac"] - r["achieved"] / cp["gbs"]) < 1e-3
     assert d["cpu_baseline"] is None
+
+
+@pytest.mark.gpu
+def test_bench_study_options():
+    print("bench --shape / --splits / --uint8", file=sys.stderr, flush=True)
+    r = _bench("--config", "2", "--shape", "1024,1024,8192,1", "--steps", "2", "--warmup", "1",
+               "--no-cpu-baseline", "--no-ceiling")
+    d = _line(r)
+    assert d["config"]["M"] == 1024 and d["config"]["K"] == 8192
+    assert "128x128" in r.stderr and "4 K slice(s) on 64 split tile(s)" in r.stderr, r.stderr
+    r = _bench("--config", "2", "--shape", "1024,1024,8192,1", "--splits", "1", "--steps", "2", "--warmup", "1",
+               "--no-cpu-baseline", "--no-ceiling")
+    _line(r)
+    assert "1 K slice(s) on 0 split tile(s)" in r.stderr, r.stderr
+    d = _line(_bench("--config", "3", "--uint8", "--shape", "512,512,512,1", "--steps", "2", "--warmup", "1",
+                     "--cpu-seconds", "0.5", "--no-ceiling"))
+    assert d["dtype"] == "u8" and d["config"]["workload"].startswith("u8_")
+    assert d["cpu_baseline"]["value"] > 0
