@@ -188,6 +188,10 @@ def main():
     ap.add_argument("--shape", default=None, metavar="M,N,K,L",
                     help="other sizes for the workload's types, layouts and scalars (a shape study, "
                          "not the metric's workload)")
+    ap.add_argument("--a-major", choices=("K", "M"), default=None,
+                    help="A's majorness instead of the workload's (a layout study)")
+    ap.add_argument("--b-major", choices=("K", "N"), default=None,
+                    help="B's majorness instead of the workload's (a layout study)")
     ap.add_argument("--uint8", action="store_true",
                     help="with an int8 workload: the same shape and layouts with uint8 A and B "
                          "(integers in [0, 255])")
@@ -240,6 +244,9 @@ def main():
     if args.shape:
         M, N, Kd, L = (int(v) for v in args.shape.split(","))
         p = p.replace(name="%s_at_%dx%dx%dx%d" % (p.name, M, N, Kd, L), M=M, N=N, K=Kd, L=L)
+    for attr, val in (("a_major", args.a_major), ("b_major", args.b_major)):
+        if val and val != getattr(p, attr):
+            p = p.replace(name="%s_%s%s" % (p.name, attr[0], val.lower()), **{attr: val})
     if args.uint8:
         if p.ab != "i8":
             sys.exit("--uint8 takes an int8 workload")
