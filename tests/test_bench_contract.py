@@ -75,3 +75,8 @@ def test_bench_study_options():
                      "--cpu-seconds", "0.5", "--no-ceiling"))
     assert d["dtype"] == "u8" and d["config"]["workload"].startswith("u8_")
     assert d["cpu_baseline"]["value"] > 0
+    r = _bench("--config", "2", "--a-major", "M", "--b-major", "N", "--shape", "520,264,392,2", "--steps", "2",
+               "--warmup", "1", "--no-cpu-baseline", "--no-ceiling")
+    d = _line(r)
+    assert d["config"]["a_major"] == "M" and d["config"]["b_major"] == "N"
+    assert "plan f16_mn_n_" in r.stderr, r.stderr
