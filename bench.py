@@ -192,6 +192,14 @@ def main():
                     help="A's majorness instead of the workload's (a layout study)")
     ap.add_argument("--b-major", choices=("K", "N"), default=None,
                     help="B's majorness instead of the workload's (a layout study)")
+    ap.add_argument("--cd-major", choices=("N", "M"), default=None,
+                    help="C, X, D and Y majorness instead of the workload's (a layout study)")
+    ap.add_argument("--e5m2", action="store_true",
+                    help="with an e4m3 workload: e5m2 A and B (finite values with |v| <= 4)")
+    ap.add_argument("--bf16-out", action="store_true",
+                    help="bf16 D (and Y) instead of the workload's 16-bit float outputs")
+    ap.add_argument("--inplace", action="store_true",
+                    help="D written over C (same type and layout), as the library allows")
     ap.add_argument("--uint8", action="store_true",
                     help="with an int8 workload: the same shape and layouts with uint8 A and B "
                          "(integers in [0, 255])")
@@ -244,9 +252,21 @@ def main():
     if args.shape:
         M, N, Kd, L = (int(v) for v in args.shape.split(","))
         p = p.replace(name="%s_at_%dx%dx%dx%d" % (p.name, M, N, Kd, L), M=M, N=N, K=Kd, L=L)
-    for attr, val in (("a_major", args.a_major), ("b_major", args.b_major)):
+    for attr, val in (("a_major", args.a_major), ("b_major", args.b_major), ("cd_major", args.cd_major)):
         if val and val != getattr(p, attr):
             p = p.replace(name="%s_%s%s" % (p.name, attr[0], val.lower()), **{attr: val})
+    if args.e5m2:
+        if p.ab != "e4m3":
+            sys.exit("--e5m2 takes an e4m3 workload")
+        p = p.replace(name=p.name.replace("e4m3", "e5m2", 1), ab="e5m2", dist_ab="e5m2tab")
+    if args.bf16_out:
+        if p.d not in ("f16", "bf16") or (p.y and p.y not in ("f16", "bf16")):
+            sys.exit("--bf16-out takes a workload with 16-bit float outputs")
+        p = p.replace(name=p.name + "_bf16out", d="bf16", y="bf16" if p.y else None)
+    if args.inplace:
+        if p.c != p.d:
+            sys.exit("--inplace needs C and D of one type")
+        p = p.replace(name=p.name + "_inplace")
     if args.uint8:
         if p.ab != "i8":
             sys.exit("--uint8 takes an int8 workload")
@@ -258,7 +278,10 @@ def main():
     ins = synth.make_inputs(p)
     dev = {k: (v.cuda() if v is not None else None) for k, v in ins.items()}
     shape = p.storage_shape("D")
-    D = torch.empty(shape, dtype=synth.TORCH_DTYPE[p.d], device="cuda")
+    if args.inplace:
+        D = dev["C"]  # every step updates C; its values grow but stay finite over a run
+    else:
+        D = torch.empty(shape, dtype=synth.TORCH_DTYPE[p.d], device="cuda")
     Y = torch.empty(shape, dtype=synth.TORCH_DTYPE[p.y], device="cuda") if p.y else None
     variant = args.variant
     if not variant.lstrip("-").isdigit():

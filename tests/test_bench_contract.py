@@ -80,3 +80,19 @@ def test_bench_study_options():
     d = _line(r)
     assert d["config"]["a_major"] == "M" and d["config"]["b_major"] == "N"
     assert "plan f16_mn_n_" in r.stderr, r.stderr
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("opts,plan", [
+    (("--config", "2", "--cd-major", "M"), "plan f16_kk_m_"),
+    (("--config", "2", "--bf16-out"), "plan f16_kk_n_"),
+    (("--config", "2", "--inplace", "--epilogue", "relu"), "plan f16_kk_n_"),
+    (("--config", "4", "--e5m2"), "plan e5m2_kk_n_"),
+], ids=["cd_m", "bf16_out", "inplace_relu", "e5m2"])
+def test_bench_form_options(opts, plan):
+    print("bench", *opts, file=sys.stderr, flush=True)
+    r = _bench(*opts, "--shape", "520,264,400,2", "--steps", "2", "--warmup", "1", "--no-cpu-baseline",
+               "--no-ceiling")
+    d = _line(r)
+    assert plan in r.stderr, r.stderr
+    assert d["value"] > 0 and d["config"]["M"] == 520
