@@ -22,6 +22,16 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU only" in r.stderr and r.stdout.strip() == ""
 
 
+@pytest.mark.parametrize("opts,msg", [
+    (("--config", "2", "--uint8"), "--uint8 takes an int8 workload"),
+    (("--config", "2", "--e5m2"), "--e5m2 takes an e4m3 workload"),
+    (("--config", "3", "--bf16-out"), "--bf16-out takes a workload with 16-bit float outputs"),
+], ids=["uint8", "e5m2", "bf16_out"])
+def test_study_options_refuse_other_workloads(opts, msg):
+    r = _bench(*opts, timeout=120)
+    assert r.returncode != 0 and msg in r.stderr and r.stdout.strip() == ""
+
+
 def _line(r):
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
